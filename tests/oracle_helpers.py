@@ -1,0 +1,153 @@
+"""Test-side helpers: independent plain computations used to pin the oracle.
+
+Nothing here imports the HIP library.  The brute-force enumerator below recomputes every
+candidate node's distribution with numpy (its own code, not the oracle's), so that a dropped
+term, a wrong index or a wrong order in the oracle shows up as a mismatch.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+from scipy.special import logsumexp
+
+import oracle
+
+
+def small_instance(seed: int, *, V=24, r=4, B=3, k=2, Ncap=6, mode="greedy", temperature=1.0,
+                   cal="monotone", strong=True, tau=0.0, peak="one6"):
+    from draft_tree_construction_rank_amd import inputs
+    return inputs.make_instance("tiny", seed=seed, V=V, r=r, B=B, k=k, Ncap=Ncap, mode=mode,
+                                temperature=temperature, cal=cal, tau=tau, peak=peak,
+                                strong_head=strong)
+
+
+def node_dist(inst, req, depth, token, T):
+    """float64 tempered logits y of a node's children distribution (numpy, independent)."""
+    z = inst.L[req, depth].astype(np.float64) + \
+        inst.Wt.astype(np.float64) @ inst.U[token].astype(np.float64)
+    return z / T
+
+
+def ranked_children(inst, req, depth, token, h, mode, T):
+    y = node_dist(inst, req, depth, token, T)
+    lse = logsumexp(y)
+    if mode == "sample":
+        u = np.array([oracle.uniform(inst.seed, h, oracle.STREAM_GUMBEL, c) for c in range(inst.V)])
+        key = y - np.log(-np.log(u))
+    else:
+        key = y
+    order = sorted(range(inst.V), key=lambda c: (-key[c], c))[: inst.k]
+    return [(c, y[c] - lse) for c in order]
+
+
+def cal_bin(q):
+    return min(15, int(np.floor(16.0 * q)))
+
+
+def brute_force(inst, req, N, tau, mode="greedy", T=1.0, round_=0):
+    """Enumerate the whole k-ary candidate tree to depth B; keep s >= tau; sort by
+    (s desc, depth asc, rank path asc); keep the first N.  Returns the kept nodes in
+    canonical (depth, rank path) order as dicts."""
+    Teff = T if mode == "sample" else 1.0
+    root = int(inst.root_token[req])
+    h0 = oracle.mix64(oracle.mix64((round_ << 32) | req) ^ root)
+    allnodes = []
+    frontier = [dict(token=root, depth=0, s=np.float32(1.0), ranks=(), toks=(), h=h0)]
+    while frontier:
+        nxt = []
+        for nd in frontier:
+            if nd["depth"] >= inst.B:
+                continue
+            for j, (c, lq) in enumerate(ranked_children(inst, req, nd["depth"], nd["token"],
+                                                        nd["h"], mode, Teff)):
+                a = inst.cal[cal_bin(np.exp(lq))]
+                ch = dict(token=c, depth=nd["depth"] + 1, s=np.float32(nd["s"] * a),
+                          ranks=nd["ranks"] + (j,), toks=nd["toks"] + (c,),
+                          h=oracle.mix64(nd["h"] ^ c), logq=np.float32(lq))
+                allnodes.append(ch)
+                nxt.append(ch)
+        frontier = nxt
+    keep = [n for n in allnodes if not (n["s"] < np.float32(tau))]
+    keep.sort(key=lambda n: (-float(n["s"]), n["depth"], n["ranks"]))
+    keep = keep[:N]
+    keep.sort(key=lambda n: (n["depth"], n["ranks"]))
+    return keep
+
+
+def tree_paths(tree, i_req=0):
+    """Token paths of an emitted tree, in canonical order."""
+    n = int(tree["n_nodes"][i_req])
+    paths = []
+    for i in range(n):
+        p = int(tree["parent"][i_req, i])
+        prefix = () if p < 0 else paths[p]
+        paths.append(prefix + (int(tree["token"][i_req, i]),))
+    return paths
+
+
+def check_structure(inst, tree, i_req=0):
+    """Invariants every emitted tree satisfies."""
+    n = int(tree["n_nodes"][i_req])
+    k, B = inst.k, inst.B
+    par = tree["parent"][i_req]
+    dep = tree["depth"][i_req]
+    msk = tree["mask"][i_req]
+    srv = tree["surv"][i_req]
+    kids = {}
+    for i in range(n):
+        p = int(par[i])
+        assert p < i  # parents first
+        assert 1 <= dep[i] <= B
+        if p < 0:
+            assert dep[i] == 1
+        else:
+            assert dep[i] == dep[p] + 1
+            assert srv[i] <= srv[p]  # survival never increases along a path
+            assert int(msk[i]) == int(msk[p]) | (1 << i)
+        assert bin(int(msk[i])).count("1") == int(dep[i])
+        kids.setdefault(p, []).append(int(tree["token"][i_req, i]))
+    for p, ts in kids.items():
+        assert len(ts) <= k and len(set(ts)) == len(ts)
+    for i in range(n, inst.Ncap):
+        assert tree["token"][i_req, i] == -1 and par[i] == -2 and dep[i] == 0 and msk[i] == 0
+    # canonical order: depth then rank path
+    ranks = []
+    for i in range(n):
+        p = int(par[i])
+        row = tree["cand"][i_req, p + 1]
+        j = list(row).index(int(tree["token"][i_req, i]))
+        ranks.append((() if p < 0 else ranks[p]) + (j,))
+    keyed = [(int(dep[i]), ranks[i]) for i in range(n)]
+    assert keyed == sorted(keyed)
+    return ranks
+
+
+def plackett_luce(q, xs):
+    """Probability that sampling without replacement from q yields the ordered tuple xs."""
+    pr = 1.0
+    taken = set()
+    for x in xs:
+        left = sum(q[y] for y in range(len(q)) if y not in taken)  # no 1 - sum cancellation
+        pr *= q[x] / left
+        taken.add(x)
+    return pr
+
+
+def exact_emitted_law(p, q, k):
+    """Law of the token emitted at one node by the rejection chain, enumerating every
+    ordered draw of k siblings (Plackett-Luce weights) and every accept/reject branch; the
+    per-step acceptance probabilities and the final residual come from the oracle."""
+    V = len(p)
+    law = np.zeros(V)
+    for xs in itertools.permutations(range(V), k):
+        w = plackett_luce(q, xs)
+        if w == 0.0:
+            continue
+        acc, resid = oracle.chain_probs(p, q, xs)
+        rej = 1.0
+        for j, x in enumerate(xs):
+            law[x] += w * rej * acc[j]
+            rej *= 1.0 - acc[j]
+        law += w * rej * resid
+    return law

@@ -1,0 +1,208 @@
+"""ctypes binding of libdtree.so (argument marshalling only).
+
+Every step of tree construction and verification runs in the HIP kernels of libdtree.so; this
+module only converts torch tensors to device pointers and fills the C structs declared in
+include/dtree.h.  There is no CPU fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdtree.so")
+
+DT_OK, DT_EINVAL, DT_ENOSPC, DT_EDEVICE = 0, 1, 2, 3
+DT_F32, DT_BF16 = 0, 1
+DT_GREEDY, DT_SAMPLE = 0, 1
+DT_REQ_BAD_ROOT, DT_REQ_BUDGET_CLAMPED = 1, 2
+
+EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_verify_greedy",
+            "tree_verify_sample", "dt_status_string", "dt_timing_enable", "dt_timing_read")
+
+
+class DtError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__("%s failed: %s" % (fn, status_string(code)))
+        self.code = code
+
+
+class dt_params(C.Structure):
+    _fields_ = [("R", C.c_int32), ("B", C.c_int32), ("k", C.c_int32), ("V", C.c_int32),
+                ("r", C.c_int32), ("Ncap", C.c_int32), ("logits_dtype", C.c_int32),
+                ("head_dtype", C.c_int32), ("mode", C.c_int32), ("temperature", C.c_float),
+                ("cal", C.c_float * 16), ("seed", C.c_uint64), ("round", C.c_uint32),
+                ("reserved", C.c_uint32)]
+
+
+class dt_tree(C.Structure):
+    _fields_ = [("token", C.c_void_p), ("parent", C.c_void_p), ("depth", C.c_void_p),
+                ("anc_mask", C.c_void_p), ("surv", C.c_void_p), ("logq", C.c_void_p),
+                ("n_nodes", C.c_void_p), ("cand", C.c_void_p), ("status", C.c_void_p),
+                ("n_expand", C.c_void_p), ("level_rows", C.c_void_p)]
+
+
+class dt_verify_out(C.Structure):
+    _fields_ = [("accept_len", C.c_void_p), ("path", C.c_void_p), ("out_tokens", C.c_void_p),
+                ("n_out", C.c_void_p)]
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def lib() -> C.CDLL:
+    """Load libdtree.so (built by draft_tree_construction_rank_amd.build); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libdtree.so is not built (%s); run __graft_entry__.build() or "
+                              "python draft_tree_construction_rank_amd/build.py" % LIB_PATH)
+        L = C.CDLL(LIB_PATH)
+        vp = C.c_void_p
+        P = C.POINTER(dt_params)
+        L.dt_build_workspace_bytes.argtypes = [P, C.POINTER(C.c_size_t)]
+        L.dt_build_workspace_bytes.restype = C.c_int
+        L.tree_build.argtypes = [P, vp, vp, vp, vp, vp, vp, C.POINTER(dt_tree), vp, C.c_size_t, vp]
+        L.tree_build.restype = C.c_int
+        L.tree_verify_greedy.argtypes = [P, C.POINTER(dt_tree), vp, C.POINTER(dt_verify_out), vp,
+                                         C.c_size_t, vp]
+        L.tree_verify_greedy.restype = C.c_int
+        L.tree_verify_sample.argtypes = [P, C.POINTER(dt_tree), vp, vp, vp, vp, vp,
+                                         C.POINTER(dt_verify_out), vp, C.c_size_t, vp]
+        L.tree_verify_sample.restype = C.c_int
+        L.dt_status_string.argtypes = [C.c_int]
+        L.dt_status_string.restype = C.c_char_p
+        L.dt_timing_enable.argtypes = [C.c_int32]
+        L.dt_timing_enable.restype = C.c_int
+        L.dt_timing_read.argtypes = [C.POINTER(C.c_double), C.POINTER(C.c_int32)]
+        L.dt_timing_read.restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().dt_status_string(code).decode()
+
+
+def make_params(*, R: int, B: int, k: int, V: int, r: int, Ncap: int, logits_dtype: int,
+                head_dtype: int, mode: int, temperature: float, cal: Sequence[float],
+                seed: int = 0, round_: int = 0) -> dt_params:
+    p = dt_params()
+    p.R, p.B, p.k, p.V, p.r, p.Ncap = R, B, k, V, r, Ncap
+    p.logits_dtype, p.head_dtype, p.mode = logits_dtype, head_dtype, mode
+    p.temperature = float(temperature)
+    for i in range(16):
+        p.cal[i] = float(cal[i])
+    p.seed = int(seed)
+    p.round = int(round_)
+    p.reserved = 0
+    return p
+
+
+def dt_build_workspace_bytes(p: dt_params) -> int:
+    n = C.c_size_t(0)
+    rc = lib().dt_build_workspace_bytes(C.byref(p), C.byref(n))
+    if rc != DT_OK:
+        raise DtError("dt_build_workspace_bytes", rc)
+    return int(n.value)
+
+
+def alloc_workspace(p: dt_params, device) -> torch.Tensor:
+    return torch.empty(dt_build_workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+def alloc_tree(p: dt_params, device) -> dict:
+    R, N, k, B = p.R, p.Ncap, p.k, p.B
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(token=torch.empty(R, N, **i32), parent=torch.empty(R, N, dtype=torch.int16, device=device),
+                depth=torch.empty(R, N, dtype=torch.uint8, device=device),
+                anc_mask=torch.empty(R, N, dtype=torch.int64, device=device),
+                surv=torch.empty(R, N, dtype=torch.float32, device=device),
+                logq=torch.empty(R, N, dtype=torch.float32, device=device),
+                n_nodes=torch.empty(R, **i32), cand=torch.empty(R, N + 1, k, **i32),
+                status=torch.empty(R, **i32), n_expand=torch.empty(R, **i32),
+                level_rows=torch.empty(B, **i32))
+
+
+def alloc_verify(p: dt_params, device) -> dict:
+    R, B = p.R, p.B
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(accept_len=torch.empty(R, **i32), path=torch.empty(R, B, **i32),
+                out_tokens=torch.empty(R, B + 1, **i32), n_out=torch.empty(R, **i32))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libdtree must be contiguous")
+    return t.data_ptr()
+
+
+def _tree_struct(t: dict) -> dt_tree:
+    s = dt_tree()
+    for f, _ in dt_tree._fields_:
+        setattr(s, f, _ptr(t.get(f)))
+    return s
+
+
+def _verify_struct(o: dict) -> dt_verify_out:
+    s = dt_verify_out()
+    for f, _ in dt_verify_out._fields_:
+        setattr(s, f, _ptr(o[f]))
+    return s
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def tree_build(p: dt_params, block_logits: torch.Tensor, U: torch.Tensor, Wt: torch.Tensor,
+               root_token: torch.Tensor, n_budget: torch.Tensor, tau: torch.Tensor, out: dict,
+               workspace: torch.Tensor, stream=None) -> None:
+    ts = _tree_struct(out)
+    rc = lib().tree_build(C.byref(p), _ptr(block_logits), _ptr(U), _ptr(Wt), _ptr(root_token),
+                          _ptr(n_budget), _ptr(tau), C.byref(ts), _ptr(workspace),
+                          workspace.numel(), _stream(stream))
+    if rc != DT_OK:
+        raise DtError("tree_build", rc)
+
+
+def tree_verify_greedy(p: dt_params, tree: dict, target_logits: torch.Tensor, out: dict,
+                       workspace: torch.Tensor, stream=None) -> None:
+    ts = _tree_struct(tree)
+    vs = _verify_struct(out)
+    rc = lib().tree_verify_greedy(C.byref(p), C.byref(ts), _ptr(target_logits), C.byref(vs),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != DT_OK:
+        raise DtError("tree_verify_greedy", rc)
+
+
+def tree_verify_sample(p: dt_params, tree: dict, block_logits: torch.Tensor, U: torch.Tensor,
+                       Wt: torch.Tensor, root_token: torch.Tensor, target_logits: torch.Tensor,
+                       out: dict, workspace: torch.Tensor, stream=None) -> None:
+    ts = _tree_struct(tree)
+    vs = _verify_struct(out)
+    rc = lib().tree_verify_sample(C.byref(p), C.byref(ts), _ptr(block_logits), _ptr(U), _ptr(Wt),
+                                  _ptr(root_token), _ptr(target_logits), C.byref(vs),
+                                  _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != DT_OK:
+        raise DtError("tree_verify_sample", rc)
+
+
+def timing_enable(on: bool) -> None:
+    lib().dt_timing_enable(1 if on else 0)
+
+
+def timing_read() -> tuple:
+    ms = C.c_double(0.0)
+    n = C.c_int32(0)
+    rc = lib().dt_timing_read(C.byref(ms), C.byref(n))
+    if rc != DT_OK:
+        raise DtError("dt_timing_read", rc)
+    return float(ms.value), int(n.value)

@@ -1,0 +1,281 @@
+// Host side of libdtree: argument validation, workspace layout and the launch sequence.
+// Every entry point validates on the host and returns before enqueuing anything when an
+// argument is bad; otherwise it only enqueues work on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <mutex>
+#include <vector>
+
+#include "dt_internal.h"
+
+namespace dt {
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Layout make_layout(const dt_params* p) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    const size_t R = p->R, B = p->B, N = p->Ncap, k = p->k, V = p->V;
+    L.NC = (int)((V + kChunkCols - 1) / kChunkCols);
+    L.KT = kt_for(p->k);
+    const int tmax = (int)((R * N + kTileRows - 1) / kTileRows);
+    L.G = tmax > 1024 ? tmax : 1024;
+    L.rows = take(R * N * sizeof(int2));
+    L.ctl = take(8 * sizeof(int));
+    L.front = take(R * (B + 1) * N * sizeof(FrontEntry));
+    L.fcount = take(R * (B + 1) * sizeof(int));
+    L.arena = take(R * B * N * k * sizeof(ChildRec));
+    L.ckeys = take(R * N * k * sizeof(uint64_t));
+    L.skeys = take(R * N * sizeof(uint64_t));
+    L.scount = take(R * sizeof(int));
+    L.nbeff = take(R * sizeof(int));
+    L.rstat = take(R * sizeof(int));
+    L.partials = take((size_t)kTileRows * L.G * (2 + 3 * L.KT) * sizeof(float));
+    L.vsplits = 0;
+    L.vrow = L.vprow = L.vstate = L.vpart = 0;
+    if (p->mode == DT_SAMPLE) {
+        // sample verify: ceil(R/64) request tiles x vsplits vocabulary splits, grid <= 1024
+        const int tiles = (int)((R + kTileRows - 1) / kTileRows);
+        int s = 1024 / tiles;
+        if (s >= 8) s &= ~7;
+        if (s > L.NC) s = L.NC;
+        if (s < 1) s = 1;
+        L.vsplits = s;
+        L.vrow = take(R * V * sizeof(float));
+        L.vprow = take(R * V * sizeof(float));
+        L.vstate = take(R * sizeof(VState));
+        L.vpart = take(R * (size_t)L.vsplits * 4 * sizeof(float));
+    }
+    L.total = off;
+    return L;
+}
+
+static dt_status validate(const dt_params* p) {
+    if (!p) return DT_EINVAL;
+    if (p->R < 1 || p->R > 4096) return DT_EINVAL;
+    if (p->B < 1 || p->B > kMaxB) return DT_EINVAL;
+    if (p->k < 1 || p->k > kMaxK) return DT_EINVAL;
+    if (p->V < 1 || p->V > (1 << 24) || p->k > p->V) return DT_EINVAL;
+    if (p->Ncap < 1 || p->Ncap > kMaxNcap) return DT_EINVAL;
+    if (p->logits_dtype != DT_F32 && p->logits_dtype != DT_BF16) return DT_EINVAL;
+    if (p->head_dtype != DT_F32 && p->head_dtype != DT_BF16) return DT_EINVAL;
+    if (p->mode != DT_GREEDY && p->mode != DT_SAMPLE) return DT_EINVAL;
+    if (p->head_dtype == DT_BF16 && (p->r < 8 || p->r > 256 || (p->r & 7) != 0)) return DT_EINVAL;
+    if (p->head_dtype == DT_F32 && (p->r < 1 || p->r > 64)) return DT_EINVAL;
+    if (!std::isfinite(p->temperature) || !(p->temperature > 0.0f)) return DT_EINVAL;
+    for (int i = 0; i < 16; ++i) {
+        const float c = p->cal[i];
+        if (!(c >= 0.0f && c <= 1.0f)) return DT_EINVAL;
+        if (i > 0 && c < p->cal[i - 1]) return DT_EINVAL;
+    }
+    if (p->reserved != 0) return DT_EINVAL;
+    return DT_OK;
+}
+
+static bool tree_ptrs_ok(const dt_tree* t) {
+    return t && t->token && t->parent && t->depth && t->anc_mask && t->surv && t->logq &&
+           t->n_nodes && t->cand && t->status;
+}
+
+static bool verify_ptrs_ok(const dt_verify_out* o) {
+    return o && o->accept_len && o->path && o->out_tokens && o->n_out;
+}
+
+// ---- optional event timing of the expansion kernel
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    size_t used = 0;
+};
+static Timing g_timing;
+
+static void timing_mark(hipStream_t st) {
+    if (!g_timing.on) return;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    if (g_timing.used == g_timing.pool.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return;
+        g_timing.pool.push_back(e);
+    }
+    (void)hipEventRecord(g_timing.pool[g_timing.used++], st);
+}
+
+}  // namespace dt
+
+using namespace dt;
+
+extern "C" {
+
+const char* dt_status_string(dt_status s) {
+    switch (s) {
+        case DT_OK: return "DT_OK";
+        case DT_EINVAL: return "DT_EINVAL: invalid argument";
+        case DT_ENOSPC: return "DT_ENOSPC: workspace too small";
+        case DT_EDEVICE: return "DT_EDEVICE: HIP launch or device error";
+    }
+    return "unknown dt_status";
+}
+
+dt_status dt_build_workspace_bytes(const dt_params* p, size_t* bytes) {
+    const dt_status v = validate(p);
+    if (v != DT_OK) return v;
+    if (!bytes) return DT_EINVAL;
+    *bytes = make_layout(p).total;
+    return DT_OK;
+}
+
+dt_status tree_build(const dt_params* p, const void* block_logits, const void* U, const void* Wt,
+                     const int32_t* root_token, const int32_t* n_budget, const float* tau,
+                     const dt_tree* out, void* workspace, size_t ws_bytes, void* stream) {
+    const dt_status v = validate(p);
+    if (v != DT_OK) return v;
+    if (!block_logits || !U || !Wt || !root_token || !n_budget || !tau || !tree_ptrs_ok(out) ||
+        !workspace)
+        return DT_EINVAL;
+    if (((uintptr_t)U & 15) || ((uintptr_t)Wt & 15) || ((uintptr_t)block_logits & 15) ||
+        ((uintptr_t)workspace & 255))
+        return DT_EINVAL;
+    const Layout lay = make_layout(p);
+    if (ws_bytes < lay.total) return DT_ENOSPC;
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+
+    if (launch_build_init(p, lay, ws, root_token, n_budget, out->level_rows, st) != hipSuccess)
+        return DT_EDEVICE;
+
+    const float Teff = (p->mode == DT_SAMPLE) ? p->temperature : 1.0f;
+    ExpandArgs ea{};
+    ea.L = block_logits;
+    ea.U = U;
+    ea.Wt = Wt;
+    ea.rows = (const int2*)(ws + lay.rows);
+    ea.ctl = (const int*)(ws + lay.ctl);
+    ea.front = (const FrontEntry*)(ws + lay.front);
+    ea.partials = (float*)(ws + lay.partials);
+    ea.R = p->R;
+    ea.B = p->B;
+    ea.V = p->V;
+    ea.r = p->r;
+    ea.Ncap = p->Ncap;
+    ea.G = lay.G;
+    ea.NC = lay.NC;
+    ea.y2scale = (float)(1.4426950408889634 / (double)Teff);
+    ea.invT = (float)(1.0 / (double)Teff);
+    ea.seed_lo = (uint32_t)p->seed;
+    ea.seed_hi = (uint32_t)(p->seed >> 32);
+    ea.logits_bf16 = p->logits_dtype == DT_BF16;
+
+    MergeArgs ma{};
+    ma.rows = ea.rows;
+    ma.ctl = ea.ctl;
+    ma.partials = ea.partials;
+    ma.front = ea.front;
+    ma.arena = (ChildRec*)(ws + lay.arena);
+    ma.ckeys = (uint64_t*)(ws + lay.ckeys);
+    ma.R = p->R;
+    ma.B = p->B;
+    ma.k = p->k;
+    ma.Ncap = p->Ncap;
+    ma.G = lay.G;
+    ma.NC = lay.NC;
+    ma.KT = lay.KT;
+    for (int i = 0; i < 16; ++i) ma.cal[i] = p->cal[i];
+
+    SelectArgs sa{};
+    sa.rows = (int2*)(ws + lay.rows);
+    sa.ctl = (int*)(ws + lay.ctl);
+    sa.front = (FrontEntry*)(ws + lay.front);
+    sa.fcount = (int*)(ws + lay.fcount);
+    sa.arena = ma.arena;
+    sa.ckeys = ma.ckeys;
+    sa.skeys = (uint64_t*)(ws + lay.skeys);
+    sa.scount = (int*)(ws + lay.scount);
+    sa.nbeff = (const int*)(ws + lay.nbeff);
+    sa.tau = tau;
+    sa.level_rows = out->level_rows;
+    sa.R = p->R;
+    sa.B = p->B;
+    sa.k = p->k;
+    sa.Ncap = p->Ncap;
+
+    for (int level = 1; level <= p->B; ++level) {
+        ea.level = ma.level = sa.level = level;
+        timing_mark(st);
+        if (launch_expand(p, lay, ea, st) != hipSuccess) return DT_EDEVICE;
+        timing_mark(st);
+        if (launch_merge(p, lay, ma, st) != hipSuccess) return DT_EDEVICE;
+        if (launch_select(p, sa, st) != hipSuccess) return DT_EDEVICE;
+    }
+    if (launch_emit(p, lay, ws, out, st) != hipSuccess) return DT_EDEVICE;
+    return DT_OK;
+}
+
+dt_status tree_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target_logits,
+                             const dt_verify_out* out, void* workspace, size_t ws_bytes,
+                             void* stream) {
+    const dt_status v = validate(p);
+    if (v != DT_OK) return v;
+    if (!tree_ptrs_ok(tree) || !target_logits || !verify_ptrs_ok(out)) return DT_EINVAL;
+    if ((uintptr_t)target_logits & 15) return DT_EINVAL;
+    (void)workspace;
+    (void)ws_bytes;
+    if (launch_verify_greedy(p, tree, target_logits, out, (hipStream_t)stream) != hipSuccess)
+        return DT_EDEVICE;
+    return DT_OK;
+}
+
+dt_status tree_verify_sample(const dt_params* p, const dt_tree* tree, const void* block_logits,
+                             const void* U, const void* Wt, const int32_t* root_token,
+                             const void* target_logits, const dt_verify_out* out,
+                             void* workspace, size_t ws_bytes, void* stream) {
+    const dt_status v = validate(p);
+    if (v != DT_OK) return v;
+    if (p->mode != DT_SAMPLE) return DT_EINVAL;
+    if (!tree_ptrs_ok(tree) || !block_logits || !U || !Wt || !root_token || !target_logits ||
+        !verify_ptrs_ok(out) || !workspace)
+        return DT_EINVAL;
+    if (((uintptr_t)U & 15) || ((uintptr_t)Wt & 15) || ((uintptr_t)block_logits & 15) ||
+        ((uintptr_t)target_logits & 15) || ((uintptr_t)workspace & 255))
+        return DT_EINVAL;
+    const Layout lay = make_layout(p);
+    if (ws_bytes < lay.total) return DT_ENOSPC;
+    if (launch_verify_sample(p, lay, (char*)workspace, tree, block_logits, U, Wt, root_token,
+                             target_logits, out, (hipStream_t)stream) != hipSuccess)
+        return DT_EDEVICE;
+    return DT_OK;
+}
+
+dt_status dt_timing_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    g_timing.on = on != 0;
+    g_timing.used = 0;
+    return DT_OK;
+}
+
+dt_status dt_timing_read(double* total_ms, int32_t* launches) {
+    if (!total_ms || !launches) return DT_EINVAL;
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    double tot = 0.0;
+    const size_t pairs = g_timing.used / 2;
+    if (pairs > 0 && hipEventSynchronize(g_timing.pool[2 * pairs - 1]) != hipSuccess)
+        return DT_EDEVICE;
+    for (size_t i = 0; i < pairs; ++i) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, g_timing.pool[2 * i], g_timing.pool[2 * i + 1]) != hipSuccess)
+            return DT_EDEVICE;
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = (int32_t)pairs;
+    g_timing.used = 0;
+    return DT_OK;
+}
+
+}  // extern "C"

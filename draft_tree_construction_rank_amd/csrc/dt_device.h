@@ -1,0 +1,180 @@
+// Device-side helpers of libdtree: counter-based randomness, selection keys, bf16 loads and
+// the top-k register lists used by the fused expansion kernel.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dt_internal.h"
+
+namespace dt {
+
+// ---------------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11): ten rounds; each multiplies counter words 0 and 2 by the two Philox constants,
+// mixes the high halves with words 1, 3 and the key, and advances the key by the Weyl
+// constants.  Written here from that definition; checked against the published
+// known-answer vectors by the test suite.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return c;
+}
+
+// SplitMix64 output function applied to x + golden gamma (Steele, Lea, Flood 2014).
+__device__ __host__ __forceinline__ uint64_t mix64(uint64_t x) {
+    uint64_t z = x + 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// Random stream of a node = hash of its token path; the root's also folds in the round and
+// the request index.
+__device__ __host__ __forceinline__ uint64_t root_hash(uint32_t round, int32_t req, int32_t tok) {
+    const uint64_t a = mix64(((uint64_t)round << 32) | (uint64_t)(uint32_t)req);
+    return mix64(a ^ (uint64_t)(uint32_t)tok);
+}
+__device__ __host__ __forceinline__ uint64_t child_hash(uint64_t h, int32_t tok) {
+    return mix64(h ^ (uint64_t)(uint32_t)tok);
+}
+
+enum : uint32_t { STREAM_GUMBEL = 1, STREAM_ACCEPT = 2, STREAM_RESID = 3 };
+
+// Four words for indices 4*g .. 4*g+3 of one (stream, node) pair.
+__device__ __forceinline__ uint4 rand4(uint32_t g, uint32_t stream, uint64_t h, uint32_t k0,
+                                       uint32_t k1) {
+    return philox10(make_uint4(g, stream, (uint32_t)h, (uint32_t)(h >> 32)), k0, k1);
+}
+
+// Uniform in (0, 1): u = (m + 1/2) 2^-24 with m = the top 24 bits of a word.  In float32,
+// m + 1/2 is exact only for m < 2^23; above that the sum would round, so callers that need
+// 1 - u use one_minus_u01(), which is exact for m >= 2^23.
+__device__ __forceinline__ float u01(uint32_t w) {
+    return ((float)(w >> 8) + 0.5f) * (1.0f / 16777216.0f);
+}
+__device__ __forceinline__ float one_minus_u01(uint32_t w) {
+    return ((float)(16777216u - (w >> 8)) - 0.5f) * (1.0f / 16777216.0f);
+}
+
+// Gumbel(0, 1) = -log(-log u).  For u > 1/2, -log u = -log1p(-(1 - u)) with 1 - u exact, so
+// it keeps full relative precision near u = 1, where the largest Gumbel values, the ones
+// that decide the top-k, come from.
+__device__ __forceinline__ float gumbel(uint32_t w) {
+    const uint32_t m = w >> 8;
+    const float t = (m >= (1u << 23)) ? -log1pf(-one_minus_u01(w))
+                                      : -logf(((float)m + 0.5f) * (1.0f / 16777216.0f));
+    return -logf(t);
+}
+
+// ---------------------------------------------------------------------------------------
+// Selection keys: one u64, larger = better.  High word = survival bits (survival >= 0, so
+// the IEEE bit pattern orders like the value); low word = (63 - depth, 127 - frontier index
+// of the parent, 15 - sibling rank), so ties go to the shallower node, then to the earlier
+// parent in canonical order, then to the lower sibling rank: the (survival desc, depth asc,
+// rank-path asc) order.  The low word alone orders nodes canonically (depth, path).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t node_low(int depth, int fi, int j) {
+    return ((uint32_t)(63 - depth) << 11) | ((uint32_t)(127 - fi) << 4) | (uint32_t)(15 - j);
+}
+__device__ __forceinline__ uint64_t make_key(float s, int depth, int fi, int j) {
+    return ((uint64_t)__float_as_uint(s) << 32) | node_low(depth, fi, j);
+}
+__device__ __forceinline__ float key_surv(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
+__device__ __forceinline__ int low_depth(uint32_t low) { return 63 - (int)((low >> 11) & 63u); }
+__device__ __forceinline__ int low_fi(uint32_t low) { return 127 - (int)((low >> 4) & 127u); }
+__device__ __forceinline__ int low_rank(uint32_t low) { return 15 - (int)(low & 15u); }
+
+// ---------------------------------------------------------------------------------------
+// bf16 / f32 element access
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float load_logit(const void* base, size_t idx, bool bf16) {
+    return bf16 ? bf16_to_f32(((const uint16_t*)base)[idx]) : ((const float*)base)[idx];
+}
+
+// ---------------------------------------------------------------------------------------
+// Ranked lists held in registers: (key desc, token asc), length KT, compile-time indices
+// only (no scratch).
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float ka, int ta, float kb, int tb) {
+    return ka > kb || (ka == kb && ta < tb);
+}
+
+template <int KT>
+struct TopK {
+    float key[KT];
+    float y[KT];  // tempered logit in log2 units (z / T * log2 e)
+    int tok[KT];
+
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+            key[i] = -INFINITY;
+            y[i] = -INFINITY;
+            tok[i] = 0x7fffffff;
+        }
+    }
+    // Insert (k, yy, t) if it ranks among the KT best.
+    __device__ __forceinline__ void push(float k, float yy, int t) {
+        if (!better(k, t, key[KT - 1], tok[KT - 1])) return;
+#pragma unroll
+        for (int i = KT - 1; i >= 0; --i) {
+            const bool gi = better(k, t, key[i], tok[i]);
+            const bool gp = (i > 0) ? better(k, t, key[i - 1], tok[i - 1]) : false;
+            if (gi) {
+                if (gp) {
+                    key[i] = key[i - 1];
+                    y[i] = y[i - 1];
+                    tok[i] = tok[i - 1];
+                } else {
+                    key[i] = k;
+                    y[i] = yy;
+                    tok[i] = t;
+                }
+            }
+        }
+    }
+    // Merge with the list held by lane (lane ^ off) of the same wavefront.
+    __device__ __forceinline__ void merge_xor(int off) {
+        float ok[KT], oy[KT];
+        int ot[KT];
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+            ok[i] = __shfl_xor(key[i], off);
+            oy[i] = __shfl_xor(y[i], off);
+            ot[i] = __shfl_xor(tok[i], off);
+        }
+#pragma unroll
+        for (int i = 0; i < KT; ++i) push(ok[i], oy[i], ot[i]);
+    }
+};
+
+// Online log-sum-exp in log2 units: value = m + log2(s).
+struct Lse2 {
+    float m, s;
+    __device__ __forceinline__ void init() { m = -INFINITY; s = 0.0f; }
+    __device__ __forceinline__ void merge(float om, float os) {
+        if (om == -INFINITY) return;
+        if (m == -INFINITY) { m = om; s = os; return; }
+        const float nm = fmaxf(m, om);
+        s = s * exp2f(m - nm) + os * exp2f(om - nm);
+        m = nm;
+    }
+    __device__ __forceinline__ void merge_xor(int off) {
+        const float om = __shfl_xor(m, off), os = __shfl_xor(s, off);
+        merge(om, os);
+    }
+};
+
+}  // namespace dt

@@ -1,0 +1,517 @@
+// Verification kernels for gfx950.
+//
+// Greedy accept-walk (PCTree setup: greedy verification): one workgroup per request walks
+// from the root; each step is a row argmax over the vocabulary (bandwidth-bound, 16-byte
+// loads spread over 1024 threads) followed by a lookup of the argmax among the current
+// node's children (at most 64 tree nodes, held in LDS).
+#include <hip/hip_runtime.h>
+
+#include "dt_device.h"
+#include "dt_mma.h"
+
+namespace dt {
+
+struct ArgMax {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ ArgMax amax(ArgMax a, ArgMax b) {
+    return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
+}
+
+__device__ __forceinline__ ArgMax wave_amax(ArgMax a) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        ArgMax o;
+        o.v = __shfl_xor(a.v, off);
+        o.i = __shfl_xor(a.i, off);
+        a = amax(a, o);
+    }
+    return a;
+}
+
+// Argmax of one row (ties: lower index) over the whole workgroup; every thread gets it.
+template <bool BF16>
+__device__ ArgMax row_argmax(const void* row, int V, bool vec, ArgMax* sh) {
+    ArgMax best{-INFINITY, 0x7fffffff};
+    const int tid = threadIdx.x, nt = blockDim.x;
+    if (BF16) {
+        const uint16_t* p = (const uint16_t*)row;
+        if (vec) {
+            const int nv = V >> 3;
+            for (int i = tid; i < nv; i += nt) {
+                const uint4 w = ((const uint4*)p)[i];
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    best = amax(best, ArgMax{bf16_lo(ws[e]), i * 8 + 2 * e});
+                    best = amax(best, ArgMax{bf16_hi(ws[e]), i * 8 + 2 * e + 1});
+                }
+            }
+        } else {
+            for (int i = tid; i < V; i += nt) best = amax(best, ArgMax{bf16_to_f32(p[i]), i});
+        }
+    } else {
+        const float* p = (const float*)row;
+        if (vec) {
+            const int nv = V >> 2;
+            for (int i = tid; i < nv; i += nt) {
+                const float4 w = ((const float4*)p)[i];
+                best = amax(best, ArgMax{w.x, i * 4});
+                best = amax(best, ArgMax{w.y, i * 4 + 1});
+                best = amax(best, ArgMax{w.z, i * 4 + 2});
+                best = amax(best, ArgMax{w.w, i * 4 + 3});
+            }
+        } else {
+            for (int i = tid; i < V; i += nt) best = amax(best, ArgMax{p[i], i});
+        }
+    }
+    best = wave_amax(best);
+    const int wv = tid >> 6, nw = nt >> 6;
+    if ((tid & 63) == 0) sh[wv] = best;
+    __syncthreads();
+    if (tid < 64) {
+        ArgMax b = (tid < nw) ? sh[tid] : ArgMax{-INFINITY, 0x7fffffff};
+        b = wave_amax(b);
+        if (tid == 0) sh[0] = b;
+    }
+    __syncthreads();
+    const ArgMax r = sh[0];
+    __syncthreads();
+    return r;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(1024) void k_verify_greedy(int B, int V, int Ncap, const void* target,
+                                                        dt_tree tree, dt_verify_out out) {
+    __shared__ ArgMax sh[16];
+    __shared__ int s_tok[kMaxNcap], s_par[kMaxNcap];
+    __shared__ int s_child;
+    const int req = blockIdx.x, tid = threadIdx.x;
+    const int n = tree.n_nodes[req];
+    const bool bad = (tree.status[req] & DT_REQ_BAD_ROOT) != 0;
+    if (tid < Ncap) {
+        s_tok[tid] = tree.token[(size_t)req * Ncap + tid];
+        s_par[tid] = tree.parent[(size_t)req * Ncap + tid];
+    }
+    for (int i = tid; i < B; i += blockDim.x) out.path[(size_t)req * B + i] = -1;
+    for (int i = tid; i <= B; i += blockDim.x) out.out_tokens[(size_t)req * (B + 1) + i] = -1;
+    __syncthreads();
+    if (bad) {
+        if (tid == 0) {
+            out.accept_len[req] = 0;
+            out.n_out[req] = 0;
+        }
+        return;
+    }
+    const bool vec = BF16 ? (V & 7) == 0 : (V & 3) == 0;
+    const size_t esz = BF16 ? 2 : 4;
+    int v = -1, row = 0, nacc = 0;
+    for (;;) {
+        const char* rp = (const char*)target + ((size_t)req * (Ncap + 1) + row) * (size_t)V * esz;
+        const ArgMax am = row_argmax<BF16>(rp, V, vec, sh);
+        if (tid == 0) s_child = -1;
+        __syncthreads();
+        if (tid < n && s_par[tid] == v && s_tok[tid] == am.i) s_child = tid;
+        __syncthreads();
+        const int w = s_child;
+        __syncthreads();
+        if (tid == 0) out.out_tokens[(size_t)req * (B + 1) + nacc] = am.i;
+        if (w < 0) break;
+        if (tid == 0) out.path[(size_t)req * B + nacc] = w;
+        ++nacc;
+        v = w;
+        row = w + 1;
+    }
+    if (tid == 0) {
+        out.accept_len[req] = nacc;
+        out.n_out[req] = nacc + 1;
+    }
+}
+
+hipError_t launch_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target,
+                                const dt_verify_out* out, hipStream_t st) {
+    if (p->logits_dtype == DT_BF16)
+        hipLaunchKernelGGL(k_verify_greedy<true>, dim3(p->R), dim3(1024), 0, st, p->B, p->V,
+                           p->Ncap, target, *tree, *out);
+    else
+        hipLaunchKernelGGL(k_verify_greedy<false>, dim3(p->R), dim3(1024), 0, st, p->B, p->V,
+                           p->Ncap, target, *tree, *out);
+    return hipGetLastError();
+}
+
+
+// =======================================================================================
+// Lossless sample verify (TreeSpark lossless section).  The requests walk in lock-step,
+// one node per step; a step is two launches:
+//   k_vs_rows  - for every request still walking at a node of depth < B: the node's draft
+//                row y_q = (L[d] + U[t] . Wt) * log2(e)/T on MFMA (same tile as expansion),
+//                stored to vrow, plus per-split (max, sum) of y_q and of the target row;
+//   k_vs_chain - one workgroup per request: the normalisers, then recursive rejection over
+//                the k drawn siblings in draw order, then the final draw and the move.
+// Residuals in closed form: after j rejections the target law is max(p - a_j q, 0) / S_j
+// with a_0 = 0, S_0 = 1, a_{j+1} = a_j + S_j / c_j, c_j = 1 - (q mass of the rejected
+// siblings), S_{j+1} = sum max(p - a_{j+1} q, 0), and the draft law is q / c_j on the
+// siblings not yet tried.  This equals the literal update p_{j+1} = max(p_j - q_j, 0)/Z,
+// q_{j+1} = q_j without x_j renormalised (induction on j: a rejected x_j has
+// p_j(x_j) < q_j(x_j), so it stays at zero residual for every later a).  Acceptance of x_j:
+// u_j * q(x_j) * S_j < max(p(x_j) - a_j q(x_j), 0) * c_j.
+// =======================================================================================
+__global__ __launch_bounds__(256) void k_vs_init(int R, int B, uint32_t round,
+                                                 const int32_t* root_token, dt_tree tree,
+                                                 VState* state, dt_verify_out out) {
+    const int req = blockIdx.x * blockDim.x + threadIdx.x;
+    if (req >= R) return;
+    VState s;
+    s.active = (tree.status[req] & DT_REQ_BAD_ROOT) ? 0 : 1;
+    s.v = -1;
+    s.row = 0;
+    s.depth = 0;
+    s.token = root_token[req];
+    s.nacc = 0;
+    s.nemit = 0;
+    s.pad = 0;
+    s.hash = root_hash(round, req, s.token);
+    state[req] = s;
+    for (int i = 0; i < B; ++i) out.path[(size_t)req * B + i] = -1;
+    for (int i = 0; i <= B; ++i) out.out_tokens[(size_t)req * (B + 1) + i] = -1;
+    out.accept_len[req] = 0;
+    out.n_out[req] = 0;
+}
+
+struct VsArgs {
+    const void* L;
+    const void* U;
+    const void* Wt;
+    const void* target;
+    const VState* state;
+    float* vrow;
+    float* vpart;
+    int R, B, V, r, Ncap, NC, S;
+    float y2scale;
+    int bf16;
+};
+
+template <bool HEAD_BF16>
+__global__ __launch_bounds__(256) void k_vs_rows(const VsArgs a) {
+    const int T = (a.R + kTileRows - 1) / kTileRows;
+    const int tile = blockIdx.x / a.S, split = blockIdx.x % a.S;
+    if (tile >= T) return;
+    const int m0 = tile * kTileRows;
+    const int nrows = min(kTileRows, a.R - m0);
+    __shared__ __attribute__((aligned(16))) uint16_t sA[HEAD_BF16 ? kTileRows * kAStride : 1];
+    __shared__ __attribute__((aligned(16))) float sAf[HEAD_BF16 ? 1 : kTileRows * kAfStride];
+    __shared__ float sZ[kTileRows * kZStride];
+    __shared__ int sLive[kTileRows];
+    __shared__ int sAny;
+    const int tid = threadIdx.x;
+    if (tid == 0) sAny = 0;
+    __syncthreads();
+    if (tid < kTileRows) {
+        int live = 0;
+        if (tid < nrows) {
+            const VState& s = a.state[m0 + tid];
+            live = s.active && s.depth < a.B;
+        }
+        sLive[tid] = live;
+        if (live) atomicOr(&sAny, 1);
+    }
+    __syncthreads();
+    if (!sAny) return;
+    load_a_tile<HEAD_BF16>(a.U, a.r, nrows, [&](int row) {
+        return sLive[row] ? a.state[m0 + row].token : 0;
+    }, sA, sAf);
+    __syncthreads();
+
+    const int erow = tid >> 2, epart = tid & 3;
+    const bool eactive = erow < nrows && sLive[erow];
+    const int req = m0 + erow;
+    VState st;
+    if (eactive) st = a.state[req];
+    const size_t lbase = eactive ? ((size_t)req * a.B + st.depth) * (size_t)a.V : 0;
+    const size_t tbase = eactive ? ((size_t)req * (a.Ncap + 1) + st.row) * (size_t)a.V : 0;
+    Lse2 lq, lp;
+    lq.init();
+    lp.init();
+    const int c_beg = (int)((long long)split * a.NC / a.S);
+    const int c_end = (int)((long long)(split + 1) * a.NC / a.S);
+    const bool two = nrows > 32;
+    for (int c = c_beg; c < c_end; ++c) {
+        const int col0 = c * kChunkCols;
+        mma_chunk<HEAD_BF16>(a.Wt, a.V, a.r, col0, two, sA, sAf, sZ);
+        if (eactive) {
+            const int cb = col0 + epart * 32;
+            const float* zr = sZ + erow * kZStride + epart * 32;
+            float* vr = a.vrow + (size_t)req * a.V;
+            float mq = -INFINITY, mp = -INFINITY;
+            float yq[32], yp[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const int x = cb + j;
+                if (x < a.V) {
+                    yq[j] = (zr[j] + load_logit(a.L, lbase + x, a.bf16)) * a.y2scale;
+                    yp[j] = load_logit(a.target, tbase + x, a.bf16) * a.y2scale;
+                    vr[x] = yq[j];
+                    mq = fmaxf(mq, yq[j]);
+                    mp = fmaxf(mp, yp[j]);
+                } else {
+                    yq[j] = -INFINITY;
+                    yp[j] = -INFINITY;
+                }
+            }
+            float sq = 0.0f, sp = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                if (cb + j < a.V) {
+                    sq += exp2f(yq[j] - mq);
+                    sp += exp2f(yp[j] - mp);
+                }
+            }
+            if (mq != -INFINITY) {
+                lq.merge(mq, sq);
+                lp.merge(mp, sp);
+            }
+        }
+        __syncthreads();
+    }
+    lq.merge_xor(1);
+    lq.merge_xor(2);
+    lp.merge_xor(1);
+    lp.merge_xor(2);
+    if (eactive && epart == 0) {
+        float* rec = a.vpart + ((size_t)req * a.S + split) * 4;
+        rec[0] = lq.m;
+        rec[1] = lq.s;
+        rec[2] = lp.m;
+        rec[3] = lp.s;
+    }
+}
+
+// Block-wide float sum in a fixed order (deterministic); every thread gets the total.
+__device__ float block_sum_f(float v, float* sh) {
+    const int tid = threadIdx.x, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();
+    if ((tid & 63) == 0) sh[tid >> 6] = v;
+    __syncthreads();
+    float t = 0.0f;
+    for (int i = 0; i < nw; ++i) t += sh[i];
+    return t;
+}
+
+struct ChainArgs {
+    const void* target;
+    VState* state;
+    float* vrow;
+    float* vprow;
+    const float* vpart;
+    dt_tree tree;
+    dt_verify_out out;
+    int R, B, V, k, Ncap, S;
+    float y2scale, invT;
+    uint32_t seed_lo, seed_hi;
+    int bf16;
+};
+
+__global__ __launch_bounds__(1024) void k_vs_chain(const ChainArgs a) {
+    __shared__ float shf[16];
+    __shared__ ArgMax sha[16];
+    __shared__ Lse2 shl[2][16];
+    __shared__ int s_tok[kMaxNcap], s_par[kMaxNcap];
+    const int req = blockIdx.x, tid = threadIdx.x;
+    VState st = a.state[req];
+    if (!st.active) return;
+    const int n = a.tree.n_nodes[req];
+    if (tid < a.Ncap) {
+        s_tok[tid] = a.tree.token[(size_t)req * a.Ncap + tid];
+        s_par[tid] = a.tree.parent[(size_t)req * a.Ncap + tid];
+    }
+    const size_t tbase = ((size_t)req * (a.Ncap + 1) + st.row) * (size_t)a.V;
+    float* q = a.vrow + (size_t)req * a.V;
+    float* p = a.vprow + (size_t)req * a.V;
+    int emitted = -1;
+    bool descend = false;
+
+    if (st.depth == a.B) {
+        // a draw from p: Gumbel-max over target / T
+        ArgMax best{-INFINITY, 0x7fffffff};
+        for (int g = tid; 4 * g < a.V; g += blockDim.x) {
+            const uint4 w = rand4((uint32_t)g, STREAM_RESID, st.hash, a.seed_lo, a.seed_hi);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int x = 4 * g + e;
+                if (x < a.V)
+                    best = amax(best, ArgMax{load_logit(a.target, tbase + x, a.bf16) * a.invT +
+                                             gumbel(ws[e]), x});
+            }
+        }
+        best = wave_amax(best);
+        __syncthreads();
+        if ((tid & 63) == 0) sha[tid >> 6] = best;
+        __syncthreads();
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) best = amax(best, sha[i]);
+        emitted = best.i;
+    } else {
+        // normalisers of q and p (log2 units)
+        Lse2 lq, lp;
+        lq.init();
+        lp.init();
+        for (int s = tid; s < a.S; s += blockDim.x) {
+            const float* rec = a.vpart + ((size_t)req * a.S + s) * 4;
+            lq.merge(rec[0], rec[1]);
+            lp.merge(rec[2], rec[3]);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            lq.merge_xor(off);
+            lp.merge_xor(off);
+        }
+        if ((tid & 63) == 0) {
+            shl[0][tid >> 6] = lq;
+            shl[1][tid >> 6] = lp;
+        }
+        __syncthreads();
+        lq.init();
+        lp.init();
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+            lq.merge(shl[0][i].m, shl[0][i].s);
+            lp.merge(shl[1][i].m, shl[1][i].s);
+        }
+        const float lse_q = lq.m + log2f(lq.s), lse_p = lp.m + log2f(lp.s);
+        for (int x = tid; x < a.V; x += blockDim.x) {
+            q[x] = exp2f(q[x] - lse_q);
+            p[x] = exp2f(load_logit(a.target, tbase + x, a.bf16) * a.y2scale - lse_p);
+        }
+        __syncthreads();
+        const int32_t* cand = a.tree.cand + ((size_t)req * (a.Ncap + 1) + st.row) * a.k;
+        float alpha = 0.0f, S = 1.0f, c = 1.0f;
+        for (int j = 0; j < a.k; ++j) {
+            const int x = cand[j];
+            const float qx = q[x], px = p[x];
+            const uint4 w = rand4((uint32_t)(j >> 2), STREAM_ACCEPT, st.hash, a.seed_lo, a.seed_hi);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            const float u = u01(ws[j & 3]);
+            if (u * qx * S < fmaxf(px - alpha * qx, 0.0f) * c) {
+                emitted = x;
+                descend = true;
+                break;
+            }
+            alpha += S / c;
+            c -= qx;
+            float part = 0.0f;
+            for (int y = tid; y < a.V; y += blockDim.x) part += fmaxf(p[y] - alpha * q[y], 0.0f);
+            S = block_sum_f(part, shf);
+            if (!(S > 0.0f)) {
+                emitted = x;
+                descend = true;
+                break;
+            }
+        }
+        if (emitted < 0) {
+            // every sibling rejected: a draw from the residual max(p - alpha q, 0)
+            ArgMax best{-INFINITY, 0x7fffffff};
+            for (int g = tid; 4 * g < a.V; g += blockDim.x) {
+                const uint4 w = rand4((uint32_t)g, STREAM_RESID, st.hash, a.seed_lo, a.seed_hi);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int x = 4 * g + e;
+                    if (x < a.V) {
+                        const float d = p[x] - alpha * q[x];
+                        if (d > 0.0f) best = amax(best, ArgMax{logf(d) + gumbel(ws[e]), x});
+                    }
+                }
+            }
+            best = wave_amax(best);
+            __syncthreads();
+            if ((tid & 63) == 0) sha[tid >> 6] = best;
+            __syncthreads();
+            for (int i = 0; i < (int)(blockDim.x >> 6); ++i) best = amax(best, sha[i]);
+            emitted = best.i;
+        }
+    }
+    __syncthreads();
+    int w = -1;
+    if (descend) {
+        for (int i = 0; i < n; ++i)
+            if (s_par[i] == st.v && s_tok[i] == emitted) w = i;
+    }
+    if (tid == 0) {
+        a.out.out_tokens[(size_t)req * (a.B + 1) + st.nemit] = emitted;
+        st.nemit += 1;
+        if (w >= 0) {
+            a.out.path[(size_t)req * a.B + st.nacc] = w;
+            st.nacc += 1;
+            st.v = w;
+            st.row = w + 1;
+            st.depth += 1;
+            st.token = emitted;
+            st.hash = child_hash(st.hash, emitted);
+        } else {
+            st.active = 0;
+            a.out.accept_len[req] = st.nacc;
+            a.out.n_out[req] = st.nemit;
+        }
+        a.state[req] = st;
+    }
+}
+
+hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
+                                const dt_tree* tree, const void* L, const void* U,
+                                const void* Wt, const int32_t* root_token, const void* target,
+                                const dt_verify_out* out, hipStream_t st) {
+    VState* state = (VState*)(ws + lay.vstate);
+    hipLaunchKernelGGL(k_vs_init, dim3((p->R + 255) / 256), dim3(256), 0, st, p->R, p->B,
+                       p->round, root_token, *tree, state, *out);
+    VsArgs va{};
+    va.L = L;
+    va.U = U;
+    va.Wt = Wt;
+    va.target = target;
+    va.state = state;
+    va.vrow = (float*)(ws + lay.vrow);
+    va.vpart = (float*)(ws + lay.vpart);
+    va.R = p->R;
+    va.B = p->B;
+    va.V = p->V;
+    va.r = p->r;
+    va.Ncap = p->Ncap;
+    va.NC = lay.NC;
+    va.S = lay.vsplits;
+    va.y2scale = (float)(1.4426950408889634 / (double)p->temperature);
+    va.bf16 = p->logits_dtype == DT_BF16;
+    ChainArgs ca{};
+    ca.target = target;
+    ca.state = state;
+    ca.vrow = va.vrow;
+    ca.vprow = (float*)(ws + lay.vprow);
+    ca.vpart = va.vpart;
+    ca.tree = *tree;
+    ca.out = *out;
+    ca.R = p->R;
+    ca.B = p->B;
+    ca.V = p->V;
+    ca.k = p->k;
+    ca.Ncap = p->Ncap;
+    ca.S = lay.vsplits;
+    ca.y2scale = va.y2scale;
+    ca.invT = (float)(1.0 / (double)p->temperature);
+    ca.seed_lo = (uint32_t)p->seed;
+    ca.seed_hi = (uint32_t)(p->seed >> 32);
+    ca.bf16 = va.bf16;
+    const int tiles = (p->R + kTileRows - 1) / kTileRows;
+    const dim3 grid(tiles * lay.vsplits);
+    for (int step = 0; step <= p->B; ++step) {
+        if (p->head_dtype == DT_BF16)
+            hipLaunchKernelGGL(k_vs_rows<true>, grid, dim3(256), 0, st, va);
+        else
+            hipLaunchKernelGGL(k_vs_rows<false>, grid, dim3(256), 0, st, va);
+        hipLaunchKernelGGL(k_vs_chain, dim3(p->R), dim3(1024), 0, st, ca);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dt

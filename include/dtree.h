@@ -1,0 +1,167 @@
+/* dtree.h - C ABI of libdtree.so: parent-conditioned draft-tree construction and
+ * verification for a semi-autoregressive block drafter, on one AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *  - "From Chains to Trees: Parent-Conditioned Drafting for Semi-Autoregressive Speculative
+ *    Decoding" (PCTree summary): one backbone forward gives logits for every position of the
+ *    block; a light Markov head biases the block by the previous token; the chain becomes a
+ *    budget-limited tree with k children per parent and N nodes (method paragraph, main
+ *    setting k = 4, N = 32); k = 1 is the greedy chain; verification is greedy.
+ *  - "TreeSpark: adaptive draft trees" (kongchang article): the parent-conditioned
+ *    distribution is calibrated to an edge-acceptance estimate, path survival (the product
+ *    of edge estimates) drives best-first expansion and per-round stopping, and lossless
+ *    decoding samples siblings without replacement and matches residuals in recursive
+ *    rejection (core-idea and lossless sections).
+ *
+ * Conventions shared by every call
+ *  - Every array pointer is caller-owned DEVICE memory (e.g. from PyTorch) unless noted;
+ *    the library never allocates or frees device memory and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work; outputs
+ *    are valid once the stream has been synchronised.  Calls on different streams with
+ *    different workspaces are independent.
+ *  - Host-side argument errors return synchronously before anything is enqueued.
+ *    Device-side data errors are reported per request in `status` and never abort.
+ *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *
+ * Markov head form: bias[p][c] = sum_j U[p][j] * W[j][c], a rank-r head shared by all block
+ * positions (the pages fix what the head does, not its form).  W is passed TRANSPOSED,
+ * as Wt[V][r] (row c holds W[:, c]), so both tables are row-per-token.
+ */
+#ifndef DTREE_H
+#define DTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DT_OK = 0,
+    DT_EINVAL = 1,  /* bad argument (checked on the host, nothing enqueued) */
+    DT_ENOSPC = 2,  /* workspace smaller than dt_build_workspace_bytes() */
+    DT_EDEVICE = 3  /* a HIP call or kernel launch failed */
+} dt_status;
+
+enum { DT_F32 = 0, DT_BF16 = 1 };   /* storage dtypes */
+enum { DT_GREEDY = 0, DT_SAMPLE = 1 };
+
+/* Per-request status bits written to dt_tree.status. */
+enum {
+    DT_REQ_BAD_ROOT = 1,       /* root_token outside [0, V): empty tree, nothing emitted */
+    DT_REQ_BUDGET_CLAMPED = 2  /* n_budget outside [0, Ncap]: clamped into range */
+};
+
+/* Round parameters (host struct, read synchronously). */
+typedef struct dt_params {
+    int32_t R;            /* requests in the batch, >= 1 */
+    int32_t B;            /* block positions = maximum tree depth, 1..32 */
+    int32_t k;            /* children per expanded parent, 1..8, k <= V */
+    int32_t V;            /* vocabulary size, 1..2^24 */
+    int32_t r;            /* Markov-head rank: bf16 head 8..256 and a multiple of 8; f32 head 1..64 */
+    int32_t Ncap;         /* node capacity per request (tree arrays' width), 1..64 */
+    int32_t logits_dtype; /* DT_BF16 | DT_F32: block logits and target logits */
+    int32_t head_dtype;   /* DT_BF16 | DT_F32: U and Wt */
+    int32_t mode;         /* DT_GREEDY: rank children by logit, q at T = 1.
+                             DT_SAMPLE: Gumbel-top-k children, q at `temperature`. */
+    float temperature;    /* > 0, finite; used in DT_SAMPLE mode */
+    float cal[16];        /* calibration table: edge estimate for q in [i/16, (i+1)/16);
+                             values in [0, 1] and non-decreasing */
+    uint64_t seed;        /* key of the counter-based generator (sample mode) */
+    uint32_t round;       /* round counter, folded into every node's random stream */
+    uint32_t reserved;    /* must be 0 */
+} dt_params;
+
+/* Emitted trees.  Node order is canonical: depth ascending, then the path of sibling ranks
+ * from the root ascending (parents precede children).  Slots >= n_nodes hold token -1,
+ * parent -2, depth 0, mask 0, surv 0, logq 0. */
+typedef struct dt_tree {
+    int32_t* token;     /* [R][Ncap] draft token of each node */
+    int16_t* parent;    /* [R][Ncap] parent's node index; -1 = the root */
+    uint8_t* depth;     /* [R][Ncap] 1..B */
+    uint64_t* anc_mask; /* [R][Ncap] bit j set iff node j is this node or one of its
+                           ancestors (the root is not a node): the tree-attention mask */
+    float* surv;        /* [R][Ncap] path survival (float32 product of table entries) */
+    float* logq;        /* [R][Ncap] log of the node's probability under its parent's
+                           parent-conditioned draft distribution */
+    int32_t* n_nodes;   /* [R] */
+    int32_t* cand;      /* [R][Ncap+1][k] ranked children of every expanded node: row 0 =
+                           the root, row i+1 = node i; -1 for nodes never expanded */
+    int32_t* status;    /* [R] DT_REQ_* bits */
+    int32_t* n_expand;  /* [R] optional (NULL = not written): expansions made */
+    int32_t* level_rows;/* [B] optional (NULL = not written): parents expanded at each
+                           level, summed over requests */
+} dt_tree;
+
+/* Verification outputs. */
+typedef struct dt_verify_out {
+    int32_t* accept_len; /* [R] accepted tree nodes (0..B) */
+    int32_t* path;       /* [R][B] accepted node indices in order, -1 padded */
+    int32_t* out_tokens; /* [R][B+1] accepted tokens, then the round's final token, -1 pad */
+    int32_t* n_out;      /* [R] tokens emitted this round: accept_len + 1 (0 for a bad root) */
+} dt_verify_out;
+
+/* Workspace needed by tree_build, tree_verify_greedy and tree_verify_sample for these
+ * parameters (one size covers all three).  Writes *bytes on the host.  DT_EINVAL on bad
+ * parameters. */
+dt_status dt_build_workspace_bytes(const dt_params* p, size_t* bytes);
+
+/* Build one round's draft trees for R requests.
+ *  block_logits [R][B][V]  (logits_dtype): row d of request i = the drafter's logits for
+ *                          block position d; a node at depth d is expanded with row d
+ *  U            [V][r]     (head_dtype): parent-token embedding of the Markov head
+ *  Wt           [V][r]     (head_dtype): W transposed (child-token embedding)
+ *  root_token   [R] int32: the last committed token (depth 0; not a node)
+ *  n_budget     [R] int32: node budget N per request, 0..Ncap
+ *  tau          [R] float: stopping threshold; nodes with survival < tau are never kept
+ *                          (tau <= 0 disables stopping)
+ *  out          host struct of device pointers (dt_tree), fully overwritten
+ * Expansion of node v (token t, depth d): z[c] = L[d][c] + U[t] . Wt[c]; q = softmax(z / T')
+ * with T' = 1 (greedy) or temperature (sample); the k children are the largest z (greedy;
+ * ties to the lower token id) or the largest z/T + Gumbel noise (sample); a child's survival
+ * is fl32(s_parent * cal[min(15, floor(16 q))]), the root's is 1; logq = log q.  The tree is
+ * the best n_budget nodes with survival >= tau under the order (survival desc, depth asc,
+ * sibling-rank path asc), which equals best-first expansion with per-round stopping. */
+dt_status tree_build(const dt_params* p, const void* block_logits, const void* U,
+                     const void* Wt, const int32_t* root_token, const int32_t* n_budget,
+                     const float* tau, const dt_tree* out, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Greedy accept-walk (PCTree setup: greedy verification).
+ *  tree          the dt_tree written by tree_build (device arrays; read only)
+ *  target_logits [R][Ncap+1][V] (logits_dtype): row 0 = the root, row i+1 = node i
+ * From the root: t* = argmax of the current row (ties: lower id); if a child of the current
+ * node carries t*, accept it and continue from it; otherwise t* is the final (bonus) token. */
+dt_status tree_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target_logits,
+                             const dt_verify_out* out, void* workspace, size_t ws_bytes,
+                             void* stream);
+
+/* Lossless sample verify (TreeSpark lossless section), p->mode must be DT_SAMPLE and the
+ * tree built in that mode with the same seed and round.  At each visited node v:
+ * p = softmax(target_row / T), q = softmax(z_v / T) (recomputed from block_logits, U, Wt);
+ * the k drawn siblings cand[v] are tried in draw order; x_j is accepted iff
+ * u_j * q_j(x_j) < p_j(x_j), else p and q become the residual laws
+ * p_{j+1} = max(p_j - q_j, 0) / Z and q_{j+1} = q_j without x_j, renormalised.  An accepted
+ * sibling that is a tree node is descended into; one that is not ends the round; if all are
+ * rejected the round ends with a draw from the final residual; at depth B it ends with a
+ * draw from p. */
+dt_status tree_verify_sample(const dt_params* p, const dt_tree* tree, const void* block_logits,
+                             const void* U, const void* Wt, const int32_t* root_token,
+                             const void* target_logits, const dt_verify_out* out,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* dt_status_string(dt_status s);
+
+/* Measurement support (host only, not thread-safe): when enabled, the library brackets each
+ * launch of the fused Markov-bias/top-k kernel with HIP events on the caller's stream.
+ * dt_timing_read() synchronises those events and returns the summed kernel time and the
+ * number of timed launches since the last enable, then clears the record. */
+dt_status dt_timing_enable(int32_t on);
+dt_status dt_timing_read(double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DTREE_H */

@@ -1,0 +1,108 @@
+"""C ABI checks that need no GPU: the library loads, exports every function that
+include/dtree.h declares, sizes its workspace, and rejects bad arguments on the host before
+enqueuing anything (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from draft_tree_construction_rank_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dtree.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libdtree.so is not built; run __graft_entry__.build()")
+    return B.lib()
+
+
+def test_header_declares_the_abi():
+    names = _declared()
+    for fn in B.EXPORTED:
+        assert fn in names, fn
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for fn in _declared():
+        assert fn in syms, fn
+        assert getattr(lib, fn) is not None
+
+
+def _params(**kw):
+    base = dict(R=2, B=4, k=2, V=64, r=8, Ncap=8, logits_dtype=B.DT_F32, head_dtype=B.DT_F32,
+                mode=B.DT_GREEDY, temperature=1.0, cal=[(i + 0.5) / 16 for i in range(16)])
+    base.update(kw)
+    return B.make_params(**base)
+
+
+def test_workspace_size_is_positive_and_monotone(lib):
+    a = B.dt_build_workspace_bytes(_params())
+    b = B.dt_build_workspace_bytes(_params(R=4))
+    c = B.dt_build_workspace_bytes(_params(mode=B.DT_SAMPLE))
+    assert 0 < a < b and a < c
+
+
+BAD = [
+    dict(R=0), dict(R=5000), dict(B=0), dict(B=33), dict(k=0), dict(k=9), dict(V=0),
+    dict(V=4, k=5), dict(Ncap=0), dict(Ncap=65), dict(logits_dtype=7), dict(head_dtype=3),
+    dict(mode=2), dict(head_dtype=B.DT_BF16, r=12), dict(head_dtype=B.DT_BF16, r=264),
+    dict(r=65), dict(r=0), dict(temperature=0.0), dict(temperature=float("nan")),
+    dict(temperature=-1.0), dict(cal=[0.5] * 15 + [1.5]), dict(cal=[0.9] + [0.5] * 15),
+    dict(cal=[float("nan")] * 16),
+]
+
+
+@pytest.mark.parametrize("kw", BAD, ids=lambda d: ",".join("%s" % k for k in d))
+def test_bad_params_rejected_on_host(lib, kw):
+    p = _params(**kw)
+    n = C.c_size_t(0)
+    assert lib.dt_build_workspace_bytes(C.byref(p), C.byref(n)) == B.DT_EINVAL
+    t = B.dt_tree()
+    assert lib.tree_build(C.byref(p), 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                          C.byref(t), 0x1000, 1 << 30, None) == B.DT_EINVAL
+
+
+def test_null_pointers_and_small_workspace_rejected(lib):
+    p = _params()
+    t = B.dt_tree()
+    for f, _ in B.dt_tree._fields_:
+        setattr(t, f, 0x2000)
+    fake = 0x10000
+    assert lib.tree_build(C.byref(p), None, fake, fake, fake, fake, fake, C.byref(t), fake,
+                          1 << 30, None) == B.DT_EINVAL
+    t.token = None
+    assert lib.tree_build(C.byref(p), fake, fake, fake, fake, fake, fake, C.byref(t), fake,
+                          1 << 30, None) == B.DT_EINVAL
+    t.token = 0x2000
+    need = B.dt_build_workspace_bytes(p)
+    assert lib.tree_build(C.byref(p), fake, fake, fake, fake, fake, fake, C.byref(t), fake,
+                          need - 1, None) == B.DT_ENOSPC
+    # misaligned workspace
+    assert lib.tree_build(C.byref(p), fake, fake, fake, fake, fake, fake, C.byref(t), fake + 8,
+                          need, None) == B.DT_EINVAL
+    # sample verify in greedy mode
+    v = B.dt_verify_out()
+    for f, _ in B.dt_verify_out._fields_:
+        setattr(v, f, 0x3000)
+    assert lib.tree_verify_sample(C.byref(p), C.byref(t), fake, fake, fake, fake, fake,
+                                  C.byref(v), fake, need, None) == B.DT_EINVAL
+
+
+def test_status_strings(lib):
+    for code in range(4):
+        assert B.status_string(code).startswith("DT_")

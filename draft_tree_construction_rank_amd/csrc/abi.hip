@@ -24,10 +24,13 @@ Layout make_layout(const dt_params* p) {
     const size_t R = p->R, B = p->B, N = p->Ncap, k = p->k, V = p->V;
     L.NC = (int)((V + kChunkCols - 1) / kChunkCols);
     L.KT = kt_for(p->k);
-    const int tmax = (int)((R * N + kTileRows - 1) / kTileRows);
-    L.G = tmax > 1024 ? tmax : 1024;
+    L.G = 512;
+    const size_t tmax = (R * N + kTileRows - 1) / kTileRows;
+    const size_t cap_rows = (size_t)kTileRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
+    L.sync = take(kSyncWords * sizeof(unsigned));
+    L.roff = take(R * sizeof(int));
+    L.pdone = take(R * sizeof(int));
     L.rows = take(R * N * sizeof(int2));
-    L.ctl = take(8 * sizeof(int));
     L.front = take(R * (B + 1) * N * sizeof(FrontEntry));
     L.fcount = take(R * (B + 1) * sizeof(int));
     L.arena = take(R * B * N * k * sizeof(ChildRec));
@@ -36,7 +39,7 @@ Layout make_layout(const dt_params* p) {
     L.scount = take(R * sizeof(int));
     L.nbeff = take(R * sizeof(int));
     L.rstat = take(R * sizeof(int));
-    L.partials = take((size_t)kTileRows * L.G * (2 + 3 * L.KT) * sizeof(float));
+    L.partials = take(cap_rows * rec_floats(L.KT) * sizeof(float));
     L.vsplits = 0;
     L.vrow = L.vprow = L.vstate = L.vpart = 0;
     if (p->mode == DT_SAMPLE) {
@@ -107,6 +110,8 @@ static void timing_mark(hipStream_t st) {
     (void)hipEventRecord(g_timing.pool[g_timing.used++], st);
 }
 
+static void timing_hook(hipStream_t st, int) { timing_mark(st); }
+
 }  // namespace dt
 
 using namespace dt;
@@ -147,73 +152,45 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
 
-    if (launch_build_init(p, lay, ws, root_token, n_budget, out->level_rows, st) != hipSuccess)
-        return DT_EDEVICE;
-
     const float Teff = (p->mode == DT_SAMPLE) ? p->temperature : 1.0f;
-    ExpandArgs ea{};
-    ea.L = block_logits;
-    ea.U = U;
-    ea.Wt = Wt;
-    ea.rows = (const int2*)(ws + lay.rows);
-    ea.ctl = (const int*)(ws + lay.ctl);
-    ea.front = (const FrontEntry*)(ws + lay.front);
-    ea.partials = (float*)(ws + lay.partials);
-    ea.R = p->R;
-    ea.B = p->B;
-    ea.V = p->V;
-    ea.r = p->r;
-    ea.Ncap = p->Ncap;
-    ea.G = lay.G;
-    ea.NC = lay.NC;
-    ea.y2scale = (float)(1.4426950408889634 / (double)Teff);
-    ea.invT = (float)(1.0 / (double)Teff);
-    ea.seed_lo = (uint32_t)p->seed;
-    ea.seed_hi = (uint32_t)(p->seed >> 32);
-    ea.logits_bf16 = p->logits_dtype == DT_BF16;
+    BuildArgs a{};
+    a.timing_hook = g_timing.on ? timing_hook : nullptr;
+    a.L = block_logits;
+    a.U = U;
+    a.Wt = Wt;
+    a.root_token = root_token;
+    a.n_budget = n_budget;
+    a.tau = tau;
+    a.sync = (unsigned*)(ws + lay.sync);
+    a.rows = (int2*)(ws + lay.rows);
+    a.roff = (int*)(ws + lay.roff);
+    a.pdone = (int*)(ws + lay.pdone);
+    a.front = (FrontEntry*)(ws + lay.front);
+    a.fcount = (int*)(ws + lay.fcount);
+    a.arena = (ChildRec*)(ws + lay.arena);
+    a.ckeys = (uint64_t*)(ws + lay.ckeys);
+    a.skeys = (uint64_t*)(ws + lay.skeys);
+    a.scount = (int*)(ws + lay.scount);
+    a.nbeff = (int*)(ws + lay.nbeff);
+    a.rstat = (int*)(ws + lay.rstat);
+    a.partials = (float*)(ws + lay.partials);
+    a.out = *out;
+    a.R = p->R;
+    a.B = p->B;
+    a.k = p->k;
+    a.V = p->V;
+    a.r = p->r;
+    a.Ncap = p->Ncap;
+    a.NC = lay.NC;
+    a.y2scale = (float)(1.4426950408889634 / (double)Teff);
+    a.invT = (float)(1.0 / (double)Teff);
+    a.seed_lo = (uint32_t)p->seed;
+    a.seed_hi = (uint32_t)(p->seed >> 32);
+    a.round = p->round;
+    a.logits_bf16 = p->logits_dtype == DT_BF16;
+    for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
 
-    MergeArgs ma{};
-    ma.rows = ea.rows;
-    ma.ctl = ea.ctl;
-    ma.partials = ea.partials;
-    ma.front = ea.front;
-    ma.arena = (ChildRec*)(ws + lay.arena);
-    ma.ckeys = (uint64_t*)(ws + lay.ckeys);
-    ma.R = p->R;
-    ma.B = p->B;
-    ma.k = p->k;
-    ma.Ncap = p->Ncap;
-    ma.G = lay.G;
-    ma.NC = lay.NC;
-    ma.KT = lay.KT;
-    for (int i = 0; i < 16; ++i) ma.cal[i] = p->cal[i];
-
-    SelectArgs sa{};
-    sa.rows = (int2*)(ws + lay.rows);
-    sa.ctl = (int*)(ws + lay.ctl);
-    sa.front = (FrontEntry*)(ws + lay.front);
-    sa.fcount = (int*)(ws + lay.fcount);
-    sa.arena = ma.arena;
-    sa.ckeys = ma.ckeys;
-    sa.skeys = (uint64_t*)(ws + lay.skeys);
-    sa.scount = (int*)(ws + lay.scount);
-    sa.nbeff = (const int*)(ws + lay.nbeff);
-    sa.tau = tau;
-    sa.level_rows = out->level_rows;
-    sa.R = p->R;
-    sa.B = p->B;
-    sa.k = p->k;
-    sa.Ncap = p->Ncap;
-
-    for (int level = 1; level <= p->B; ++level) {
-        ea.level = ma.level = sa.level = level;
-        timing_mark(st);
-        if (launch_expand(p, lay, ea, st) != hipSuccess) return DT_EDEVICE;
-        timing_mark(st);
-        if (launch_merge(p, lay, ma, st) != hipSuccess) return DT_EDEVICE;
-        if (launch_select(p, sa, st) != hipSuccess) return DT_EDEVICE;
-    }
-    if (launch_emit(p, lay, ws, out, st) != hipSuccess) return DT_EDEVICE;
+    if (launch_build(p, lay, a, st) != hipSuccess) return DT_EDEVICE;
     return DT_OK;
 }
 

@@ -23,13 +23,25 @@ __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, Tok
                                             uint16_t* sA, float* sAf) {
     const int tid = threadIdx.x;
     if constexpr (HEAD_BF16) {
-        const int segs = kAStride / 8;  // 16-byte segments per LDS row (incl. padding)
-        for (int i = tid; i < kTileRows * segs; i += 256) {
+        // 64 rows x 33 16-byte segments: every address is clamped into the row so that all
+        // loads of a thread are unconditional and can be in flight together.
+        constexpr int segs = kAStride / 8;
+        constexpr int per = (kTileRows * segs + 255) / 256;
+        uint4 v[per];
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            const int i = tid + q * 256;
             const int row = i / segs, seg = i % segs;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row < nrows && seg * 8 < r)
-                v = *(const uint4*)((const uint16_t*)U + (size_t)token_of(row) * r + seg * 8);
-            *(uint4*)(sA + row * kAStride + seg * 8) = v;
+            const bool ok = i < kTileRows * segs && row < nrows && seg * 8 < r;
+            const int tok = (i < kTileRows * segs && row < nrows) ? token_of(row) : 0;
+            const uint4 x = *(const uint4*)((const uint16_t*)U + (size_t)tok * r +
+                                            (seg * 8 < r ? seg * 8 : 0));
+            v[q] = ok ? x : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+            const int i = tid + q * 256;
+            if (i < kTileRows * segs) *(uint4*)(sA + (i / segs) * kAStride + (i % segs) * 8) = v[q];
         }
     } else {
         for (int i = tid; i < kTileRows * kAfStride; i += 256) {
@@ -56,27 +68,38 @@ __device__ __forceinline__ void mma_chunk(const void* Wt, int V, int r, int col0
         acc1[i] = 0.0f;
     }
     if constexpr (HEAD_BF16) {
-        const int nsteps = (r + 15) >> 4;
-        bf16x8 bfr[16];
+        // Two halves of 8 K-steps: 8 unconditional 16-byte loads from clamped addresses are
+        // issued back to back, then 8 (or 16) MFMAs.  Columns past V read column V-1 (their
+        // results are never used); K offsets past r read offset 0 (multiplied by the zero
+        // padding of the A tile), so all 16 K-steps always run.
         const int khalf = (lane >> 5) * 8;
+        const uint16_t* wrow = (const uint16_t*)Wt + (size_t)(bcol < V ? bcol : V - 1) * r;
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (s < nsteps && bcol < V && s * 16 + khalf < r)
-                v = *(const uint4*)((const uint16_t*)Wt + (size_t)bcol * r + s * 16 + khalf);
-            bfr[s] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int h = 0; h < 2; ++h) {
+            bf16x8 bfr[8];
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            if (s < nsteps) {
-                const uint4 a0 = *(const uint4*)(sA + (lane & 31) * kAStride + s * 16 + khalf);
-                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
-                                                               bfr[s], acc0, 0, 0, 0);
-                if (two) {
-                    const uint4 a1 =
-                        *(const uint4*)(sA + (32 + (lane & 31)) * kAStride + s * 16 + khalf);
-                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, a1), bfr[s], acc1, 0, 0, 0);
+            for (int s = 0; s < 8; ++s) {
+                const int kk = (h * 8 + s) * 16 + khalf;
+                bfr[s] = __builtin_bit_cast(bf16x8, *(const uint4*)(wrow + (kk < r ? kk : 0)));
+            }
+            if (two) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int ko = (h * 8 + s) * 16 + khalf;
+                    const uint4 a0 = *(const uint4*)(sA + (lane & 31) * kAStride + ko);
+                    const uint4 a1 = *(const uint4*)(sA + (32 + (lane & 31)) * kAStride + ko);
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                                   bfr[s], acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                                   bfr[s], acc1, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const int ko = (h * 8 + s) * 16 + khalf;
+                    const uint4 a0 = *(const uint4*)(sA + (lane & 31) * kAStride + ko);
+                    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0),
+                                                                   bfr[s], acc0, 0, 0, 0);
                 }
             }
         }

@@ -24,12 +24,12 @@ Layout make_layout(const dt_params* p) {
     const size_t R = p->R, B = p->B, N = p->Ncap, k = p->k, V = p->V;
     L.NC = (int)((V + kChunkCols - 1) / kChunkCols);
     L.KT = kt_for(p->k);
-    L.G = 512;
+    L.G = kMaxGrid;
     const size_t tmax = (R * N + kTileRows - 1) / kTileRows;
     const size_t cap_rows = (size_t)kTileRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
     L.sync = take(kSyncWords * sizeof(unsigned));
-    L.roff = take(R * sizeof(int));
-    L.pdone = take(R * sizeof(int));
+    L.tdone = take((size_t)max_tiles((int)R, (int)N) * sizeof(unsigned));
+    L.rdone = take(R * sizeof(unsigned));
     L.rows = take(R * N * sizeof(int2));
     L.front = take(R * (B + 1) * N * sizeof(FrontEntry));
     L.fcount = take(R * (B + 1) * sizeof(int));
@@ -163,8 +163,8 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     a.tau = tau;
     a.sync = (unsigned*)(ws + lay.sync);
     a.rows = (int2*)(ws + lay.rows);
-    a.roff = (int*)(ws + lay.roff);
-    a.pdone = (int*)(ws + lay.pdone);
+    a.tdone = (unsigned*)(ws + lay.tdone);
+    a.rdone = (unsigned*)(ws + lay.rdone);
     a.front = (FrontEntry*)(ws + lay.front);
     a.fcount = (int*)(ws + lay.fcount);
     a.arena = (ChildRec*)(ws + lay.arena);

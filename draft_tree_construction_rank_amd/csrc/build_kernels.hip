@@ -1,21 +1,29 @@
-// Tree construction on gfx950: a level-synchronous loop of two kernels per level.
+// Tree construction on gfx950: a set-up kernel and one persistent kernel per round.
 //
 // The round walks block positions d = 1..B (PCTree summary: every position's logits come
-// from one backbone forward, so a level needs no new drafter pass):
-//   k_expand        - fused Markov bias (bf16 MFMA 32x32x16, fp32 accumulate) + bias-add +
-//                     temperature + online log-sum-exp + per-row top-k (or Gumbel-top-k)
-//                     over a vocabulary split, for every frontier parent of every request;
-//   k_merge_select  - one workgroup per request: combine the splits of each of its parents,
-//                     calibrate each child's probability to an edge estimate and multiply
-//                     survivals (TreeSpark core idea), then keep the best n_budget nodes with
-//                     survival >= tau (best-first with per-round stopping equals this
-//                     expand-then-select because survival never increases along a path) and
-//                     define the next frontier; the last workgroup compacts the next level's
-//                     parent rows across requests.
-// Kernels of a level with no parent rows return at once.  k_build_init and k_emit open and
-// close the round (emit: canonical order and ancestor masks).
+// from one backbone forward, so a level needs no new drafter pass).  Per level, inside the
+// persistent kernel k_build:
+//   expand  - every workgroup takes (tile of 64 parent rows, vocabulary split) items: the
+//             Markov bias of the tile's parents over the split (bf16 MFMA 32x32x16, fp32
+//             accumulate, W as the A operand so that each lane holds one parent row) is added
+//             to the block logits, tempered, and folded into that row's online log-sum-exp
+//             and top-k (or Gumbel-top-k) in registers; z never reaches memory;
+//   merge   - as soon as all splits of a tile are in, workgroups take its parent rows from a
+//             task counter and combine the split records; each child's probability is
+//             calibrated to an edge estimate and multiplied into the path survival
+//             (TreeSpark core idea);
+//   select  - the workgroup that merges a request's last row keeps the best n_budget nodes
+//             with survival >= tau (best-first with per-round stopping equals this
+//             expand-then-select because survival never increases along a path) and defines
+//             the next frontier;
+//   release - the workgroup that finishes the last request lays out the next level's rows
+//             and bumps the generation word every workgroup waits on.
+// A level with no parent rows ends the loop at once (per-round stopping), and the kernel
+// emits the trees.  Workgroups hand data to each other only through agent-coherent accesses
+// (dt_device.h) and counters; every wait is bounded and raises an error flag on time-out.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "dt_device.h"
@@ -48,328 +56,464 @@ __device__ __forceinline__ int block_sum(int v, int* sh) {
     return total;
 }
 
-__device__ __forceinline__ int load_int(const unsigned* p) {
-    return (int)__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Upper bound on the iterations of one bounded wait (each sleeps ~128 cycles): about two
+// seconds, far above any level's work.
+constexpr uint32_t kSpinLimit = 1u << 25;
+
+// Thread 0 waits until *p >= target (or the error flag is set); the result is broadcast to
+// the workgroup.  Returns false on error or time-out.
+__device__ __forceinline__ bool wait_at_least(unsigned* sync, const unsigned* p, unsigned target,
+                                              int* bcast) {
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        uint32_t it = 0;
+        while ((int)(cld32(p) - target) < 0) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it > kSpinLimit) {
+                cst32(sync + kSyncErr, 1u);
+                ok = 0;
+                break;
+            }
+            if ((it & 63u) == 0u && cld32(sync + kSyncErr) != 0u) {
+                ok = 0;
+                break;
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        bcast[0] = ok;
+    }
+    __syncthreads();
+    const bool ok = bcast[0] != 0;
+    __syncthreads();
+    return ok;
 }
 
 // Vocabulary splits for T tiles on a grid of G workgroups: about one item per workgroup,
-// at most kMaxSplits (so that one workgroup can merge a request's records), and a multiple
-// of 8 when >= 8 so that all tiles of one split run on the same XCD (blocks are dealt
-// round-robin to the 8 XCDs) and share that split's W columns in its L2.
-__device__ __forceinline__ int splits_for(int T, int G, int NC) {
+// at most kMaxSplits (so that one workgroup can merge a row's records in one pass), and a
+// multiple of 8 when >= 8 so that all tiles of one split run on the same XCD (blocks are
+// dealt round-robin to the 8 XCDs) and share that split's W rows in its L2.
+__device__ __forceinline__ int splits_for(int T, int G, int NB) {
     int s = T > 0 ? G / T : 1;
     if (s > kMaxSplits) s = kMaxSplits;
     if (s >= 8) s &= ~7;
-    if (s > NC) s = NC;
+    if (s > NB) s = NB;
     if (s < 1) s = 1;
     return s;
 }
 
-// Writes the parent-row list (request, frontier index) for front level `level` from fcount,
-// in request order, and the row count.  One workgroup.
-__device__ __forceinline__ void compact_rows(const BuildArgs& a, int level, int* sh) {
-    const int R = a.R, B = a.B;
-    const int per = (R + blockDim.x - 1) / blockDim.x;
-    const int r0 = threadIdx.x * per;
-    int cnt = 0;
-    for (int r = r0; r < r0 + per && r < R; ++r) cnt += a.fcount[r * (B + 1) + level];
-    int total;
-    int off = block_exclusive_scan(cnt, sh, &total);
-    for (int r = r0; r < r0 + per && r < R; ++r) {
-        const int f = a.fcount[r * (B + 1) + level];
-        a.roff[r] = off;
-        for (int i = 0; i < f; ++i) a.rows[off + i] = make_int2(r, i);
-        off += f;
+// Staging of one request's emit (see emit_request).
+struct EmitSmem {
+    uint64_t keys[kMaxNcap];
+    uint32_t lowc[kMaxNcap];
+    int parc[kMaxNcap];
+    int fcnt[kMaxB + 1];
+    int n;
+    uint32_t fself[kMaxB * kMaxNcap];  // front[d][m].self for d = 1..B-1
+};
+
+// ---------------------------------------------------------------------------------------
+// Shared memory of the persistent kernel (one workgroup; phases reuse the first region).
+// ---------------------------------------------------------------------------------------
+template <int KT>
+struct BuildSmem {
+    union {
+        uint16_t sA[kTileRows * kAStride];  // bf16 parent rows of U (expand)
+        float sAf[kTileRows * kAfStride];   // f32 parent rows of U (expand)
+        uint64_t keys[kSelectSlots];        // select
+        EmitSmem em;                        // emit
+    } u;
+    float xrec[4][kTileRows][rec_floats(KT)];  // per-wavefront lists of an expansion item
+    float mrec[4][rec_floats(KT)];             // per-wavefront lists of a merged row
+    size_t lbase[kTileRows];
+    uint64_t hash[kTileRows];
+    int tok[kTileRows];
+    int sh[256];
+    int bcast[4];
+};
+
+// ---------------------------------------------------------------------------------------
+// Expansion epilogue on the accumulators.  Lane half h holds columns c0 + 8j + 4h + i
+// (j, i = 0..3) of its parent row; lw[j] holds the raw block logits of group j (4 bf16 in
+// .x/.y, or 4 floats).
+// ---------------------------------------------------------------------------------------
+constexpr float kGumbelMax = 17.35f;  // -log(-log u) < 17.33 for u <= 1 - 2^-25
+
+// Raw block logits of the four column groups of a lane: 4 bf16 per group in a uint2, or 4
+// floats in a uint4.
+template <bool L_BF16>
+struct LGroups {
+    typename std::conditional<L_BF16, uint2, uint4>::type g[4];
+};
+
+template <bool L_BF16>
+__device__ __forceinline__ void load_lgroups(const BuildArgs& a, size_t lbase, int c0, int h,
+                                             bool lvec, LGroups<L_BF16>& lw) {
+    if (lvec) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int c = c0 + 8 * j + 4 * h;
+            c = c < a.V ? c : a.V - 4;  // V is a multiple of 4 here; masked in the epilogue
+            if constexpr (L_BF16)
+                lw.g[j] = *(const uint2*)((const uint16_t*)a.L + lbase + c);
+            else
+                lw.g[j] = *(const uint4*)((const float*)a.L + lbase + c);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int c = c0 + 8 * j + 4 * h + i;
+                c = c < a.V ? c : a.V - 1;
+                if constexpr (L_BF16)
+                    w[i] = (uint32_t)((const uint16_t*)a.L)[lbase + c];
+                else
+                    w[i] = __float_as_uint(((const float*)a.L)[lbase + c]);
+            }
+            if constexpr (L_BF16)
+                lw.g[j] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+            else
+                lw.g[j] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
     }
-    if (threadIdx.x == 0) a.sync[kSyncRows] = (unsigned)total;
 }
 
-// ---------------------------------------------------------------------------------------
-// Phase A, one item: a tile of 64 parent rows x one vocabulary split.
-// C[64 x 128 chunk] = A[64 x r] . Wt[chunk x r]^T on MFMA into LDS, then the epilogue:
-// thread t owns row t/4 and columns (t%4)*32 .. +32 of every chunk; its running (max, sum)
-// and top-KT list persist across the split's chunks.  The block-logit values of the next
-// chunk are loaded right after the current chunk's epilogue so that their latency overlaps
-// the next MFMA.
-// ---------------------------------------------------------------------------------------
-struct ExpandSmem {
-    uint16_t sA[kTileRows * kAStride];
-    float sZ[kTileRows * kZStride];
-    int sTok[kTileRows];
-    int sReq[kTileRows];
-    uint64_t sHash[kTileRows];
-};
-struct ExpandSmemF {
-    float sAf[kTileRows * kAfStride];
-    float sZ[kTileRows * kZStride];
-    int sTok[kTileRows];
-    int sReq[kTileRows];
-    uint64_t sHash[kTileRows];
-};
-
-// Largest value the Gumbel transform can return: u <= 1 - 2^-25, so -log(-log u) < 17.33;
-// the bound below leaves room for float32 rounding.
-constexpr float kGumbelMax = 17.35f;
-
-// One chunk of one row for one thread: 32 columns cb .. cb+31 whose bias is in zr (LDS, this
-// thread's own slots) and whose block logits are in l.  Updates the online log-sum-exp and
-// the ranked list.  Candidates for the list are found with a mask against the current k-th
-// key, then inserted one at a time from LDS, so the insertion code exists once.
-template <int KT, bool SAMPLE>
-__device__ __forceinline__ void epilogue_chunk(const BuildArgs& a, float* zr, int cb,
-                                               const float (&l)[32], uint64_t ehash,
-                                               TopK<KT>& top, Lse2& acc2) {
-    const int nvalid = min(32, a.V - cb);
-    float z[32];
-    float cm = -INFINITY;
-    // columns past V hold -inf in zr (see expand_item), so no per-column conditions here
+template <int KT, bool SAMPLE, bool L_BF16>
+__device__ __forceinline__ void expand_epilogue(const BuildArgs& a, const f32x16& acc,
+                                                const LGroups<L_BF16>& lw, int c0, int h,
+                                                uint64_t hh, TopK<KT>& top, Lse2& st) {
+    float z[16];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        z[j] = zr[j] + l[j];
-        cm = fmaxf(cm, z[j]);
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (L_BF16) {
+            z[4 * j + 0] = acc[4 * j + 0] + bf16_lo(lw.g[j].x);
+            z[4 * j + 1] = acc[4 * j + 1] + bf16_hi(lw.g[j].x);
+            z[4 * j + 2] = acc[4 * j + 2] + bf16_lo(lw.g[j].y);
+            z[4 * j + 3] = acc[4 * j + 3] + bf16_hi(lw.g[j].y);
+        } else {
+            z[4 * j + 0] = acc[4 * j + 0] + __uint_as_float(lw.g[j].x);
+            z[4 * j + 1] = acc[4 * j + 1] + __uint_as_float(lw.g[j].y);
+            z[4 * j + 2] = acc[4 * j + 2] + __uint_as_float(lw.g[j].z);
+            z[4 * j + 3] = acc[4 * j + 3] + __uint_as_float(lw.g[j].w);
+        }
     }
-    cm *= a.y2scale;
-    if (cm > acc2.m) {
-        acc2.s = (acc2.m == -INFINITY) ? 0.0f : acc2.s * exp2f(acc2.m - cm);
-        acc2.m = cm;
-    }
-    float ps = 0.0f;
+    uint32_t vmask = 0xFFFFu;
+    if (c0 + kBlockCols > a.V) {
 #pragma unroll
-    for (int j = 0; j < 32; ++j) ps += exp2f(z[j] * a.y2scale - acc2.m);  // exp2(-inf) = 0
-    acc2.s += ps;
-    // Candidates: a superset test against the current k-th key (ties and the Gumbel noise are
-    // settled by push(), which re-checks the exact order).
-    const float tk = top.key[KT - 1];
-    // sample keys are z / T + G with G < kGumbelMax, so z < (tk - kGumbelMax) T cannot qualify
-    const float thr = SAMPLE ? (tk - kGumbelMax) / a.invT : tk;
+        for (int e = 0; e < 16; ++e) {
+            const int c = c0 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (c >= a.V) {
+                z[e] = -INFINITY;
+                vmask &= ~(1u << e);
+            }
+        }
+    }
+    float cm = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) cm = fmaxf(cm, z[e]);
+    if (cm != -INFINITY) {
+        cm *= a.y2scale;
+        if (cm > st.m) {
+            st.s = (st.m == -INFINITY) ? 0.0f : st.s * exp2f(st.m - cm);
+            st.m = cm;
+        }
+        float ps = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ps += exp2f(z[e] * a.y2scale - st.m);  // exp2(-inf) = 0
+        st.s += ps;
+    }
+    // Candidates: a superset test against a lower bound of the KT-th best key among the list
+    // and this block (ties and the Gumbel noise are settled by push(), which compares exact
+    // entries).  Greedy: the bound is the larger of the list's KT-th key and the smallest of
+    // the maxima of KT disjoint groups of the block (KT elements of the block are >= it).
+    // Sample keys are z / T + G with G < kGumbelMax, so z < (tk - kGumbelMax) T cannot
+    // qualify.
+    const float tk = top.k[KT - 1] ? entry_key(top.k[KT - 1]) : -INFINITY;
+    float thr;
+    if constexpr (SAMPLE) {
+        thr = (tk - kGumbelMax) / a.invT;
+    } else {
+        constexpr int GS = 16 / KT;
+        float bb = INFINITY;
+#pragma unroll
+        for (int g = 0; g < KT; ++g) {
+            float gm = z[g * GS];
+#pragma unroll
+            for (int i = 1; i < GS; ++i) gm = fmaxf(gm, z[g * GS + i]);
+            bb = fminf(bb, gm);
+        }
+        thr = fmaxf(tk, bb);
+    }
     uint32_t mask = 0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) mask |= (z[j] >= thr ? 1u : 0u) << j;
-    if (nvalid < 32) mask &= nvalid > 0 ? (1u << nvalid) - 1u : 0u;
+    for (int e = 0; e < 16; ++e) mask |= (z[e] >= thr ? 1u : 0u) << e;
+    mask &= vmask;
     if (mask == 0u) return;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) zr[j] = z[j];
     if constexpr (SAMPLE) {
-        for (int g = 0; g < 8; ++g) {
-            uint32_t gm = (mask >> (4 * g)) & 15u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t gm = (mask >> (4 * j)) & 15u;
             if (gm == 0u) continue;
-            const uint4 w = rand4((uint32_t)((cb >> 2) + g), STREAM_GUMBEL, ehash, a.seed_lo,
-                                  a.seed_hi);
+            const int cg = c0 + 8 * j + 4 * h;
+            const uint4 w = rand4((uint32_t)(cg >> 2), STREAM_GUMBEL, hh, a.seed_lo, a.seed_hi);
             while (gm) {
                 const int e = __builtin_ctz(gm);
                 gm &= gm - 1u;
                 const uint32_t we = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
-                const float zj = zr[4 * g + e];
-                top.push(zj * a.invT + gumbel(we), zj * a.y2scale, cb + 4 * g + e);
+                const float zj = e == 0 ? z[4 * j] : e == 1 ? z[4 * j + 1] : e == 2 ? z[4 * j + 2]
+                                                                                  : z[4 * j + 3];
+                top.push(pack_entry(zj * a.invT + gumbel(we), cg + e), zj * a.y2scale);
             }
         }
     } else {
         while (mask) {
-            const int j = __builtin_ctz(mask);
+            const int e = __builtin_ctz(mask);
             mask &= mask - 1u;
-            const float zj = zr[j];
-            top.push(zj, zj * a.y2scale, cb + j);
+            float zj = z[0];
+#pragma unroll
+            for (int q = 1; q < 16; ++q) zj = (e == q) ? z[q] : zj;
+            top.push(pack_entry(zj, c0 + 8 * (e >> 2) + 4 * h + (e & 3)), zj * a.y2scale);
         }
     }
 }
 
-// Raw block-logit words of 32 consecutive columns: 4 x 16 bytes for bf16 rows (the common
-// case), else nothing (float32 or unaligned rows are read in the epilogue itself).
-struct LWords {
-    uint4 w[4];
-};
-
-__device__ __forceinline__ void load_lwords(const BuildArgs& a, size_t lbase, int cb, bool lvec,
-                                            LWords& lw) {
-    if (lvec && a.logits_bf16 && cb + 32 <= a.V) {
-        const uint4* lp = (const uint4*)((const uint16_t*)a.L + lbase + cb);
+// Record of a list: (m, s) of the log-sum-exp, then KT packed entries as (lo, hi) words,
+// then the KT tempered logits.
+template <int KT>
+__device__ __forceinline__ void put_list(float* v, const TopK<KT>& t, const Lse2& s) {
+    v[0] = s.m;
+    v[1] = s.s;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) lw.w[q] = lp[q];
+    for (int i = 0; i < KT; ++i) {
+        v[2 + 2 * i] = __uint_as_float((uint32_t)t.k[i]);
+        v[3 + 2 * i] = __uint_as_float((uint32_t)(t.k[i] >> 32));
+        v[2 + 2 * KT + i] = t.y[i];
     }
 }
 
-// Block-logit values of 32 consecutive columns.  The common case (bf16 rows, 16-byte
-// aligned, a full chunk) unpacks the prefetched words; otherwise the values are added into
-// the thread's LDS slots here, with -inf past V, and l is zero.
-__device__ __forceinline__ void block_logits32(const BuildArgs& a, size_t lbase, int cb, bool lvec,
-                                               const LWords& lw, float* zr, float (&l)[32]) {
-    if (lvec && a.logits_bf16 && cb + 32 <= a.V) {
+template <int KT>
+__device__ __forceinline__ void get_list(const float* v, TopK<KT>& t, Lse2& s) {
+    s.m = v[0];
+    s.s = v[1];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const uint4 v = lw.w[q];
-            l[q * 8 + 0] = bf16_lo(v.x); l[q * 8 + 1] = bf16_hi(v.x);
-            l[q * 8 + 2] = bf16_lo(v.y); l[q * 8 + 3] = bf16_hi(v.y);
-            l[q * 8 + 4] = bf16_lo(v.z); l[q * 8 + 5] = bf16_hi(v.z);
-            l[q * 8 + 6] = bf16_lo(v.w); l[q * 8 + 7] = bf16_hi(v.w);
-        }
-        return;
+    for (int i = 0; i < KT; ++i) {
+        t.k[i] = (uint64_t)__float_as_uint(v[2 + 2 * i]) |
+                 ((uint64_t)__float_as_uint(v[3 + 2 * i]) << 32);
+        t.y[i] = v[2 + 2 * KT + i];
     }
-#pragma unroll 1
-    for (int j = 0; j < 32; ++j)
-        zr[j] = (cb + j < a.V) ? zr[j] + load_logit(a.L, lbase + cb + j, a.logits_bf16) : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) l[j] = 0.0f;
 }
 
-template <int KT, bool SAMPLE, bool HEAD_BF16, typename Sm>
+// One item: tile `tile` of the level's parent rows x vocabulary split `split`.  Wavefront w
+// takes the split's 32-column blocks w, w+4, ...; the four wavefronts' lists are combined in
+// LDS and one record per parent row is published.
+template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
 __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M, int S, int tile,
-                                            int split, Sm& sm) {
-    const int tid = threadIdx.x;
+                                            int split, BuildSmem<KT>& sm) {
+    constexpr int RS = rec_floats(KT);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
     const int lvl = level - 1;
     const int m0 = tile * kTileRows;
     const int nrows = min(kTileRows, M - m0);
-    const int c_beg = (int)((long long)split * a.NC / S);
-    const int c_end = (int)((long long)(split + 1) * a.NC / S);
+    const int NB = (a.V + kBlockCols - 1) / kBlockCols;
+    const int b_beg = (int)((long long)split * NB / S);
+    const int b_end = (int)((long long)(split + 1) * NB / S);
 
     if (tid < kTileRows) {
-        int tok = 0, req = 0;
-        uint64_t h = 0;
+        int tok = 0;
+        size_t lb = 0;
+        uint64_t hh = 0;
         if (tid < nrows) {
-            const int2 rq = a.rows[m0 + tid];
-            const FrontEntry& fe = a.front[((size_t)rq.x * (a.B + 1) + lvl) * a.Ncap + rq.y];
-            tok = fe.token;
-            req = rq.x;
-            h = fe.hash;
+            const uint64_t rq = cld64(a.rows + m0 + tid);
+            const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
+            const FrontEntry* fe = a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi;
+            tok = (int)(uint32_t)(cld64(fe) >> 32);
+            hh = cld64((const char*)fe + 16);
+            lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
         }
-        sm.sTok[tid] = tok;
-        sm.sReq[tid] = req;
-        sm.sHash[tid] = h;
+        sm.tok[tid] = tok;
+        sm.lbase[tid] = lb;
+        sm.hash[tid] = hh;
     }
     __syncthreads();
     if constexpr (HEAD_BF16)
-        load_a_tile<true>(a.U, a.r, nrows, [&](int row) { return sm.sTok[row]; }, sm.sA, nullptr);
+        load_a_tile<true>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, sm.u.sA, nullptr);
     else
-        load_a_tile<false>(a.U, a.r, nrows, [&](int row) { return sm.sTok[row]; }, nullptr, sm.sAf);
+        load_a_tile<false>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, nullptr, sm.u.sAf);
     __syncthreads();
 
-    const int erow = tid >> 2, epart = tid & 3;
-    const bool eactive = erow < nrows;
-    const uint64_t ehash = sm.sHash[erow];
-    const size_t lbase = ((size_t)sm.sReq[erow] * a.B + lvl) * (size_t)a.V;
-    const bool lvec = a.logits_bf16 ? ((a.V & 7) == 0) : ((a.V & 3) == 0);
-    TopK<KT> top;
-    top.init();
-    Lse2 acc2;
-    acc2.init();
     const bool two = nrows > 32;
-
-    LWords lw;
-    if (eactive && c_beg < c_end) load_lwords(a, lbase, c_beg * kChunkCols + epart * 32, lvec, lw);
-    for (int c = c_beg; c < c_end; ++c) {
-        const int col0 = c * kChunkCols;
-        if constexpr (HEAD_BF16)
-            mma_chunk<true>(a.Wt, a.V, a.r, col0, two, sm.sA, nullptr, sm.sZ);
-        else
-            mma_chunk<false>(a.Wt, a.V, a.r, col0, two, nullptr, sm.sAf, sm.sZ);
-        if (eactive) {
-            float lv[32];
-            float* zr = sm.sZ + erow * kZStride + epart * 32;
-            block_logits32(a, lbase, col0 + epart * 32, lvec, lw, zr, lv);
-            if (c + 1 < c_end) load_lwords(a, lbase, col0 + kChunkCols + epart * 32, lvec, lw);
-            epilogue_chunk<KT, SAMPLE>(a, zr, col0 + epart * 32, lv, ehash, top, acc2);
+    const int p0 = lane & 31;
+    const size_t lb0 = sm.lbase[p0], lb1 = sm.lbase[32 + p0];
+    const uint64_t hh0 = sm.hash[p0], hh1 = sm.hash[32 + p0];
+    const bool lvec = (a.V & 3) == 0;
+    TopK<KT> t0, t1;
+    Lse2 s0, s1;
+    t0.init();
+    t1.init();
+    s0.init();
+    s1.init();
+    if constexpr (HEAD_BF16) {
+        // Software pipeline: the W fragments and block logits of block b + 4 are in flight
+        // while block b's epilogue runs.
+        int blk = b_beg + wave;
+        bf16x8 wf[16];
+        LGroups<L_BF16> n0, n1;
+        if (blk < b_end) {
+            load_wfrag(a.Wt, a.V, a.r, blk * kBlockCols, wf);
+            load_lgroups<L_BF16>(a, lb0, blk * kBlockCols, h, lvec, n0);
+            if (two) load_lgroups<L_BF16>(a, lb1, blk * kBlockCols, h, lvec, n1);
         }
-        __syncthreads();
+        for (; blk < b_end; blk += 4) {
+            const int c0 = blk * kBlockCols;
+            const LGroups<L_BF16> l0 = n0, l1 = n1;
+            f32x16 acc0, acc1;
+            mma_wfrag(wf, two, sm.u.sA, acc0, acc1);
+            if (blk + 4 < b_end) {
+                load_wfrag(a.Wt, a.V, a.r, c0 + 4 * kBlockCols, wf);
+                load_lgroups<L_BF16>(a, lb0, c0 + 4 * kBlockCols, h, lvec, n0);
+                if (two) load_lgroups<L_BF16>(a, lb1, c0 + 4 * kBlockCols, h, lvec, n1);
+            }
+            expand_epilogue<KT, SAMPLE, L_BF16>(a, acc0, l0, c0, h, hh0, t0, s0);
+            if (two) expand_epilogue<KT, SAMPLE, L_BF16>(a, acc1, l1, c0, h, hh1, t1, s1);
+        }
+    } else {
+        for (int blk = b_beg + wave; blk < b_end; blk += 4) {
+            const int c0 = blk * kBlockCols;
+            LGroups<L_BF16> l0, l1;
+            load_lgroups<L_BF16>(a, lb0, c0, h, lvec, l0);
+            if (two) load_lgroups<L_BF16>(a, lb1, c0, h, lvec, l1);
+            f32x16 acc0, acc1;
+            xblock_mma_f32(a.Wt, a.V, a.r, c0, two, sm.u.sAf, acc0, acc1);
+            expand_epilogue<KT, SAMPLE, L_BF16>(a, acc0, l0, c0, h, hh0, t0, s0);
+            if (two) expand_epilogue<KT, SAMPLE, L_BF16>(a, acc1, l1, c0, h, hh1, t1, s1);
+        }
     }
-    acc2.merge_xor(1);
-    acc2.merge_xor(2);
-    top.merge_xor(1);
-    top.merge_xor(2);
-    if (eactive && epart == 0) {
-        constexpr int RS = rec_floats(KT);
-        float v[RS];
+    // lanes l and l ^ 32 hold the same parent row
+    s0.merge_xor(32);
+    t0.merge_xor(32);
+    if (two) {
+        s1.merge_xor(32);
+        t1.merge_xor(32);
+    }
+    if (h == 0) {
+        put_list<KT>(sm.xrec[wave][p0], t0, s0);
+        if (two) put_list<KT>(sm.xrec[wave][32 + p0], t1, s1);
+    }
+    __syncthreads();
+    {
+        const int row = tid >> 2, w = tid & 3;
+        TopK<KT> t;
+        Lse2 s;
+        get_list<KT>(sm.xrec[w][row], t, s);
+        s.merge_xor(1);
+        s.merge_xor(2);
+        t.merge_xor(1);
+        t.merge_xor(2);
+        if (w == 0 && row < nrows) {
+            float v[RS];
 #pragma unroll
-        for (int i = 0; i < RS; ++i) v[i] = 0.0f;
-        v[0] = acc2.m;
-        v[1] = acc2.s;
+            for (int i = 0; i < RS; ++i) v[i] = 0.0f;
+            put_list<KT>(v, t, s);
+            char* rec = (char*)(a.partials + ((size_t)(m0 + row) * S + split) * RS);
 #pragma unroll
-        for (int i = 0; i < KT; ++i) {
-            v[2 + i] = top.key[i];
-            v[2 + KT + i] = top.y[i];
-            v[2 + 2 * KT + i] = __int_as_float(top.tok[i]);
+            for (int q = 0; q < RS / 2; ++q)
+                cst64(rec + 8 * q, (uint64_t)__float_as_uint(v[2 * q]) |
+                                       ((uint64_t)__float_as_uint(v[2 * q + 1]) << 32));
         }
-        float4* rec = (float4*)(a.partials + ((size_t)(m0 + erow) * S + split) * RS);
-#pragma unroll
-        for (int q = 0; q < RS / 4; ++q)
-            rec[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
     }
     __syncthreads();
 }
 
 // ---------------------------------------------------------------------------------------
-// Phase B, one wavefront per parent row: combine the S split records; child j gets
+// Merge of one parent row (whole workgroup): combine its S split records; child j gets
 // q = 2^(y2 - lse2), bin = min(15, floor(16 q)), s = fl32(s_parent * cal[bin]),
-// logq = (y2 - lse2) ln 2, and its selection key.
+// logq = (y2 - lse2) ln 2, and its selection key.  Returns the row's request.
 // ---------------------------------------------------------------------------------------
 template <int KT>
-__device__ __forceinline__ void merge_record(const float4 (&q)[rec_floats(KT) / 4], TopK<KT>& top,
-                                             Lse2& acc) {
-    float v[rec_floats(KT)];
+__device__ __forceinline__ void fetch_record(const float* rec, uint64_t (&w)[rec_floats(KT) / 2]) {
 #pragma unroll
-    for (int i = 0; i < rec_floats(KT) / 4; ++i) {
-        v[4 * i] = q[i].x;
-        v[4 * i + 1] = q[i].y;
-        v[4 * i + 2] = q[i].z;
-        v[4 * i + 3] = q[i].w;
-    }
-    acc.merge(v[0], v[1]);
-#pragma unroll
-    for (int i = 0; i < KT; ++i) top.push(v[2 + i], v[2 + KT + i], __float_as_int(v[2 + 2 * KT + i]));
+    for (int q = 0; q < rec_floats(KT) / 2; ++q) w[q] = cld64((const char*)rec + 8 * q);
 }
 
 template <int KT>
-__device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, int row) {
-    constexpr int RS = rec_floats(KT), NQ = RS / 4;
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void merge_fetched(const uint64_t (&w)[rec_floats(KT) / 2], TopK<KT>& top,
+                                              Lse2& acc) {
+    constexpr int RS = rec_floats(KT);
+    float v[RS];
+#pragma unroll
+    for (int q = 0; q < RS / 2; ++q) {
+        v[2 * q] = __uint_as_float((uint32_t)w[q]);
+        v[2 * q + 1] = __uint_as_float((uint32_t)(w[q] >> 32));
+    }
+    TopK<KT> o;
+    Lse2 os;
+    get_list<KT>(v, o, os);
+    acc.merge(os.m, os.s);
+    top.merge(o.k, o.y);
+}
+
+template <int KT>
+__device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, int m,
+                                         BuildSmem<KT>& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int RS = rec_floats(KT);
     TopK<KT> top;
     top.init();
     Lse2 acc;
     acc.init();
-    const float4* base = (const float4*)(a.partials + (size_t)row * S * RS);
-    // two records per lane per round, both loaded before either is merged
-    for (int s0 = lane; s0 < S; s0 += 128) {
-        const int s1 = s0 + 64 < S ? s0 + 64 : s0;
-        float4 q0[NQ], q1[NQ];
-#pragma unroll
-        for (int i = 0; i < NQ; ++i) {
-            q0[i] = base[(size_t)s0 * NQ + i];
-            q1[i] = base[(size_t)s1 * NQ + i];
-        }
-        merge_record<KT>(q0, top, acc);
-        if (s0 + 64 < S) merge_record<KT>(q1, top, acc);
-    }
+    const float* base = a.partials + (size_t)m * S * RS;
+    const int s0 = tid < S ? tid : S - 1, s1 = tid + 256 < S ? tid + 256 : S - 1;
+    uint64_t w0[RS / 2], w1[RS / 2];
+    fetch_record<KT>(base + (size_t)s0 * RS, w0);
+    fetch_record<KT>(base + (size_t)s1 * RS, w1);
+    const uint64_t rq = cld64(a.rows + m);
+    if (tid < S) merge_fetched<KT>(w0, top, acc);
+    if (tid + 256 < S) merge_fetched<KT>(w1, top, acc);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         acc.merge_xor(off);
         top.merge_xor(off);
     }
-    const float lse2 = acc.m + log2f(acc.s);
-    const int2 rq = a.rows[row];
-    const int lvl = level - 1;
-    const FrontEntry par = a.front[((size_t)rq.x * (a.B + 1) + lvl) * a.Ncap + rq.y];
+    if (lane == 0) put_list<KT>(sm.mrec[wave], top, acc);
+    __syncthreads();
+    const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
+    if (wave == 0) {
+        get_list<KT>(sm.mrec[lane & 3], top, acc);
+        acc.merge_xor(1);
+        acc.merge_xor(2);
+        top.merge_xor(1);
+        top.merge_xor(2);
+        const float lse2 = acc.m + log2f(acc.s);
+        const int lvl = level - 1;
+        const FrontEntry par = ld_front(a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi);
 #pragma unroll
-    for (int j = 0; j < KT; ++j) {
-        if (j < a.k && lane == j) {
-            const float l2 = top.y[j] - lse2;
-            const float q = exp2f(l2);
-            int bin = (int)floorf(16.0f * q);
-            bin = bin > 15 ? 15 : (bin < 0 ? 0 : bin);
-            ChildRec c;
-            c.token = top.tok[j];
-            float cv = a.cal[0];
+        for (int j = 0; j < KT; ++j) {
+            if (j < a.k && lane == j) {
+                const float l2 = top.y[j] - lse2;
+                const float q = exp2f(l2);
+                int bin = (int)floorf(16.0f * q);
+                bin = bin > 15 ? 15 : (bin < 0 ? 0 : bin);
+                float cv = a.cal[0];
 #pragma unroll
-            for (int ii = 1; ii < 16; ++ii) cv = (bin == ii) ? a.cal[ii] : cv;
-            c.s = par.s * cv;
-            c.logq = l2 * 0.69314718055994530942f;
-            c.pad = 0;
-            c.hash = child_hash(par.hash, c.token);
-            a.arena[(((size_t)rq.x * a.B + lvl) * a.Ncap + rq.y) * a.k + j] = c;
-            a.ckeys[(size_t)rq.x * a.Ncap * a.k + rq.y * a.k + j] = make_key(c.s, level, rq.y, j);
+                for (int ii = 1; ii < 16; ++ii) cv = (bin == ii) ? a.cal[ii] : cv;
+                ChildRec c;
+                c.token = entry_tok(top.k[j]);
+                c.s = par.s * cv;
+                c.logq = l2 * 0.69314718055994530942f;
+                c.pad = 0;
+                c.hash = child_hash(par.hash, c.token);
+                st_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j, c);
+                cst64(a.ckeys + (size_t)req * a.Ncap * a.k + fi * a.k + j,
+                      make_key(c.s, level, fi, j));
+            }
         }
     }
+    return req;
 }
 
 // ---------------------------------------------------------------------------------------
-// Phase C, one workgroup per request: candidates = the kept set + this level's children;
+// Select, one workgroup per request: candidates = the kept set + this level's children;
 // drop survival < tau; bitonic sort (descending key) in LDS; keep min(n_budget, #left).
 // The kept nodes of depth `level` become the next frontier in canonical order.
 // ---------------------------------------------------------------------------------------
@@ -377,16 +521,17 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
                                                uint64_t* keys, int* sh) {
     const int tid = threadIdx.x;
     const int lvl = level - 1;
-    const int F = a.fcount[req * (a.B + 1) + lvl];
-    const int nprev = a.scount[req];
+    const int F = cldi(a.fcount + req * (a.B + 1) + lvl);
+    const int nprev = cldi(a.scount + req);
+    const int nbudget = cldi(a.nbeff + req);
     const int ncand = nprev + F * a.k;
     const float tau = a.tau[req];
     int P = 2;
     while (P < ncand) P <<= 1;
     for (int i = tid; i < P; i += blockDim.x) {
         uint64_t key = 0;
-        if (i < nprev) key = a.skeys[(size_t)req * a.Ncap + i];
-        else if (i < ncand) key = a.ckeys[(size_t)req * a.Ncap * a.k + (i - nprev)];
+        if (i < nprev) key = cld64(a.skeys + (size_t)req * a.Ncap + i);
+        else if (i < ncand) key = cld64(a.ckeys + (size_t)req * a.Ncap * a.k + (i - nprev));
         if (key != 0 && key_surv(key) < tau) key = 0;
         keys[i] = key;
     }
@@ -409,9 +554,9 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
     int nz = 0;
     for (int i = tid; i < P; i += blockDim.x) nz += keys[i] != 0 ? 1 : 0;
     nz = block_sum(nz, sh);
-    const int nkept = min(a.nbeff[req], nz);
-    for (int i = tid; i < nkept; i += blockDim.x) a.skeys[(size_t)req * a.Ncap + i] = keys[i];
-    if (tid == 0) a.scount[req] = nkept;
+    const int nkept = min(nbudget, nz);
+    for (int i = tid; i < nkept; i += blockDim.x) cst64(a.skeys + (size_t)req * a.Ncap + i, keys[i]);
+    if (tid == 0) csti(a.scount + req, nkept);
     int fnext = 0;
     if (level < a.B) {
         for (int i = tid; i < nkept; i += blockDim.x) {
@@ -423,104 +568,143 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
                 if (low_depth(lm) == level && lm > low) ++rank;
             }
             const int fi = low_fi(low), j = low_rank(low);
-            const ChildRec& c = a.arena[(((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j];
+            const ChildRec c = ld_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j);
             FrontEntry e;
             e.self = low;
             e.token = c.token;
             e.s = c.s;
             e.pad = 0;
             e.hash = c.hash;
-            a.front[((size_t)req * (a.B + 1) + level) * a.Ncap + rank] = e;
+            st_front(a.front + ((size_t)req * (a.B + 1) + level) * a.Ncap + rank, e);
         }
         int cnt = 0;
         for (int i = tid; i < nkept; i += blockDim.x)
             cnt += (low_depth((uint32_t)keys[i]) == level) ? 1 : 0;
         fnext = block_sum(cnt, sh);
     }
-    if (tid == 0) a.fcount[req * (a.B + 1) + level] = fnext;
-    __syncthreads();
+    if (tid == 0) csti(a.fcount + req * (a.B + 1) + level, fnext);
+}
+
+// Lays out the parent rows of level `level + 1` from the frontier sizes fcount[.][level],
+// in request order, with the row and request counts, and clears the counters of level
+// `level` (every increment of them has happened).  One workgroup.
+__device__ __forceinline__ void release_rows(const BuildArgs& a, int level, int Tcur, int* sh) {
+    const int R = a.R, B = a.B;
+    const int per = (R + blockDim.x - 1) / blockDim.x;
+    const int r0 = threadIdx.x * per;
+    int cnt = 0, nreq = 0, f0 = 0;
+    for (int r = r0; r < r0 + per && r < R; ++r) {
+        const int f = level < B ? cldi(a.fcount + r * (B + 1) + level) : 0;
+        if (r == r0) f0 = f;
+        cnt += f;
+        nreq += f > 0 ? 1 : 0;
+    }
+    int total;
+    int off = block_exclusive_scan(cnt, sh, &total);
+    const int rtotal = block_sum(nreq, sh);
+    for (int r = r0; r < r0 + per && r < R; ++r) {
+        const int f = r == r0 ? f0 : (level < B ? cldi(a.fcount + r * (B + 1) + level) : 0);
+        for (int i = 0; i < f; ++i)
+            cst64(a.rows + off + i, (uint64_t)(uint32_t)r | ((uint64_t)(uint32_t)i << 32));
+        off += f;
+    }
+    for (int t = threadIdx.x; t < Tcur; t += blockDim.x) cst32(a.tdone + t, 0u);
+    for (int r = threadIdx.x; r < R; r += blockDim.x) cst32(a.rdone + r, 0u);
+    if (threadIdx.x == 0) {
+        cst32(a.sync + kSyncRows + level + 1, (unsigned)total);
+        cst32(a.sync + kSyncReqs + level + 1, (unsigned)rtotal);
+    }
 }
 
 // ---------------------------------------------------------------------------------------
-// Emit, one request (threads 0..63 of the workgroup).  Canonical index of a kept node =
-// number of kept nodes whose key low word is larger (depth asc, parent index asc, rank asc).
+// Emit, one request per workgroup.  The request's selected keys, frontier sizes and
+// frontier identities are staged in LDS first (one round of parallel loads), then node i
+// (thread i) finds its canonical index = number of kept nodes whose key low word is larger
+// (depth asc, parent index asc, rank asc), its parent and its expansion slot from LDS.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void emit_request(const BuildArgs& a, int req, uint32_t* lowc,
-                                             int* parc) {
-    const int lane = threadIdx.x;
+
+__device__ __forceinline__ void emit_request(const BuildArgs& a, int req, bool failed,
+                                             EmitSmem& e) {
+    const int tid = threadIdx.x;
     const int B = a.B, k = a.k, Ncap = a.Ncap;
-    const int n = a.scount[req];
-    if (lane < n) {
-        const uint32_t mylow = (uint32_t)a.skeys[(size_t)req * Ncap + lane];
+    if (tid < Ncap) e.keys[tid] = cld64(a.skeys + (size_t)req * Ncap + tid);
+    if (tid <= B) e.fcnt[tid] = failed ? 0 : cldi(a.fcount + req * (B + 1) + tid);
+    if (tid == 0) e.n = failed ? 0 : cldi(a.scount + req);
+    __syncthreads();
+    for (int i = tid; i < (B - 1) * Ncap; i += blockDim.x) {
+        const int d = 1 + i / Ncap, m = i % Ncap;
+        if (m < e.fcnt[d])
+            e.fself[i] = (uint32_t)cld64(a.front + ((size_t)req * (B + 1) + d) * Ncap + m);
+    }
+    const int n = e.n;
+    if (tid < n) {
+        const uint32_t mylow = (uint32_t)e.keys[tid];
         int canon = 0;
-        for (int m = 0; m < n; ++m)
-            if ((uint32_t)a.skeys[(size_t)req * Ncap + m] > mylow) ++canon;
-        lowc[canon] = mylow;
+        for (int m = 0; m < n; ++m) canon += ((uint32_t)e.keys[m] > mylow) ? 1 : 0;
+        e.lowc[canon] = mylow;
     }
     __syncthreads();
     const size_t ob = (size_t)req * Ncap;
     int par = -2;
-    if (lane < n) {
-        const uint32_t low = lowc[lane];
+    if (tid < n) {
+        const uint32_t low = e.lowc[tid];
         const int depth = low_depth(low);
         const int fi = low_fi(low), j = low_rank(low);
-        const ChildRec& c = a.arena[(((size_t)req * B + (depth - 1)) * Ncap + fi) * k + j];
-        if (depth == 1) {
-            par = -1;
-        } else {
-            const uint32_t pid = a.front[((size_t)req * (B + 1) + (depth - 1)) * Ncap + fi].self;
-            par = -1;
+        const ChildRec c = ld_child(a.arena + (((size_t)req * B + (depth - 1)) * Ncap + fi) * k + j);
+        par = -1;
+        if (depth > 1) {
+            const uint32_t pid = e.fself[(depth - 2) * Ncap + fi];
             for (int m = 0; m < n; ++m)
-                if (lowc[m] == pid) par = m;
+                if (e.lowc[m] == pid) par = m;
         }
-        a.out.token[ob + lane] = c.token;
-        a.out.depth[ob + lane] = (uint8_t)depth;
-        a.out.surv[ob + lane] = c.s;
-        a.out.logq[ob + lane] = c.logq;
-        const size_t cb = ((size_t)req * (Ncap + 1) + lane + 1) * k;
         int slot = -1;
         if (depth < B) {
-            const int F = a.fcount[req * (B + 1) + depth];
+            const int F = e.fcnt[depth];
             for (int m = 0; m < F; ++m)
-                if (a.front[((size_t)req * (B + 1) + depth) * Ncap + m].self == low) slot = m;
+                if (e.fself[(depth - 1) * Ncap + m] == low) slot = m;
         }
+        a.out.token[ob + tid] = c.token;
+        a.out.depth[ob + tid] = (uint8_t)depth;
+        a.out.surv[ob + tid] = c.s;
+        a.out.logq[ob + tid] = c.logq;
+        const size_t cb = ((size_t)req * (Ncap + 1) + tid + 1) * k;
+        const ChildRec* crow = a.arena + (((size_t)req * B + depth) * Ncap + (slot >= 0 ? slot : 0)) * k;
         for (int jj = 0; jj < k; ++jj)
-            a.out.cand[cb + jj] =
-                slot >= 0 ? a.arena[(((size_t)req * B + depth) * Ncap + slot) * k + jj].token : -1;
+            a.out.cand[cb + jj] = slot >= 0 ? (int)(uint32_t)cld64(crow + jj) : -1;
     }
-    if (lane < kMaxNcap) parc[lane] = par;
+    if (tid < kMaxNcap) e.parc[tid] = par;
     __syncthreads();
-    if (lane < n) {
+    if (tid < n) {
         uint64_t m = 0;
-        int x = lane;
+        int x = tid;
         while (x >= 0) {
             m |= 1ull << x;
-            x = parc[x];
+            x = e.parc[x];
         }
-        a.out.anc_mask[ob + lane] = m;
-        a.out.parent[ob + lane] = (int16_t)par;
-    } else if (lane < Ncap) {
-        a.out.token[ob + lane] = -1;
-        a.out.parent[ob + lane] = -2;
-        a.out.depth[ob + lane] = 0;
-        a.out.anc_mask[ob + lane] = 0;
-        a.out.surv[ob + lane] = 0.0f;
-        a.out.logq[ob + lane] = 0.0f;
-        const size_t cb = ((size_t)req * (Ncap + 1) + lane + 1) * k;
+        a.out.anc_mask[ob + tid] = m;
+        a.out.parent[ob + tid] = (int16_t)par;
+    } else if (tid < Ncap) {
+        a.out.token[ob + tid] = -1;
+        a.out.parent[ob + tid] = -2;
+        a.out.depth[ob + tid] = 0;
+        a.out.anc_mask[ob + tid] = 0;
+        a.out.surv[ob + tid] = 0.0f;
+        a.out.logq[ob + tid] = 0.0f;
+        const size_t cb = ((size_t)req * (Ncap + 1) + tid + 1) * k;
         for (int jj = 0; jj < k; ++jj) a.out.cand[cb + jj] = -1;
     }
-    if (lane < k) {
-        const bool rooted = a.fcount[req * (B + 1)] == 1;
-        a.out.cand[(size_t)req * (Ncap + 1) * k + lane] =
-            rooted ? a.arena[((size_t)req * B * Ncap) * k + lane].token : -1;
+    if (tid < k) {
+        const bool rooted = e.fcnt[0] == 1;
+        a.out.cand[(size_t)req * (Ncap + 1) * k + tid] =
+            rooted ? (int)(uint32_t)cld64(a.arena + ((size_t)req * B * Ncap) * k + tid) : -1;
     }
-    if (lane == 0) {
+    if (tid == 0) {
         a.out.n_nodes[req] = n;
-        a.out.status[req] = a.rstat[req];
+        a.out.status[req] = cldi(a.rstat + req) | (failed ? DT_REQ_SYNC_TIMEOUT : 0);
         if (a.out.n_expand) {
-            int e = 0;
-            for (int l = 0; l < B; ++l) e += a.fcount[req * (B + 1) + l];
-            a.out.n_expand[req] = e;
+            int ex = 0;
+            for (int l = 0; l < B; ++l) ex += e.fcnt[l];
+            a.out.n_expand[req] = ex;
         }
     }
     __syncthreads();
@@ -529,11 +713,18 @@ __device__ __forceinline__ void emit_request(const BuildArgs& a, int req, uint32
 // ---------------------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------------------
-// Round set-up (one workgroup): roots, budgets, status bits, the level-1 parent rows.
-__global__ __launch_bounds__(256) void k_build_init(const BuildArgs a) {
+// Round set-up (one workgroup): control words and counters, roots, budgets, status bits,
+// and the level-1 parent rows (one per request with a valid root).
+__global__ __launch_bounds__(256) void k_build_init(const BuildArgs a, int tiles) {
     __shared__ int sh[256];
     const int tid = threadIdx.x;
-    for (int r = tid; r < a.R; r += blockDim.x) {
+    for (int i = tid; i < kSyncWords; i += blockDim.x) a.sync[i] = 0u;
+    for (int t = tid; t < tiles; t += blockDim.x) a.tdone[t] = 0u;
+    const int R = a.R;
+    const int per = (R + blockDim.x - 1) / blockDim.x;
+    const int r0 = tid * per;
+    int cnt = 0;
+    for (int r = r0; r < r0 + per && r < R; ++r) {
         const int32_t root = a.root_token[r];
         int nb = a.n_budget[r];
         int st = 0;
@@ -555,106 +746,152 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a) {
         a.scount[r] = 0;
         a.nbeff[r] = nb;
         a.rstat[r] = st;
-        a.pdone[r] = 0;
+        a.rdone[r] = 0u;
+        cnt += ok ? 1 : 0;
     }
-    if (a.out.level_rows)
-        for (int l = tid; l < a.B; l += blockDim.x) a.out.level_rows[l] = 0;
-    if (tid < kSyncWords) a.sync[tid] = 0u;
-    __syncthreads();
-    compact_rows(a, 0, sh);
+    int total;
+    int off = block_exclusive_scan(cnt, sh, &total);
+    for (int r = r0; r < r0 + per && r < R; ++r) {
+        const int32_t root = a.root_token[r];
+        if (root >= 0 && root < a.V) a.rows[off++] = make_int2(r, 0);
+    }
+    if (tid == 0) {
+        a.sync[kSyncRows + 1] = (unsigned)total;
+        a.sync[kSyncReqs + 1] = (unsigned)total;
+    }
 }
 
-template <int KT, bool SAMPLE, bool HEAD_BF16>
-__global__ __launch_bounds__(256, 2) void k_expand(const BuildArgs a, int level) {
-    using Sm = typename std::conditional<HEAD_BF16, ExpandSmem, ExpandSmemF>::type;
-    __shared__ __attribute__((aligned(16))) Sm sm;
-    const int M = load_int(a.sync + kSyncRows);
-    if (M == 0) return;
-    const int T = (M + kTileRows - 1) / kTileRows;
-    const int S = splits_for(T, gridDim.x, a.NC);
-    for (int item = blockIdx.x; item < T * S; item += gridDim.x)
-        expand_item<KT, SAMPLE, HEAD_BF16>(a, level, M, S, item / S, item % S, sm);
-}
-
-// P workgroups per request: part p merges parent rows p, p+P, .. (one wavefront per row);
-// the last part to finish runs the request's select; the last request to finish compacts
-// the next level's rows.
-template <int KT>
-__global__ __launch_bounds__(256) void k_merge_select(const BuildArgs a, int level, int G, int P) {
-    __shared__ uint64_t keys[kSelectSlots];
-    __shared__ int sh[256];
-    __shared__ int s_flag;
-    const int M = load_int(a.sync + kSyncRows);
-    if (M == 0) return;
-    const int tid = threadIdx.x, req = blockIdx.x / P, part = blockIdx.x % P;
-    const int S = splits_for((M + kTileRows - 1) / kTileRows, G, a.NC);
-    const int F = a.fcount[req * (a.B + 1) + level - 1];
-    const int row0 = a.roff[req];
-    for (int fi = part + P * (tid >> 6); fi < F; fi += 4 * P) merge_row<KT>(a, level, S, row0 + fi);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_flag = (atomicAdd(a.pdone + req, 1) == P - 1) ? 1 : 0;
-    __syncthreads();
-    if (!s_flag) return;
-    __threadfence();
-    if (tid == 0) a.pdone[req] = 0;
-    select_request(a, level, req, keys, sh);
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_flag = (atomicAdd(a.sync + kSyncFinish, 1u) == (unsigned)a.R - 1u) ? 1 : 0;
-    __syncthreads();
-    if (s_flag) {
-        __threadfence();
-        if (tid == 0) {
-            a.sync[kSyncFinish] = 0u;
-            if (a.out.level_rows) a.out.level_rows[level - 1] = M;
+// The level loop (cooperative launch: all workgroups are resident).
+template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
+__global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
+    __shared__ __attribute__((aligned(16))) BuildSmem<KT> sm;
+    const int tid = threadIdx.x;
+    const int G = gridDim.x;
+    const int NB = (a.V + kBlockCols - 1) / kBlockCols;
+    bool failed = false;
+    for (int level = 1;; ++level) {
+        // the previous level's selects are complete once the generation reaches level - 1
+        if (!wait_at_least(a.sync, a.sync + kSyncGen, (unsigned)(level - 1), sm.bcast)) {
+            failed = true;
+            break;
         }
-        if (level < a.B) compact_rows(a, level, sh);
-        else if (tid == 0) a.sync[kSyncRows] = 0u;
+        if (level > a.B) break;
+        const int M = (int)cld32(a.sync + kSyncRows + level);
+        if (M == 0) break;
+        const int T = (M + kTileRows - 1) / kTileRows;
+        const int S = splits_for(T, G, NB);
+        const unsigned nreq = cld32(a.sync + kSyncReqs + level);
+        for (int item = blockIdx.x; item < T * S; item += G) {
+            expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
+            publish_wg();
+            if (tid == 0) cadd32(a.tdone + item / S, 1u);
+        }
+        // merge tasks: parent rows in order, each once its tile's splits are all in
+        for (;;) {
+            if (tid == 0) sm.bcast[1] = (int)cadd32(a.sync + kSyncTask + level, 1u);
+            __syncthreads();
+            const int m = sm.bcast[1];
+            __syncthreads();
+            if (m >= M) break;
+            if (!wait_at_least(a.sync, a.tdone + m / kTileRows, (unsigned)S, sm.bcast)) {
+                failed = true;
+                break;
+            }
+            const int req = merge_row<KT>(a, level, S, m, sm);
+            publish_wg();
+            if (tid == 0) {
+                const int F = cldi(a.fcount + req * (a.B + 1) + level - 1);
+                sm.bcast[2] = (cadd32(a.rdone + req, 1u) + 1u == (unsigned)F) ? 1 : 0;
+            }
+            __syncthreads();
+            if (sm.bcast[2]) {
+                select_request(a, level, req, sm.u.keys, sm.sh);
+                publish_wg();
+                if (tid == 0) sm.bcast[3] = (cadd32(a.sync + kSyncDone + level, 1u) + 1u == nreq) ? 1 : 0;
+                __syncthreads();
+                if (sm.bcast[3]) {
+                    release_rows(a, level, T, sm.sh);
+                    publish_wg();
+                    if (tid == 0) cst32(a.sync + kSyncGen, (unsigned)level);
+                }
+            }
+            __syncthreads();
+        }
+        if (failed) break;
     }
-}
-
-__global__ __launch_bounds__(256) void k_emit(const BuildArgs a) {
-    __shared__ uint32_t lowc[kMaxNcap];
-    __shared__ int parc[kMaxNcap];
-    emit_request(a, blockIdx.x, lowc, parc);
+    if (failed) cst32(a.sync + kSyncErr, 1u);
+    for (int req = blockIdx.x; req < a.R; req += G)
+        emit_request(a, req, failed || cld32(a.sync + kSyncErr) != 0u, sm.u.em);
+    if (blockIdx.x == 0 && a.out.level_rows)
+        for (int l = tid; l < a.B; l += blockDim.x)
+            a.out.level_rows[l] = (int)cld32(a.sync + kSyncRows + l + 1);
 }
 
 // ---------------------------------------------------------------------------------------
 // Launch sequence of one round.
 // ---------------------------------------------------------------------------------------
-template <int KT, bool SAMPLE, bool HEAD_BF16>
-static hipError_t launch_build_t(const BuildArgs& a, int G, hipStream_t st) {
-    // merge parts per request: enough workgroups to give every parent row of a small batch
-    // its own wavefront
-    const int P = a.R >= 64 ? 1 : (64 / a.R > 16 ? 16 : 64 / a.R);
-    hipLaunchKernelGGL(k_build_init, dim3(1), dim3(256), 0, st, a);
-    for (int level = 1; level <= a.B; ++level) {
-        if (a.timing_hook) a.timing_hook(st, 0);
-        hipLaunchKernelGGL((k_expand<KT, SAMPLE, HEAD_BF16>), dim3(G), dim3(256), 0, st, a, level);
-        if (a.timing_hook) a.timing_hook(st, 1);
-        hipLaunchKernelGGL(k_merge_select<KT>, dim3(a.R * P), dim3(256), 0, st, a, level, G, P);
+// Resident workgroups of a kernel on the current device (cached per kernel and device).
+static int resident_grid(const void* f) {
+    static std::mutex mu;
+    static const void* keys[64];
+    static int devs[64], vals[64], n = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> lk(mu);
+    for (int i = 0; i < n; ++i)
+        if (keys[i] == f && devs[i] == dev) return vals[i];
+    int per = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, 256, 0) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    int g = per * cus;
+    if (g > kMaxGrid) g = kMaxGrid;
+    if (n < 64) {
+        keys[n] = f;
+        devs[n] = dev;
+        vals[n] = g;
+        ++n;
     }
-    hipLaunchKernelGGL(k_emit, dim3(a.R), dim3(256), 0, st, a);
+    return g;
+}
+
+template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
+static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
+    const void* f = (const void*)k_build<KT, SAMPLE, HEAD_BF16, L_BF16>;
+    const int G = resident_grid(f);
+    if (G < 1) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL(k_build_init, dim3(1), dim3(256), 0, st, a, max_tiles(a.R, a.Ncap));
+    if (a.timing_hook) a.timing_hook(st, 0);
+    BuildArgs args = a;
+    void* kargs[] = {&args};
+    const hipError_t e = hipLaunchCooperativeKernel(f, dim3(G), dim3(256), kargs, 0, st);
+    if (a.timing_hook) a.timing_hook(st, 1);
+    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 
+template <int KT, bool SAMPLE>
+static hipError_t launch_build_ks(const dt_params* p, const BuildArgs& a, hipStream_t st) {
+    const bool hb = p->head_dtype == DT_BF16, lb = p->logits_dtype == DT_BF16;
+    if (hb) return lb ? launch_build_t<KT, SAMPLE, true, true>(a, st)
+                      : launch_build_t<KT, SAMPLE, true, false>(a, st);
+    return lb ? launch_build_t<KT, SAMPLE, false, true>(a, st)
+              : launch_build_t<KT, SAMPLE, false, false>(a, st);
+}
+
 template <int KT>
-static hipError_t launch_build_kt(const dt_params* p, const BuildArgs& a, int G, hipStream_t st) {
-    const bool sample = p->mode == DT_SAMPLE, hb = p->head_dtype == DT_BF16;
-    if (sample) return hb ? launch_build_t<KT, true, true>(a, G, st)
-                          : launch_build_t<KT, true, false>(a, G, st);
-    return hb ? launch_build_t<KT, false, true>(a, G, st)
-              : launch_build_t<KT, false, false>(a, G, st);
+static hipError_t launch_build_kt(const dt_params* p, const BuildArgs& a, hipStream_t st) {
+    return p->mode == DT_SAMPLE ? launch_build_ks<KT, true>(p, a, st)
+                                : launch_build_ks<KT, false>(p, a, st);
 }
 
 hipError_t launch_build(const dt_params* p, const Layout& lay, const BuildArgs& a,
                         hipStream_t st) {
     switch (lay.KT) {
-        case 1: return launch_build_kt<1>(p, a, lay.G, st);
-        case 2: return launch_build_kt<2>(p, a, lay.G, st);
-        case 4: return launch_build_kt<4>(p, a, lay.G, st);
-        default: return launch_build_kt<8>(p, a, lay.G, st);
+        case 1: return launch_build_kt<1>(p, a, st);
+        case 2: return launch_build_kt<2>(p, a, st);
+        case 4: return launch_build_kt<4>(p, a, st);
+        default: return launch_build_kt<8>(p, a, st);
     }
 }
 

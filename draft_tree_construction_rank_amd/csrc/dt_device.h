@@ -93,6 +93,73 @@ __device__ __forceinline__ int low_fi(uint32_t low) { return 127 - (int)((low >>
 __device__ __forceinline__ int low_rank(uint32_t low) { return 15 - (int)(low & 15u); }
 
 // ---------------------------------------------------------------------------------------
+// Coherent accesses for data that workgroups of one persistent kernel hand to each other.
+// Each XCD has its own L2, so a plain load can return a line another XCD has since
+// rewritten.  Agent-scope relaxed atomics are issued with the agent-coherence bit: stores
+// write through to the coherent level and loads read from it, so no L2 writeback or
+// invalidate is needed.  publish() waits until this wavefront's earlier stores have been
+// acknowledged; a workgroup publishes (every wavefront, then a barrier) before one thread
+// announces the data with a counter or flag.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t cld32(const void* p) {
+    return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t cld64(const void* p) {
+    return __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst32(void* p, uint32_t v) {
+    __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst64(void* p, uint64_t v) {
+    __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t cadd32(void* p, uint32_t v) {
+    return __hip_atomic_fetch_add((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int cldi(const int* p) { return (int)cld32(p); }
+__device__ __forceinline__ void csti(int* p, int v) { cst32(p, (uint32_t)v); }
+__device__ __forceinline__ void publish() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ void publish_wg() {
+    publish();
+    __syncthreads();
+}
+
+__device__ __forceinline__ FrontEntry ld_front(const FrontEntry* p) {
+    const uint64_t w0 = cld64(p), w1 = cld64((const char*)p + 8), w2 = cld64((const char*)p + 16);
+    FrontEntry e;
+    e.self = (uint32_t)w0;
+    e.token = (int32_t)(uint32_t)(w0 >> 32);
+    e.s = __uint_as_float((uint32_t)w1);
+    e.pad = (uint32_t)(w1 >> 32);
+    e.hash = w2;
+    return e;
+}
+__device__ __forceinline__ void st_front(FrontEntry* p, const FrontEntry& e) {
+    cst64(p, (uint64_t)e.self | ((uint64_t)(uint32_t)e.token << 32));
+    cst64((char*)p + 8, (uint64_t)__float_as_uint(e.s) | ((uint64_t)e.pad << 32));
+    cst64((char*)p + 16, e.hash);
+}
+__device__ __forceinline__ ChildRec ld_child(const ChildRec* p) {
+    const uint64_t w0 = cld64(p), w1 = cld64((const char*)p + 8), w2 = cld64((const char*)p + 16);
+    ChildRec c;
+    c.token = (int32_t)(uint32_t)w0;
+    c.s = __uint_as_float((uint32_t)(w0 >> 32));
+    c.logq = __uint_as_float((uint32_t)w1);
+    c.pad = (uint32_t)(w1 >> 32);
+    c.hash = w2;
+    return c;
+}
+__device__ __forceinline__ void st_child(ChildRec* p, const ChildRec& c) {
+    cst64(p, (uint64_t)(uint32_t)c.token | ((uint64_t)__float_as_uint(c.s) << 32));
+    cst64((char*)p + 8, (uint64_t)__float_as_uint(c.logq) | ((uint64_t)c.pad << 32));
+    cst64((char*)p + 16, c.hash);
+}
+
+// ---------------------------------------------------------------------------------------
 // bf16 / f32 element access
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -104,59 +171,89 @@ __device__ __forceinline__ float load_logit(const void* base, size_t idx, bool b
 }
 
 // ---------------------------------------------------------------------------------------
-// Ranked lists held in registers: (key desc, token asc), length KT, compile-time indices
-// only (no scratch).
+// Ranked lists held in registers.  An entry is one u64 whose unsigned order is the ranking
+// order (key desc, token asc): high word = the key's float bits mapped to an order-preserving
+// unsigned (ord32), low word = ~token.  0 marks an empty slot (below every real entry).  The
+// tempered logit y (log2 units) travels with each entry.  Lists are sorted descending and
+// use compile-time indices only (no scratch).
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float ka, int ta, float kb, int tb) {
-    return ka > kb || (ka == kb && ta < tb);
+__device__ __forceinline__ uint32_t ord32(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+__device__ __forceinline__ float unord32(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t pack_entry(float key, int tok) {
+    return ((uint64_t)ord32(key) << 32) | (uint64_t)(~(uint32_t)tok);
+}
+__device__ __forceinline__ int entry_tok(uint64_t e) { return (int)~(uint32_t)e; }
+__device__ __forceinline__ float entry_key(uint64_t e) { return unord32((uint32_t)(e >> 32)); }
 
 template <int KT>
 struct TopK {
-    float key[KT];
-    float y[KT];  // tempered logit in log2 units (z / T * log2 e)
-    int tok[KT];
+    uint64_t k[KT];
+    float y[KT];
 
     __device__ __forceinline__ void init() {
 #pragma unroll
         for (int i = 0; i < KT; ++i) {
-            key[i] = -INFINITY;
+            k[i] = 0;
             y[i] = -INFINITY;
-            tok[i] = 0x7fffffff;
         }
     }
-    // Insert (k, yy, t) if it ranks among the KT best.
-    __device__ __forceinline__ void push(float k, float yy, int t) {
-        if (!better(k, t, key[KT - 1], tok[KT - 1])) return;
+    // Insert one entry: a branch-free pass of compare-exchanges down the sorted list.
+    __device__ __forceinline__ void push(uint64_t c, float yc) {
 #pragma unroll
-        for (int i = KT - 1; i >= 0; --i) {
-            const bool gi = better(k, t, key[i], tok[i]);
-            const bool gp = (i > 0) ? better(k, t, key[i - 1], tok[i - 1]) : false;
-            if (gi) {
-                if (gp) {
-                    key[i] = key[i - 1];
-                    y[i] = y[i - 1];
-                    tok[i] = tok[i - 1];
-                } else {
-                    key[i] = k;
-                    y[i] = yy;
-                    tok[i] = t;
+        for (int i = 0; i < KT; ++i) {
+            const bool gt = c > k[i];
+            const uint64_t tk = k[i];
+            const float ty = y[i];
+            k[i] = gt ? c : tk;
+            y[i] = gt ? yc : ty;
+            c = gt ? tk : c;
+            yc = gt ? ty : yc;
+        }
+    }
+    // Keep the KT best of this list and another sorted list (bitonic merge: the pairwise
+    // maxima of this list and the reversed other list form a bitonic sequence holding the KT
+    // best, which half-cleaners then sort).
+    __device__ __forceinline__ void merge(const uint64_t (&ok)[KT], const float (&oy)[KT]) {
+#pragma unroll
+        for (int i = 0; i < KT; ++i) {
+            const bool gt = ok[KT - 1 - i] > k[i];
+            k[i] = gt ? ok[KT - 1 - i] : k[i];
+            y[i] = gt ? oy[KT - 1 - i] : y[i];
+        }
+#pragma unroll
+        for (int half = KT / 2; half >= 1; half >>= 1) {
+#pragma unroll
+            for (int i = 0; i < KT; ++i) {
+                if ((i & half) == 0) {
+                    const int j = i + half;
+                    const bool sw = k[j] > k[i];
+                    const uint64_t ki = k[i], kj = k[j];
+                    const float yi = y[i], yj = y[j];
+                    k[i] = sw ? kj : ki;
+                    k[j] = sw ? ki : kj;
+                    y[i] = sw ? yj : yi;
+                    y[j] = sw ? yi : yj;
                 }
             }
         }
     }
     // Merge with the list held by lane (lane ^ off) of the same wavefront.
     __device__ __forceinline__ void merge_xor(int off) {
-        float ok[KT], oy[KT];
-        int ot[KT];
+        uint64_t ok[KT];
+        float oy[KT];
 #pragma unroll
         for (int i = 0; i < KT; ++i) {
-            ok[i] = __shfl_xor(key[i], off);
+            const uint32_t lo = __shfl_xor((uint32_t)k[i], off);
+            const uint32_t hi = __shfl_xor((uint32_t)(k[i] >> 32), off);
+            ok[i] = ((uint64_t)hi << 32) | lo;
             oy[i] = __shfl_xor(y[i], off);
-            ot[i] = __shfl_xor(tok[i], off);
         }
-#pragma unroll
-        for (int i = 0; i < KT; ++i) push(ok[i], oy[i], ot[i]);
+        merge(ok, oy);
     }
 };
 

@@ -15,7 +15,9 @@ constexpr int kMaxNcap = 64;
 constexpr int kMaxB = 32;
 constexpr int kMaxK = 8;
 constexpr int kSelectSlots = 1024;  // >= Ncap + Ncap * k
-constexpr int kMaxSplits = 256;     // vocabulary splits per parent row (merge work bound)
+constexpr int kMaxSplits = 512;     // vocabulary splits per parent row (merge work bound)
+constexpr int kMaxGrid = 1024;      // largest grid of the persistent construction kernel
+constexpr int kBlockCols = 32;      // vocabulary columns per MFMA block of the expansion
 
 // A frontier entry: a node that is (or was) expanded at some level.  self = the low word of
 // its selection key (0xFFFFFFFF for the root).
@@ -39,9 +41,9 @@ struct alignas(8) ChildRec {
 // Offsets (bytes) of every workspace region; sizes depend only on the parameters.
 struct Layout {
     size_t rows;      // int2 [R*Ncap]: (request, frontier index) of every parent row
-    size_t sync;      // unsigned [kSyncWords]: level counters (offset 0)
-    size_t roff;      // int [R]: first parent row of each request at the current level
-    size_t pdone;     // int [R]: merge parts finished per request
+    size_t sync;      // unsigned [kSyncWords]: generation, error flag, per-level counters
+    size_t tdone;     // unsigned [tiles]: expansion items finished per row tile
+    size_t rdone;     // unsigned [R]: parent rows merged per request
     size_t front;     // FrontEntry [R][B+1][Ncap]
     size_t fcount;    // int [R][B+1]: frontier size per level (level 0 = the root)
     size_t arena;     // ChildRec [R][B][Ncap][k]
@@ -56,7 +58,7 @@ struct Layout {
     size_t vstate;    // VState [R]
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
     size_t total;
-    int G;            // largest grid of the construction kernel
+    int G;            // largest grid of the construction kernel (sizes the partial records)
     int NC;           // vocabulary chunks of 128 columns
     int KT;           // top-k list length used by the kernels (1, 2, 4 or 8)
     int vsplits;      // vocabulary splits per request in sample verify
@@ -76,10 +78,15 @@ struct alignas(8) VState {
     uint64_t hash;
 };
 
-// Control words at the start of the workspace.
-constexpr int kSyncFinish = 3;  // workgroups done with the select phase
-constexpr int kSyncRows = 4;    // parent rows at the current level
-constexpr int kSyncWords = 8;
+// Control words at the start of the workspace.  Per-level words are indexed by the level
+// (1..B+1) so that a late workgroup never reads the next level's value.
+constexpr int kSyncGen = 0;        // last level whose select is complete (0 after set-up)
+constexpr int kSyncErr = 1;        // set when a bounded wait gives up
+constexpr int kSyncRows = 8;       // [level]: parent rows expanded at that level
+constexpr int kSyncReqs = 48;      // [level]: requests with at least one parent row
+constexpr int kSyncTask = 88;      // [level]: merge-task counter
+constexpr int kSyncDone = 128;     // [level]: requests whose select is done
+constexpr int kSyncWords = 192;
 
 // Arguments of the tree-construction kernels (passed by value).
 struct BuildArgs {
@@ -91,9 +98,9 @@ struct BuildArgs {
     const int32_t* n_budget;
     const float* tau;
     unsigned* sync;
+    unsigned* tdone;
+    unsigned* rdone;
     int2* rows;
-    int* roff;
-    int* pdone;
     FrontEntry* front;
     int* fcount;
     ChildRec* arena;
@@ -115,6 +122,8 @@ struct BuildArgs {
 // Host-side launchers (enqueue only).
 hipError_t launch_build(const dt_params* p, const Layout& lay, const BuildArgs& a,
                         hipStream_t st);
+// Tiles of kTileRows parent rows needed for R * Ncap rows.
+inline int max_tiles(int R, int Ncap) { return (R * Ncap + kTileRows - 1) / kTileRows; }
 hipError_t launch_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target,
                                 const dt_verify_out* out, hipStream_t st);
 hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,

@@ -16,12 +16,21 @@ constexpr int kAStride = 256 + 8;  // bf16 elements per LDS row of A (padding ag
 constexpr int kAfStride = 66;      // floats per LDS row of A for float32 heads (r <= 64)
 constexpr int kZStride = kChunkCols + 4;
 
+// Zero that the compiler cannot see through: added to the thread index where per-thread
+// address arithmetic would otherwise be hoisted out of a persistent loop and kept (spilled)
+// for the kernel's lifetime.
+__device__ __forceinline__ int opaque_zero() {
+    int z;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+    return z;
+}
+
 // A tile: rows < nrows take U[token_of(row)], other rows and columns >= r are zero.
 // 256 threads.  Ends with the caller's __syncthreads().
 template <bool HEAD_BF16, typename TokFn>
 __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, TokFn token_of,
                                             uint16_t* sA, float* sAf) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x + opaque_zero();
     if constexpr (HEAD_BF16) {
         // 64 rows x 33 16-byte segments: every address is clamped into the row so that all
         // loads of a thread are unconditional and can be in flight together.
@@ -125,6 +134,80 @@ __device__ __forceinline__ void mma_chunk(const void* Wt, int V, int r, int col0
         if (two) sZ[(32 + row) * kZStride + wave * 32 + (lane & 31)] = acc1[i];
     }
     __syncthreads();
+}
+
+// Transposed block for the expansion: D[c][p] = Wt[c0 + c] . A[p] for 32 vocabulary columns c
+// and the tile's parent rows p, with the head rows of W as the MFMA A operand and the parent
+// rows (from LDS) as the B operand.  In the 32x32 output layout lane l then holds parent row
+// p = l%32 (acc0; row 32 + l%32 in acc1) at columns c0 + 8(e/4) + 4(l/32) + e%4, e = 0..15,
+// so a parent row's online softmax and top-k run on the accumulators directly.  Columns past
+// V read column V-1 and K offsets past r read offset 0 (the LDS rows are zero there).
+//
+// bf16 heads: the 16 A fragments of a block (16 KB per wavefront) are loaded by
+// load_wfrag() into registers, so the caller can issue the next block's loads before it
+// works on the current one.
+__device__ __forceinline__ void load_wfrag(const void* Wt, int V, int r, int c0, bf16x8 (&wf)[16]) {
+    const int lane = threadIdx.x & 63;
+    const int col = c0 + (lane & 31);
+    const int khalf = (lane >> 5) * 8;
+    const uint16_t* wrow = (const uint16_t*)Wt + (size_t)(col < V ? col : V - 1) * r;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const int kk = s * 16 + khalf;
+        wf[s] = __builtin_bit_cast(bf16x8, *(const uint4*)(wrow + (kk < r ? kk : 0)));
+    }
+}
+
+__device__ __forceinline__ void mma_wfrag(const bf16x8 (&wf)[16], bool two, const uint16_t* sA,
+                                          f32x16& acc0, f32x16& acc1) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        acc0[i] = 0.0f;
+        acc1[i] = 0.0f;
+    }
+    const uint16_t* b0 = sA + (lane & 31) * kAStride + (lane >> 5) * 8;
+    if (two) {
+        const uint16_t* b1 = b0 + 32 * kAStride;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const uint4 u0 = *(const uint4*)(b0 + s * 16);
+            const uint4 u1 = *(const uint4*)(b1 + s * 16);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u0),
+                                                           acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u1),
+                                                           acc1, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const uint4 u0 = *(const uint4*)(b0 + s * 16);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u0),
+                                                           acc0, 0, 0, 0);
+        }
+    }
+}
+
+// float32 heads (r <= 64): the whole transposed block, f32 32x32x2 MFMA.
+__device__ __forceinline__ void xblock_mma_f32(const void* Wt, int V, int r, int c0, bool two,
+                                               const float* sAf, f32x16& acc0, f32x16& acc1) {
+    const int lane = threadIdx.x & 63;
+    const int col = c0 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        acc0[i] = 0.0f;
+        acc1[i] = 0.0f;
+    }
+    const int kh = lane >> 5;
+    const float* wrow = (const float*)Wt + (size_t)(col < V ? col : V - 1) * r;
+    const float* b0 = sAf + (lane & 31) * kAfStride + kh;
+    const int nsteps = (r + 1) >> 1;
+    for (int s = 0; s < nsteps; ++s) {
+        const int kk = 2 * s + kh;
+        const float w = wrow[kk < r ? kk : 0];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(w, b0[2 * s], acc0, 0, 0, 0);
+        if (two) acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(w, b0[32 * kAfStride + 2 * s], acc1, 0, 0, 0);
+    }
 }
 
 }  // namespace dt

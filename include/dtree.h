@@ -50,7 +50,9 @@ enum { DT_GREEDY = 0, DT_SAMPLE = 1 };
 /* Per-request status bits written to dt_tree.status. */
 enum {
     DT_REQ_BAD_ROOT = 1,       /* root_token outside [0, V): empty tree, nothing emitted */
-    DT_REQ_BUDGET_CLAMPED = 2  /* n_budget outside [0, Ncap]: clamped into range */
+    DT_REQ_BUDGET_CLAMPED = 2, /* n_budget outside [0, Ncap]: clamped into range */
+    DT_REQ_SYNC_TIMEOUT = 4    /* an internal wait between workgroups gave up (about two
+                                  seconds): the tree is reported empty */
 };
 
 /* Round parameters (host struct, read synchronously). */

@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Benchmark: one step = one round of the whole hot path on one MI355X -- tree_build (all
+levels: Markov bias, softmax, top-k, calibration, survival, select, emit) followed by
+tree_verify_greedy -- for the batched draft-tree workload: R = 64 requests, B = 16, k = 4,
+N = 64, V = 151936, r = 256, bf16, per-request planted-peak strength U(2, 9), stopping
+threshold tau (default 0.05), greedy verification against rho = 0.8 targets.
+
+Prints one JSON line: draft trees/s (whole job), ms per step, the roofline of the dominant
+kernel (the fused expansion kernel, timed live with HIP events on the launch stream), and the
+CPU oracle's rate on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--tau T] [--no-cpu-baseline] [--no-extras]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft trees/sec & µs/round (B=16,k=4,N=64,V=151936); % HBM peak"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ("draft_tree_construction_rank_amd/csrc/build_kernels.hip",
+                  "draft_tree_construction_rank_amd/csrc/dt_mma.h",
+                  "draft_tree_construction_rank_amd/csrc/dt_device.h")
+COUNTERS = os.path.join(ROOT, "profiles", "k_build_counters.json")
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def gpu_targets(inst, tree, rho, gen_seed, torch):
+    """Target rows [R][Ncap+1][V] on the GPU: rho * L[depth] + sqrt(1-rho^2) * E, where E is a
+    fresh draw of the block-logit law (N(0, 2) plus eight planted peaks with Zipf(1.1)
+    ranks and the request's strength).  Keyed by slot (timing only, no parity use)."""
+    import numpy as np
+    R, N1, V = inst.R, inst.Ncap + 1, inst.V
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(gen_seed)
+    E = torch.randn((R, N1, V), generator=g, device=dev, dtype=torch.float32) * 2.0
+    rng = np.random.default_rng([inst.seed, 99])
+    perm = np.random.default_rng([inst.seed, 3]).permutation(V)
+    w = np.arange(1, V + 1, dtype=np.float64) ** -1.1
+    w /= w.sum()
+    cdf = np.cumsum(w)
+    picks = np.searchsorted(cdf, rng.random((R, N1, 16)))  # ranks; duplicates dropped below
+    idx, val = [], []
+    for r in range(R):
+        boosts = np.linspace(inst.strength[r], inst.strength[r] * 4.0 / 9.0, 8)
+        for i in range(N1):
+            seen = []
+            for pk in picks[r, i]:
+                if pk not in seen:
+                    seen.append(pk)
+                if len(seen) == 8:
+                    break
+            for j, pk in enumerate(seen):
+                idx.append((r * N1 + i) * V + int(perm[pk]))
+                val.append(boosts[j])
+    flat = E.view(-1)
+    flat.index_add_(0, torch.tensor(idx, device=dev, dtype=torch.int64),
+                    torch.tensor(val, device=dev, dtype=torch.float32))
+    depth = tree["depth"].to(torch.int64)  # [R][Ncap], 0 for empty slots
+    rows_depth = torch.cat([torch.zeros((R, 1), dtype=torch.int64, device=dev), depth], 1)
+    Lext = torch.from_numpy(inst.Lext).to(dev)  # [R][B+1][V]
+    Lsel = torch.gather(Lext, 1, rows_depth.unsqueeze(-1).expand(R, N1, V))
+    b = math.sqrt(max(0.0, 1.0 - rho * rho))
+    return (rho * Lsel + b * E).to(torch.bfloat16).contiguous()
+
+
+def algorithmic_bytes(inst, level_rows_per_req, n_expand) -> float:
+    """Bytes the method must move in one round (per the survey's per-unit figures):
+    L rows used (one V-row per request per level at which it expands) + W once + U rows."""
+    V, r = inst.V, inst.r
+    l_bytes = sum(level_rows_per_req) * V * 2
+    return l_bytes + r * V * 2 + sum(n_expand) * r * 2
+
+
+def run_workload(inst, tau, steps, warmup, torch, rt, B, timing=True):
+    d = rt.to_device(inst, "cuda", tau=tau)
+    rnd = rt.Round(inst)
+    rnd.build(d)
+    torch.cuda.synchronize()
+    tgt = gpu_targets(inst, rnd.tree, inst.rho, 1234, torch)
+    rnd.verify_greedy(tgt)
+    torch.cuda.synchronize()
+    tree_np = rt.tree_to_numpy(rnd.tree)
+    # per request: number of levels at which it expanded = distinct depths of expanded nodes
+    levels_used = []
+    for i in range(inst.R):
+        n = int(tree_np["n_nodes"][i])
+        ds = set(int(x) for x in tree_np["depth"][i, :n] if int(x) < inst.B)
+        levels_used.append(1 + len(ds))  # the root's level plus one per expanded depth
+    # best-first expansion count: the root plus every tree node above the last block position
+    n_expand = [1 + int((tree_np["depth"][i, :int(tree_np["n_nodes"][i])] < inst.B).sum())
+                for i in range(inst.R)]
+    for _ in range(warmup):
+        rnd.build(d)
+        rnd.verify_greedy(tgt)
+    torch.cuda.synchronize()
+    if timing:
+        B.timing_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        rnd.build(d)
+        rnd.verify_greedy(tgt)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kms, launches = B.timing_read() if timing else (0.0, 0)
+    if timing:
+        B.timing_enable(False)
+    vout = {k: v.cpu().numpy() for k, v in rnd.vout.items()}
+    return dict(ms_per_step=(t1 - t0) * 1e3 / steps, expand_ms=kms, expand_launches=launches,
+                levels_used=levels_used, n_expand=n_expand, tree=tree_np, verify=vout,
+                target=tgt, level_rows=tree_np["level_rows"].tolist())
+
+
+def build_latency(inst, torch, rt, steps=30, warmup=5):
+    """Microseconds per tree_build call alone (one request, the B=16/k=4/N=64 headline)."""
+    d = rt.to_device(inst, "cuda")
+    rnd = rt.Round(inst)
+    for _ in range(warmup):
+        rnd.build(d)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        rnd.build(d)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e3 / steps
+
+
+def cpu_baseline(inst, tau, res, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample: build + greedy verify of the first
+    requests of the same workload until ~budget_s of CPU time (single thread)."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    tgt = res["target"]
+    done, t0 = 0, time.perf_counter()
+    while done < inst.R and time.perf_counter() - t0 < budget_s:
+        row = tgt[done:done + 1].float().cpu().numpy()
+        tr = oracle.build_tree(inst, requests=[done], tau=tau)
+        oracle.verify_greedy(inst, tr, row)
+        done += 1
+    dt = time.perf_counter() - t0
+    try:
+        model = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                 if ln.startswith("model name")][0]
+    except Exception:
+        model = platform.processor()
+    return {"value": done / dt, "unit": "trees/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d requests (build + greedy verify, single thread, %.1f s); "
+                      "host %s, %d cores" % (done, inst.R, dt, model, os.cpu_count() or 0)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--tau", type=float, default=0.05)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (requests shard "
+              "across GPUs without communication; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from draft_tree_construction_rank_amd import binding as B
+    from draft_tree_construction_rank_amd import inputs
+    from draft_tree_construction_rank_amd import runner as rt
+
+    B.lib()  # fail loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    if args.copy_calibration:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    inst = inputs.make_instance("batched", tau=args.tau)
+    res = run_workload(inst, args.tau, args.steps, args.warmup, torch, rt, B)
+    ms = res["ms_per_step"]
+    value = inst.R / (ms * 1e-3)
+    # roofline of the dominant kernel: the persistent construction kernel k_build (one
+    # cooperative launch per round), timed with HIP events on the launch stream
+    launches_per_step = res["expand_launches"] / args.steps
+    avg_us = res["expand_ms"] * 1e3 / max(1, res["expand_launches"])
+    round_bytes = algorithmic_bytes(inst, res["levels_used"], res["n_expand"])
+    per_launch_bytes = round_bytes / launches_per_step
+    achieved = per_launch_bytes / (avg_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(COUNTERS):
+        c = json.load(open(COUNTERS))
+        if c.get("kernel_sha") == kernel_sha() and c.get("tau") == args.tau:
+            traffic = c.get("hbm_bytes_per_launch")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": "k_build (persistent level loop: MFMA Markov bias + online softmax + "
+                      "top-k per vocabulary split, merge, calibration, survival, select, emit)",
+            "avg_launch_us": round(avg_us, 3), "launches_per_step": launches_per_step,
+            "alg_bytes_per_launch": int(per_launch_bytes)}
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "trees/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": "batched draft-tree round: tree_build + tree_verify_greedy, "
+                                   "R=64, B=16, k=4, N=64, V=151936, r=256, tau=%g" % args.tau,
+                       "R": inst.R, "B": inst.B, "k": inst.k, "N": inst.Ncap, "V": inst.V,
+                       "r": inst.r, "tau": args.tau},
+            "us_per_round": round(ms * 1e3, 2),
+            "roofline": roof,
+            "tree_stats": {"mean_nodes": float(res["tree"]["n_nodes"].mean()),
+                           "mean_expansions": float(sum(res["n_expand"]) / inst.R),
+                           "mean_accept_len": float(res["verify"]["accept_len"].mean()),
+                           "level_rows": res["level_rows"]}}
+    if not args.no_extras:
+        extras = {}
+        h = inputs.make_instance("b16")
+        extras["tree_build_us_R1_B16_k4_N64"] = round(build_latency(h, torch, rt), 2)
+        for t in (0.2, 0.5):
+            if t != args.tau:
+                r2 = run_workload(inst, t, 20, 3, torch, rt, B, timing=False)
+                extras["batched_tau%g_trees_per_s" % t] = round(inst.R / (r2["ms_per_step"] * 1e-3), 1)
+        line["extras"] = extras
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inst, args.tau, res)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -117,7 +117,8 @@ struct EmitSmem {
 template <int KT>
 struct BuildSmem {
     union {
-        uint16_t sA[kTileRows * kAStride];  // bf16 parent rows of U (expand)
+        uint16_t sA[kTileRows * kAStride];  // bf16 parent rows of U (tile-mode expand)
+        uint4 wst[2][kBlockCols * 32];      // two staged 32-column blocks of W (group-mode expand)
         float sAf[kTileRows * kAfStride];   // f32 parent rows of U (expand)
         uint64_t keys[kSelectSlots];        // select
         EmitSmem em;                        // emit
@@ -126,6 +127,7 @@ struct BuildSmem {
     float mrec[4][rec_floats(KT)];             // per-wavefront lists of a merged row
     size_t lbase[kTileRows];
     uint64_t hash[kTileRows];
+    uint64_t rkth[128];  // per parent row of an item: the largest KT-th list entry seen so far
     int tok[kTileRows];
     int sh[256];
     int bcast[4];
@@ -179,103 +181,167 @@ __device__ __forceinline__ void load_lgroups(const BuildArgs& a, size_t lbase, i
     }
 }
 
-template <int KT, bool SAMPLE, bool L_BF16>
-__device__ __forceinline__ void expand_epilogue(const BuildArgs& a, const f32x16& acc,
-                                                const LGroups<L_BF16>& lw, int c0, int h,
-                                                uint64_t hh, TopK<KT>& top, Lse2& st) {
-    float z[16];
+// Descending bitonic sort of n = 1, 2, 4 or 8 floats (compile-time indices).
+template <int N>
+__device__ __forceinline__ void sort_desc(float* v) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        if constexpr (L_BF16) {
-            z[4 * j + 0] = acc[4 * j + 0] + bf16_lo(lw.g[j].x);
-            z[4 * j + 1] = acc[4 * j + 1] + bf16_hi(lw.g[j].x);
-            z[4 * j + 2] = acc[4 * j + 2] + bf16_lo(lw.g[j].y);
-            z[4 * j + 3] = acc[4 * j + 3] + bf16_hi(lw.g[j].y);
-        } else {
-            z[4 * j + 0] = acc[4 * j + 0] + __uint_as_float(lw.g[j].x);
-            z[4 * j + 1] = acc[4 * j + 1] + __uint_as_float(lw.g[j].y);
-            z[4 * j + 2] = acc[4 * j + 2] + __uint_as_float(lw.g[j].z);
-            z[4 * j + 3] = acc[4 * j + 3] + __uint_as_float(lw.g[j].w);
-        }
-    }
-    uint32_t vmask = 0xFFFFu;
-    if (c0 + kBlockCols > a.V) {
+    for (int size = 2; size <= N; size <<= 1) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = c0 + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (c >= a.V) {
-                z[e] = -INFINITY;
-                vmask &= ~(1u << e);
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int j = i ^ stride;
+                if (j > i) {
+                    const bool desc = (i & size) == 0;
+                    const float hi = fmaxf(v[i], v[j]), lo = fminf(v[i], v[j]);
+                    v[i] = desc ? hi : lo;
+                    v[j] = desc ? lo : hi;
+                }
             }
         }
     }
-    float cm = z[0];
+}
+
+// The KT-th largest of 16 values (a lower bound for pruning candidates): sort groups of KT,
+// then merge sorted groups pairwise keeping the KT largest (the elementwise maxima of one
+// list and the reversed other list are exactly the KT largest of both, as a bitonic
+// sequence); the last merge only needs the minimum of that set.
+template <int KT>
+__device__ __forceinline__ float kth_largest16(const float (&z)[16]) {
+    constexpr int NG = 16 / KT;
+    float g[NG][KT];
 #pragma unroll
-    for (int e = 1; e < 16; ++e) cm = fmaxf(cm, z[e]);
-    if (cm != -INFINITY) {
-        cm *= a.y2scale;
+    for (int q = 0; q < NG; ++q) {
+#pragma unroll
+        for (int i = 0; i < KT; ++i) g[q][i] = z[q * KT + i];
+        sort_desc<KT>(g[q]);
+    }
+#pragma unroll
+    for (int n = NG; n > 2; n >>= 1) {
+#pragma unroll
+        for (int q = 0; q < n / 2; ++q) {
+            float c[KT];
+#pragma unroll
+            for (int i = 0; i < KT; ++i) c[i] = fmaxf(g[2 * q][i], g[2 * q + 1][KT - 1 - i]);
+            // bitonic -> descending: half-cleaners
+#pragma unroll
+            for (int half = KT / 2; half >= 1; half >>= 1) {
+#pragma unroll
+                for (int i = 0; i < KT; ++i) {
+                    if ((i & half) == 0) {
+                        const float hi = fmaxf(c[i], c[i + half]), lo = fminf(c[i], c[i + half]);
+                        c[i] = hi;
+                        c[i + half] = lo;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < KT; ++i) g[q][i] = c[i];
+        }
+    }
+    float m = INFINITY;
+#pragma unroll
+    for (int i = 0; i < KT; ++i) m = fminf(m, fmaxf(g[0][i], g[1][KT - 1 - i]));
+    return m;
+}
+
+// Block logits of a lane's 16 columns as float32, laid out like the accumulator, so that the
+// MFMA chain adds the Markov bias onto them: z = L + U.W comes out of the MFMA directly.
+template <bool L_BF16>
+__device__ __forceinline__ void lgroups_to_acc(const LGroups<L_BF16>& lw, f32x16& acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if constexpr (L_BF16) {
+            acc[4 * j + 0] = bf16_lo(lw.g[j].x);
+            acc[4 * j + 1] = bf16_hi(lw.g[j].x);
+            acc[4 * j + 2] = bf16_lo(lw.g[j].y);
+            acc[4 * j + 3] = bf16_hi(lw.g[j].y);
+        } else {
+            acc[4 * j + 0] = __uint_as_float(lw.g[j].x);
+            acc[4 * j + 1] = __uint_as_float(lw.g[j].y);
+            acc[4 * j + 2] = __uint_as_float(lw.g[j].z);
+            acc[4 * j + 3] = __uint_as_float(lw.g[j].w);
+        }
+    }
+}
+
+// Epilogue of one 32-column block for one parent row: z holds the row's 16 values of this
+// lane (columns c0 + 8(e/4) + 4h + e%4).  Updates the online log-sum-exp, then offers the
+// values that can still rank among the KT best to the ranked list.  Any lane's KT-th list
+// entry is a lower bound for the row's final KT-th entry (its list holds KT entries of other
+// columns that rank above it), so the candidate test uses the best such bound known: the
+// lane's own and `row_kth` (LDS, shared by the workgroup's lanes of the row; may be null).
+template <int KT, bool SAMPLE>
+__device__ __forceinline__ void expand_epilogue(const BuildArgs& a, f32x16& z, int c0, int h,
+                                                uint64_t hh, bool live, uint64_t* row_kth,
+                                                TopK<KT>& top, Lse2& st) {
+    if (c0 + kBlockCols > a.V) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (c0 + 8 * (e >> 2) + 4 * h + (e & 3) >= a.V) z[e] = -INFINITY;
+    }
+    float zmax = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) zmax = fmaxf(zmax, z[e]);
+    if (zmax != -INFINITY) {
+        const float cm = zmax * a.y2scale;
         if (cm > st.m) {
             st.s = (st.m == -INFINITY) ? 0.0f : st.s * exp2f(st.m - cm);
             st.m = cm;
         }
+        // terms below 2^-126 of the running maximum flush to zero: far below float32
+        // resolution of the sum
         float ps = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) ps += exp2f(z[e] * a.y2scale - st.m);  // exp2(-inf) = 0
+        for (int e = 0; e < 16; ++e) ps += __builtin_amdgcn_exp2f(z[e] * a.y2scale - st.m);
         st.s += ps;
     }
-    // Candidates: a superset test against a lower bound of the KT-th best key among the list
-    // and this block (ties and the Gumbel noise are settled by push(), which compares exact
-    // entries).  Greedy: the bound is the larger of the list's KT-th key and the smallest of
-    // the maxima of KT disjoint groups of the block (KT elements of the block are >= it).
+    if (!live) return;
+    uint64_t kth = top.k[KT - 1];
+    if (row_kth) kth = kth > *row_kth ? kth : *row_kth;
+    const float tk = kth ? entry_key(kth) : -INFINITY;
+    // Candidates are values z with z >= thr, a superset of those that can enter the list
+    // (ties and the Gumbel noise are settled by push(), which compares exact entries).
     // Sample keys are z / T + G with G < kGumbelMax, so z < (tk - kGumbelMax) T cannot
-    // qualify.
-    const float tk = top.k[KT - 1] ? entry_key(top.k[KT - 1]) : -INFINITY;
-    float thr;
-    if constexpr (SAMPLE) {
-        thr = (tk - kGumbelMax) / a.invT;
-    } else {
-        constexpr int GS = 16 / KT;
-        float bb = INFINITY;
-#pragma unroll
-        for (int g = 0; g < KT; ++g) {
-            float gm = z[g * GS];
-#pragma unroll
-            for (int i = 1; i < GS; ++i) gm = fmaxf(gm, z[g * GS + i]);
-            bb = fminf(bb, gm);
-        }
-        thr = fmaxf(tk, bb);
+    // qualify.  thr never drops below the lowest finite float, so masked columns (-inf)
+    // never qualify.
+    float thr = SAMPLE ? (tk - kGumbelMax) / a.invT : tk;
+    if (zmax < thr) return;
+    if constexpr (!SAMPLE) {
+        if (top.k[KT - 1] == 0) thr = fmaxf(thr, kth_largest16<KT>(*(const float(*)[16]) & z));
     }
-    uint32_t mask = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) mask |= (z[e] >= thr ? 1u : 0u) << e;
-    mask &= vmask;
-    if (mask == 0u) return;
+    thr = fmaxf(thr, -3.402823466e38f);
     if constexpr (SAMPLE) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            uint32_t gm = (mask >> (4 * j)) & 15u;
-            if (gm == 0u) continue;
-            const int cg = c0 + 8 * j + 4 * h;
-            const uint4 w = rand4((uint32_t)(cg >> 2), STREAM_GUMBEL, hh, a.seed_lo, a.seed_hi);
-            while (gm) {
-                const int e = __builtin_ctz(gm);
-                gm &= gm - 1u;
-                const uint32_t we = e == 0 ? w.x : e == 1 ? w.y : e == 2 ? w.z : w.w;
-                const float zj = e == 0 ? z[4 * j] : e == 1 ? z[4 * j + 1] : e == 2 ? z[4 * j + 2]
-                                                                                  : z[4 * j + 3];
-                top.push(pack_entry(zj * a.invT + gumbel(we), cg + e), zj * a.y2scale);
+            const bool any = z[4 * j] >= thr || z[4 * j + 1] >= thr || z[4 * j + 2] >= thr ||
+                             z[4 * j + 3] >= thr;
+            if (any) {
+                const int cg = c0 + 8 * j + 4 * h;
+                const uint4 w = rand4((uint32_t)(cg >> 2), STREAM_GUMBEL, hh, a.seed_lo, a.seed_hi);
+                const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (z[4 * j + i] >= thr) {
+                        const float zi = z[4 * j + i];
+                        top.push(pack_entry(zi * a.invT + gumbel(wv[i]), cg + i), zi * a.y2scale);
+                        if (top.k[KT - 1])
+                            thr = fmaxf(thr, (entry_key(top.k[KT - 1]) - kGumbelMax) / a.invT);
+                    }
+                }
             }
         }
     } else {
-        while (mask) {
-            const int e = __builtin_ctz(mask);
-            mask &= mask - 1u;
-            float zj = z[0];
 #pragma unroll
-            for (int q = 1; q < 16; ++q) zj = (e == q) ? z[q] : zj;
-            top.push(pack_entry(zj, c0 + 8 * (e >> 2) + 4 * h + (e & 3)), zj * a.y2scale);
+        for (int e = 0; e < 16; ++e) {
+            if (z[e] >= thr) {
+                top.push(pack_entry(z[e], c0 + 8 * (e >> 2) + 4 * h + (e & 3)), z[e] * a.y2scale);
+                if (top.k[KT - 1]) thr = fmaxf(thr, entry_key(top.k[KT - 1]));
+            }
         }
     }
+    if (row_kth && top.k[KT - 1] != 0)
+        atomicMax((unsigned long long*)row_kth, (unsigned long long)top.k[KT - 1]);
 }
 
 // Record of a list: (m, s) of the log-sum-exp, then KT packed entries as (lo, hi) words,
@@ -334,6 +400,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         sm.tok[tid] = tok;
         sm.lbase[tid] = lb;
         sm.hash[tid] = hh;
+        sm.rkth[tid] = 0;
     }
     __syncthreads();
     if constexpr (HEAD_BF16)
@@ -347,6 +414,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
     const size_t lb0 = sm.lbase[p0], lb1 = sm.lbase[32 + p0];
     const uint64_t hh0 = sm.hash[p0], hh1 = sm.hash[32 + p0];
     const bool lvec = (a.V & 3) == 0;
+    const bool live0 = p0 < nrows, live1 = 32 + p0 < nrows;  // rows past nrows only pad the tile
     TopK<KT> t0, t1;
     Lse2 s0, s1;
     t0.init();
@@ -366,16 +434,17 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         }
         for (; blk < b_end; blk += 4) {
             const int c0 = blk * kBlockCols;
-            const LGroups<L_BF16> l0 = n0, l1 = n1;
             f32x16 acc0, acc1;
+            lgroups_to_acc<L_BF16>(n0, acc0);
+            if (two) lgroups_to_acc<L_BF16>(n1, acc1);
             mma_wfrag(wf, two, sm.u.sA, acc0, acc1);
             if (blk + 4 < b_end) {
                 load_wfrag(a.Wt, a.V, a.r, c0 + 4 * kBlockCols, wf);
                 load_lgroups<L_BF16>(a, lb0, c0 + 4 * kBlockCols, h, lvec, n0);
                 if (two) load_lgroups<L_BF16>(a, lb1, c0 + 4 * kBlockCols, h, lvec, n1);
             }
-            expand_epilogue<KT, SAMPLE, L_BF16>(a, acc0, l0, c0, h, hh0, t0, s0);
-            if (two) expand_epilogue<KT, SAMPLE, L_BF16>(a, acc1, l1, c0, h, hh1, t1, s1);
+            expand_epilogue<KT, SAMPLE>(a, acc0, c0, h, hh0, live0, sm.rkth + p0, t0, s0);
+            if (two) expand_epilogue<KT, SAMPLE>(a, acc1, c0, h, hh1, live1, sm.rkth + 32 + p0, t1, s1);
         }
     } else {
         for (int blk = b_beg + wave; blk < b_end; blk += 4) {
@@ -384,9 +453,11 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
             load_lgroups<L_BF16>(a, lb0, c0, h, lvec, l0);
             if (two) load_lgroups<L_BF16>(a, lb1, c0, h, lvec, l1);
             f32x16 acc0, acc1;
+            lgroups_to_acc<L_BF16>(l0, acc0);
+            if (two) lgroups_to_acc<L_BF16>(l1, acc1);
             xblock_mma_f32(a.Wt, a.V, a.r, c0, two, sm.u.sAf, acc0, acc1);
-            expand_epilogue<KT, SAMPLE, L_BF16>(a, acc0, l0, c0, h, hh0, t0, s0);
-            if (two) expand_epilogue<KT, SAMPLE, L_BF16>(a, acc1, l1, c0, h, hh1, t1, s1);
+            expand_epilogue<KT, SAMPLE>(a, acc0, c0, h, hh0, live0, sm.rkth + p0, t0, s0);
+            if (two) expand_epilogue<KT, SAMPLE>(a, acc1, c0, h, hh1, live1, sm.rkth + 32 + p0, t1, s1);
         }
     }
     // lanes l and l ^ 32 hold the same parent row
@@ -423,6 +494,126 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         }
     }
     __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------
+// Group-mode expansion (levels with more than kTileRows parent rows, bf16 heads): an item is
+// a group of kGroupRows = 128 parent rows x a vocabulary split.  Wavefront w owns rows
+// 32w .. 32w+31 of the group and keeps their U rows as MFMA B fragments in registers for the
+// whole item; each 32-column block of W (32 rows of Wt, 16 KB at r = 256) is copied once per
+// workgroup into LDS with coalesced global->LDS loads, double-buffered so that block b+1
+// arrives while block b is multiplied, and read by all four wavefronts.  W is thus read once
+// per 128 parent rows.  The LDS copy stores row j's 16-byte chunk c at slot
+// 32j + (c ^ (j & 31)), so the fragment reads of 16 consecutive lanes hit distinct banks.
+// ---------------------------------------------------------------------------------------
+constexpr int kGroupRows = 128;
+
+// Issue this wavefront's quarter of the global->LDS copy of block `blk` (4 loads of 1 KB).
+__device__ __forceinline__ void stage_wblock(const BuildArgs& a, int blk, uint4* dst) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int chunks = a.r >> 3;  // 16-byte chunks per row of Wt
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int j = 4 * wave + q;            // 1 KB piece j = LDS slots 64j .. 64j+63
+        const int row = 2 * j + (lane >> 5);   // W row within the block
+        int c = (lane & 31) ^ (row & 31);      // chunk that belongs in this slot
+        c = c < chunks ? c : 0;                // past r: any finite data (U is zero there)
+        int col = blk * kBlockCols + row;
+        col = col < a.V ? col : a.V - 1;
+        const uint16_t* src = (const uint16_t*)a.Wt + (size_t)col * a.r + c * 8;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(dst + 64 * j),
+                                         16, 0, 0);
+    }
+}
+
+// Wait for this wavefront's outstanding global loads (including global->LDS copies).
+__device__ __forceinline__ void wait_vm() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <int KT, bool SAMPLE, bool L_BF16>
+__device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int M, int S, int grp,
+                                             int split, BuildSmem<KT>& sm) {
+    constexpr int RS = rec_floats(KT);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, p0 = lane & 31;
+    const int lvl = level - 1;
+    const int row = grp * kGroupRows + 32 * wave + p0;
+    const bool live = row < M;
+    const int NB = (a.V + kBlockCols - 1) / kBlockCols;
+    const int b_beg = (int)((long long)split * NB / S);
+    const int b_end = (int)((long long)(split + 1) * NB / S);
+
+    if (b_beg < b_end) stage_wblock(a, b_beg, sm.u.wst[0]);
+    int tok = 0;
+    size_t lb = 0;
+    uint64_t hh = 0;
+    if (live) {
+        const uint64_t rq = cld64(a.rows + row);
+        const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
+        const FrontEntry* fe = a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi;
+        tok = (int)(uint32_t)(cld64(fe) >> 32);
+        hh = cld64((const char*)fe + 16);
+        lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
+    }
+    // B fragments: U[tok][16 s + 8 h .. +8], zero past r
+    bf16x8 uf[16];
+    {
+        const uint16_t* urow = (const uint16_t*)a.U + (size_t)tok * a.r;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int kk = 16 * s + 8 * h;
+            const uint4 v = *(const uint4*)(urow + (kk < a.r ? kk : 0));
+            uf[s] = __builtin_bit_cast(bf16x8, kk < a.r ? v : make_uint4(0, 0, 0, 0));
+        }
+    }
+    const bool lvec = (a.V & 3) == 0;
+    LGroups<L_BF16> lcur, lnext;
+    if (b_beg < b_end) load_lgroups<L_BF16>(a, lb, b_beg * kBlockCols, h, lvec, lnext);
+    TopK<KT> top;
+    Lse2 st;
+    top.init();
+    st.init();
+    for (int blk = b_beg; blk < b_end; ++blk) {
+        wait_vm();
+        __syncthreads();  // block blk staged by every wavefront; block blk-1 fully consumed
+        lcur = lnext;
+        if (blk + 1 < b_end) {
+            stage_wblock(a, blk + 1, sm.u.wst[(blk + 1 - b_beg) & 1]);
+            load_lgroups<L_BF16>(a, lb, (blk + 1) * kBlockCols, h, lvec, lnext);
+        }
+        const uint4* wb = sm.u.wst[(blk - b_beg) & 1] + p0 * 32;
+        // all 16 A fragments are read before the MFMA chain so that the LDS latency is paid
+        // once per block, not once per step
+        uint4 wf[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) wf[s] = wb[(2 * s + h) ^ p0];
+        f32x16 acc;
+        lgroups_to_acc<L_BF16>(lcur, acc);
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[s]), uf[s],
+                                                          acc, 0, 0, 0);
+        // each row lives in two lanes of one wavefront: no workgroup-shared bound
+        expand_epilogue<KT, SAMPLE>(a, acc, blk * kBlockCols, h, hh, live, nullptr, top, st);
+    }
+    st.merge_xor(32);
+    top.merge_xor(32);
+    if (h == 0 && live) {
+        float v[RS];
+#pragma unroll
+        for (int i = 0; i < RS; ++i) v[i] = 0.0f;
+        put_list<KT>(v, top, st);
+        char* rec = (char*)(a.partials + ((size_t)row * S + split) * RS);
+#pragma unroll
+        for (int q = 0; q < RS / 2; ++q)
+            cst64(rec + 8 * q, (uint64_t)__float_as_uint(v[2 * q]) |
+                                   ((uint64_t)__float_as_uint(v[2 * q + 1]) << 32));
+    }
+    wait_vm();
+    __syncthreads();  // no copy into the staging buffers is left in flight
 }
 
 // ---------------------------------------------------------------------------------------
@@ -778,11 +969,19 @@ __global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
         if (level > a.B) break;
         const int M = (int)cld32(a.sync + kSyncRows + level);
         if (M == 0) break;
-        const int T = (M + kTileRows - 1) / kTileRows;
+        // tile mode (<= kTileRows rows, or float32 heads) or group mode (128-row groups)
+        const bool grp_mode = HEAD_BF16 && M > kTileRows;
+        const int GR = grp_mode ? kGroupRows : kTileRows;
+        const int T = (M + GR - 1) / GR;
         const int S = splits_for(T, G, NB);
         const unsigned nreq = cld32(a.sync + kSyncReqs + level);
         for (int item = blockIdx.x; item < T * S; item += G) {
-            expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
+            if constexpr (HEAD_BF16) {
+                if (grp_mode) expand_group<KT, SAMPLE, L_BF16>(a, level, M, S, item / S, item % S, sm);
+                else expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
+            } else {
+                expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
+            }
             publish_wg();
             if (tid == 0) cadd32(a.tdone + item / S, 1u);
         }
@@ -793,7 +992,7 @@ __global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
             const int m = sm.bcast[1];
             __syncthreads();
             if (m >= M) break;
-            if (!wait_at_least(a.sync, a.tdone + m / kTileRows, (unsigned)S, sm.bcast)) {
+            if (!wait_at_least(a.sync, a.tdone + m / GR, (unsigned)S, sm.bcast)) {
                 failed = true;
                 break;
             }

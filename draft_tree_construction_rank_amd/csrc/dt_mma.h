@@ -158,46 +158,47 @@ __device__ __forceinline__ void load_wfrag(const void* Wt, int V, int r, int c0,
     }
 }
 
+// Accumulates onto acc0 (and acc1 when `two`); the caller initialises them.
 __device__ __forceinline__ void mma_wfrag(const bf16x8 (&wf)[16], bool two, const uint16_t* sA,
                                           f32x16& acc0, f32x16& acc1) {
     const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        acc0[i] = 0.0f;
-        acc1[i] = 0.0f;
-    }
     const uint16_t* b0 = sA + (lane & 31) * kAStride + (lane >> 5) * 8;
     if (two) {
         const uint16_t* b1 = b0 + 32 * kAStride;
+        // B fragments in groups of four: the LDS latency overlaps the MFMAs of the group before
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const uint4 u0 = *(const uint4*)(b0 + s * 16);
-            const uint4 u1 = *(const uint4*)(b1 + s * 16);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u0),
-                                                           acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u1),
-                                                           acc1, 0, 0, 0);
+        for (int g = 0; g < 4; ++g) {
+            uint4 u0[4], u1[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u0[q] = *(const uint4*)(b0 + (4 * g + q) * 16);
+                u1[q] = *(const uint4*)(b1 + (4 * g + q) * 16);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[4 * g + q],
+                                                               __builtin_bit_cast(bf16x8, u0[q]), acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[4 * g + q],
+                                                               __builtin_bit_cast(bf16x8, u1[q]), acc1, 0, 0, 0);
+            }
         }
     } else {
+        uint4 u0[16];
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const uint4 u0 = *(const uint4*)(b0 + s * 16);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u0),
+        for (int s = 0; s < 16; ++s) u0[s] = *(const uint4*)(b0 + s * 16);
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[s], __builtin_bit_cast(bf16x8, u0[s]),
                                                            acc0, 0, 0, 0);
-        }
     }
 }
 
 // float32 heads (r <= 64): the whole transposed block, f32 32x32x2 MFMA.
+// Accumulates onto acc0 (and acc1 when `two`); the caller initialises them.
 __device__ __forceinline__ void xblock_mma_f32(const void* Wt, int V, int r, int c0, bool two,
                                                const float* sAf, f32x16& acc0, f32x16& acc1) {
     const int lane = threadIdx.x & 63;
     const int col = c0 + (lane & 31);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        acc0[i] = 0.0f;
-        acc1[i] = 0.0f;
-    }
     const int kh = lane >> 5;
     const float* wrow = (const float*)Wt + (size_t)(col < V ? col : V - 1) * r;
     const float* b0 = sAf + (lane & 31) * kAfStride + kh;

@@ -57,6 +57,17 @@ Layout make_layout(const dt_params* p) {
         L.vstate = take(R * sizeof(VState));
         L.vpart = take(R * (size_t)L.vsplits * 4 * sizeof(float));
     }
+    {
+        // greedy verify: the root rows are split over about 1024 workgroups, each of at least
+        // 256 sixteen-byte segments of the row
+        const size_t segs = (V + 7) / 8;
+        size_t s = 1024 / R;
+        if (s > 64) s = 64;
+        if (s > segs / 256) s = segs / 256;
+        if (s < 1) s = 1;
+        L.gsplits = (int)s;
+        L.gpart = take(R * s * 8);
+    }
     L.total = off;
     return L;
 }
@@ -201,11 +212,13 @@ dt_status tree_verify_greedy(const dt_params* p, const dt_tree* tree, const void
                              void* stream) {
     const dt_status v = validate(p);
     if (v != DT_OK) return v;
-    if (!tree_ptrs_ok(tree) || !target_logits || !verify_ptrs_ok(out)) return DT_EINVAL;
-    if ((uintptr_t)target_logits & 15) return DT_EINVAL;
-    (void)workspace;
-    (void)ws_bytes;
-    if (launch_verify_greedy(p, tree, target_logits, out, (hipStream_t)stream) != hipSuccess)
+    if (!tree_ptrs_ok(tree) || !target_logits || !verify_ptrs_ok(out) || !workspace)
+        return DT_EINVAL;
+    if (((uintptr_t)target_logits & 15) || ((uintptr_t)workspace & 255)) return DT_EINVAL;
+    const Layout lay = make_layout(p);
+    if (ws_bytes < lay.total) return DT_ENOSPC;
+    if (launch_verify_greedy(p, lay, (char*)workspace, tree, target_logits, out,
+                             (hipStream_t)stream) != hipSuccess)
         return DT_EDEVICE;
     return DT_OK;
 }

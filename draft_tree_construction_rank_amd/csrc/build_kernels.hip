@@ -296,8 +296,14 @@ __device__ __forceinline__ void expand_epilogue(const BuildArgs& a, f32x16& z, i
         for (int e = 0; e < 16; ++e) ps += __builtin_amdgcn_exp2f(z[e] * a.y2scale - st.m);
         st.s += ps;
     }
-    if (!live) return;
+    // lanes l and l ^ 32 hold the same row: each takes the better of the two KT-th entries
     uint64_t kth = top.k[KT - 1];
+    {
+        const uint32_t lo = __shfl_xor((uint32_t)kth, 32), hi = __shfl_xor((uint32_t)(kth >> 32), 32);
+        const uint64_t pk = ((uint64_t)hi << 32) | lo;
+        kth = pk > kth ? pk : kth;
+    }
+    if (!live) return;
     if (row_kth) kth = kth > *row_kth ? kth : *row_kth;
     const float tk = kth ? entry_key(kth) : -INFINITY;
     // Candidates are values z with z >= thr, a superset of those that can enter the list
@@ -952,12 +958,15 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a, int tiles
     }
 }
 
-// The level loop (cooperative launch: all workgroups are resident).
+// The level loop.  The grid is the kernel's resident capacity, launched plainly: workgroups
+// wait for each other's expansion items, so the loop relies on all of them being dispatched
+// eventually (they are, once any other work sharing the GPU drains; on an idle GPU all are
+// resident at once).  Every wait is bounded, so a grid that cannot be completed ends with
+// DT_REQ_SYNC_TIMEOUT instead of hanging.
 template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
 __global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
     __shared__ __attribute__((aligned(16))) BuildSmem<KT> sm;
     const int tid = threadIdx.x;
-    const int G = gridDim.x;
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     bool failed = false;
     for (int level = 1;; ++level) {
@@ -973,9 +982,12 @@ __global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
         const bool grp_mode = HEAD_BF16 && M > kTileRows;
         const int GR = grp_mode ? kGroupRows : kTileRows;
         const int T = (M + GR - 1) / GR;
-        const int S = splits_for(T, G, NB);
+        const int S = splits_for(T, (int)gridDim.x, NB);
         const unsigned nreq = cld32(a.sync + kSyncReqs + level);
-        for (int item = blockIdx.x; item < T * S; item += G) {
+        // item i runs on workgroup i mod G.  Workgroups are dealt to the 8 XCDs round-robin,
+        // so when S and G are multiples of 8 split j of every row tile runs on one XCD, and a
+        // W block read for one tile is an L2 hit for the others.
+        for (int item = blockIdx.x; item < T * S; item += gridDim.x) {
             if constexpr (HEAD_BF16) {
                 if (grp_mode) expand_group<KT, SAMPLE, L_BF16>(a, level, M, S, item / S, item % S, sm);
                 else expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
@@ -1019,7 +1031,7 @@ __global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
         if (failed) break;
     }
     if (failed) cst32(a.sync + kSyncErr, 1u);
-    for (int req = blockIdx.x; req < a.R; req += G)
+    for (int req = blockIdx.x; req < a.R; req += gridDim.x)
         emit_request(a, req, failed || cld32(a.sync + kSyncErr) != 0u, sm.u.em);
     if (blockIdx.x == 0 && a.out.level_rows)
         for (int l = tid; l < a.B; l += blockDim.x)
@@ -1061,11 +1073,10 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     if (G < 1) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(k_build_init, dim3(1), dim3(256), 0, st, a, max_tiles(a.R, a.Ncap));
     if (a.timing_hook) a.timing_hook(st, 0);
-    BuildArgs args = a;
-    void* kargs[] = {&args};
-    const hipError_t e = hipLaunchCooperativeKernel(f, dim3(G), dim3(256), kargs, 0, st);
+    // a plain launch: the loop needs no co-residency guarantee (see k_build), and a
+    // cooperative launch costs about 18 us more per round on this stack
+    hipLaunchKernelGGL((k_build<KT, SAMPLE, HEAD_BF16, L_BF16>), dim3(G), dim3(256), 0, st, a);
     if (a.timing_hook) a.timing_hook(st, 1);
-    if (e != hipSuccess) return e;
     return hipGetLastError();
 }
 

@@ -57,11 +57,13 @@ struct Layout {
     size_t vprow;     // float [R][V]: sample verify, target probabilities p of the node
     size_t vstate;    // VState [R]
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
+    size_t gpart;     // (float, int) [R][gsplits]: greedy verify, split argmax of the root rows
     size_t total;
     int G;            // largest grid of the construction kernel (sizes the partial records)
     int NC;           // vocabulary chunks of 128 columns
     int KT;           // top-k list length used by the kernels (1, 2, 4 or 8)
     int vsplits;      // vocabulary splits per request in sample verify
+    int gsplits;      // vocabulary splits per request of the root-row argmax in greedy verify
 };
 
 Layout make_layout(const dt_params* p);
@@ -124,7 +126,8 @@ hipError_t launch_build(const dt_params* p, const Layout& lay, const BuildArgs& 
                         hipStream_t st);
 // Tiles of kTileRows parent rows needed for R * Ncap rows.
 inline int max_tiles(int R, int Ncap) { return (R * Ncap + kTileRows - 1) / kTileRows; }
-hipError_t launch_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target,
+hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
+                                const dt_tree* tree, const void* target,
                                 const dt_verify_out* out, hipStream_t st);
 hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
                                 const dt_tree* tree, const void* L, const void* U,

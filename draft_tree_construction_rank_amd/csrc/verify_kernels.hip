@@ -20,6 +20,15 @@ __device__ __forceinline__ ArgMax amax(ArgMax a, ArgMax b) {
     return (b.v > a.v || (b.v == a.v && b.i < a.i)) ? b : a;
 }
 
+// Within one thread indices arrive in increasing order, so a strict comparison keeps the
+// lowest index among equal values.
+__device__ __forceinline__ void amax_seq(ArgMax& a, float v, int i) {
+    if (v > a.v) {
+        a.v = v;
+        a.i = i;
+    }
+}
+
 __device__ __forceinline__ ArgMax wave_amax(ArgMax a) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -31,44 +40,11 @@ __device__ __forceinline__ ArgMax wave_amax(ArgMax a) {
     return a;
 }
 
-// Argmax of one row (ties: lower index) over the whole workgroup; every thread gets it.
-template <bool BF16>
-__device__ ArgMax row_argmax(const void* row, int V, bool vec, ArgMax* sh) {
-    ArgMax best{-INFINITY, 0x7fffffff};
-    const int tid = threadIdx.x, nt = blockDim.x;
-    if (BF16) {
-        const uint16_t* p = (const uint16_t*)row;
-        if (vec) {
-            const int nv = V >> 3;
-            for (int i = tid; i < nv; i += nt) {
-                const uint4 w = ((const uint4*)p)[i];
-                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    best = amax(best, ArgMax{bf16_lo(ws[e]), i * 8 + 2 * e});
-                    best = amax(best, ArgMax{bf16_hi(ws[e]), i * 8 + 2 * e + 1});
-                }
-            }
-        } else {
-            for (int i = tid; i < V; i += nt) best = amax(best, ArgMax{bf16_to_f32(p[i]), i});
-        }
-    } else {
-        const float* p = (const float*)row;
-        if (vec) {
-            const int nv = V >> 2;
-            for (int i = tid; i < nv; i += nt) {
-                const float4 w = ((const float4*)p)[i];
-                best = amax(best, ArgMax{w.x, i * 4});
-                best = amax(best, ArgMax{w.y, i * 4 + 1});
-                best = amax(best, ArgMax{w.z, i * 4 + 2});
-                best = amax(best, ArgMax{w.w, i * 4 + 3});
-            }
-        } else {
-            for (int i = tid; i < V; i += nt) best = amax(best, ArgMax{p[i], i});
-        }
-    }
+// Workgroup reduction of per-thread candidates; every thread gets the result.
+__device__ ArgMax block_amax(ArgMax best, ArgMax* sh) {
+    const int tid = threadIdx.x;
     best = wave_amax(best);
-    const int wv = tid >> 6, nw = nt >> 6;
+    const int wv = tid >> 6, nw = blockDim.x >> 6;
     if ((tid & 63) == 0) sh[wv] = best;
     __syncthreads();
     if (tid < 64) {
@@ -82,8 +58,92 @@ __device__ ArgMax row_argmax(const void* row, int V, bool vec, ArgMax* sh) {
     return r;
 }
 
+// Argmax (ties: lower index) of units [lo, hi) of one row over the whole workgroup; a unit
+// is a 16-byte segment when `vec` (V a multiple of 8 bf16 / 4 float values), else one value.
+// Each thread keeps kBatch independent loads in flight before it uses any of them.
+template <bool BF16, int kBatch>
+__device__ ArgMax range_argmax(const void* row, int lo, int hi, bool vec, ArgMax* sh) {
+    ArgMax best{-INFINITY, 0x7fffffff};
+    const int tid = threadIdx.x, nt = blockDim.x;
+    if (BF16) {
+        const uint16_t* p = (const uint16_t*)row;
+        if (vec) {
+            for (int i0 = lo + tid; i0 < hi; i0 += nt * kBatch) {
+                uint4 w[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int i = i0 + u * nt;
+                    w[u] = i < hi ? ((const uint4*)p)[i] : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int i = i0 + u * nt;
+                    if (i < hi) {
+                        const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            amax_seq(best, bf16_lo(ws[e]), i * 8 + 2 * e);
+                            amax_seq(best, bf16_hi(ws[e]), i * 8 + 2 * e + 1);
+                        }
+                    }
+                }
+            }
+        } else {
+            for (int i = lo + tid; i < hi; i += nt) amax_seq(best, bf16_to_f32(p[i]), i);
+        }
+    } else {
+        const float* p = (const float*)row;
+        if (vec) {
+            for (int i0 = lo + tid; i0 < hi; i0 += nt * kBatch) {
+                float4 w[kBatch];
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int i = i0 + u * nt;
+                    w[u] = i < hi ? ((const float4*)p)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < kBatch; ++u) {
+                    const int i = i0 + u * nt;
+                    if (i < hi) {
+                        amax_seq(best, w[u].x, i * 4);
+                        amax_seq(best, w[u].y, i * 4 + 1);
+                        amax_seq(best, w[u].z, i * 4 + 2);
+                        amax_seq(best, w[u].w, i * 4 + 3);
+                    }
+                }
+            }
+        } else {
+            for (int i = lo + tid; i < hi; i += nt) amax_seq(best, p[i], i);
+        }
+    }
+    return block_amax(best, sh);
+}
+
 template <bool BF16>
-__global__ __launch_bounds__(1024) void k_verify_greedy(int B, int V, int Ncap, const void* target,
+__device__ __forceinline__ int row_units(int V, bool vec) {
+    return vec ? (BF16 ? V >> 3 : V >> 2) : V;
+}
+
+// Root rows, split: workgroup (request, j) writes the argmax of the j-th of S equal parts of
+// the request's row 0 to part[request][j].
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_verify_root(int V, int Ncap, int S, const void* target,
+                                                     ArgMax* part) {
+    __shared__ ArgMax sh[4];
+    const int req = blockIdx.x / S, j = blockIdx.x % S;
+    const bool vec = BF16 ? (V & 7) == 0 : (V & 3) == 0;
+    const int n = row_units<BF16>(V, vec);
+    const int lo = (int)((long long)j * n / S), hi = (int)((long long)(j + 1) * n / S);
+    const char* rp = (const char*)target + (size_t)req * (Ncap + 1) * (size_t)V * (BF16 ? 2 : 4);
+    const ArgMax am = range_argmax<BF16, 8>(rp, lo, hi, vec, sh);
+    if (threadIdx.x == 0) part[(size_t)req * S + j] = am;
+}
+
+// The walk: one workgroup per request.  Row 0's argmax comes from the S partials of
+// k_verify_root; every later row is reduced here.
+template <bool BF16>
+__global__ __launch_bounds__(1024) void k_verify_greedy(int B, int V, int Ncap, int S,
+                                                        const void* target, const ArgMax* part,
                                                         dt_tree tree, dt_verify_out out) {
     __shared__ ArgMax sh[16];
     __shared__ int s_tok[kMaxNcap], s_par[kMaxNcap];
@@ -109,8 +169,16 @@ __global__ __launch_bounds__(1024) void k_verify_greedy(int B, int V, int Ncap, 
     const size_t esz = BF16 ? 2 : 4;
     int v = -1, row = 0, nacc = 0;
     for (;;) {
-        const char* rp = (const char*)target + ((size_t)req * (Ncap + 1) + row) * (size_t)V * esz;
-        const ArgMax am = row_argmax<BF16>(rp, V, vec, sh);
+        ArgMax am;
+        if (row == 0) {
+            // S <= 64 partials, in index order of their vocabulary parts
+            ArgMax c{-INFINITY, 0x7fffffff};
+            if (tid < S) c = part[(size_t)req * S + tid];
+            am = block_amax(c, sh);
+        } else {
+            const char* rp = (const char*)target + ((size_t)req * (Ncap + 1) + row) * (size_t)V * esz;
+            am = range_argmax<BF16, 20>(rp, 0, row_units<BF16>(V, vec), vec, sh);
+        }
         if (tid == 0) s_child = -1;
         __syncthreads();
         if (tid < n && s_par[tid] == v && s_tok[tid] == am.i) s_child = tid;
@@ -130,14 +198,22 @@ __global__ __launch_bounds__(1024) void k_verify_greedy(int B, int V, int Ncap, 
     }
 }
 
-hipError_t launch_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target,
+hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
+                                const dt_tree* tree, const void* target,
                                 const dt_verify_out* out, hipStream_t st) {
-    if (p->logits_dtype == DT_BF16)
+    ArgMax* part = (ArgMax*)(ws + lay.gpart);
+    const int S = lay.gsplits;
+    if (p->logits_dtype == DT_BF16) {
+        hipLaunchKernelGGL(k_verify_root<true>, dim3(p->R * S), dim3(256), 0, st, p->V, p->Ncap,
+                           S, target, part);
         hipLaunchKernelGGL(k_verify_greedy<true>, dim3(p->R), dim3(1024), 0, st, p->B, p->V,
-                           p->Ncap, target, *tree, *out);
-    else
+                           p->Ncap, S, target, (const ArgMax*)part, *tree, *out);
+    } else {
+        hipLaunchKernelGGL(k_verify_root<false>, dim3(p->R * S), dim3(256), 0, st, p->V, p->Ncap,
+                           S, target, part);
         hipLaunchKernelGGL(k_verify_greedy<false>, dim3(p->R), dim3(1024), 0, st, p->B, p->V,
-                           p->Ncap, target, *tree, *out);
+                           p->Ncap, S, target, (const ArgMax*)part, *tree, *out);
+    }
     return hipGetLastError();
 }
 

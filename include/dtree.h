@@ -19,6 +19,10 @@
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work; outputs
  *    are valid once the stream has been synchronised.  Calls on different streams with
  *    different workspaces are independent.
+ *  - `workspace` is caller-owned device memory of at least dt_build_workspace_bytes() bytes,
+ *    256-byte aligned (DT_EINVAL if misaligned or NULL, DT_ENOSPC if smaller); its contents
+ *    on entry do not matter and on return are unspecified.  A verify call may use another
+ *    workspace than the tree_build call that made its tree.
  *  - Host-side argument errors return synchronously before anything is enqueued.
  *    Device-side data errors are reported per request in `status` and never abort.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
@@ -134,7 +138,9 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
  *  tree          the dt_tree written by tree_build (device arrays; read only)
  *  target_logits [R][Ncap+1][V] (logits_dtype): row 0 = the root, row i+1 = node i
  * From the root: t* = argmax of the current row (ties: lower id); if a child of the current
- * node carries t*, accept it and continue from it; otherwise t* is the final (bonus) token. */
+ * node carries t*, accept it and continue from it; otherwise t* is the final (bonus) token.
+ * The root rows' argmax is split over many workgroups (partials in `workspace`); the walk
+ * below the root runs one workgroup per request. */
 dt_status tree_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target_logits,
                              const dt_verify_out* out, void* workspace, size_t ws_bytes,
                              void* stream);

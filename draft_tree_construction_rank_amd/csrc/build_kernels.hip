@@ -265,6 +265,32 @@ __device__ __forceinline__ void lgroups_to_acc(const LGroups<L_BF16>& lw, f32x16
     }
 }
 
+// Per-lane select through an all-ones / all-zero bit mask.  The mask passes an empty asm
+// statement so that the compiler cannot see it is a boolean: written as plain selects, a
+// tree keyed on the bits of a per-lane index is folded back into a dynamic vector index,
+// which is lowered through a private (scratch) copy of the vector.
+__device__ __forceinline__ uint32_t lane_bit_mask(int e, int bit) {
+    uint32_t m = 0u - (((uint32_t)e >> bit) & 1u);
+    asm volatile("" : "+v"(m));
+    return m;
+}
+__device__ __forceinline__ float sel_bits(uint32_t m, float if_clear, float if_set) {
+    return __uint_as_float((__float_as_uint(if_set) & m) | (__float_as_uint(if_clear) & ~m));
+}
+
+// z[e] for a per-lane index e (0..15): a 4-level select tree in registers.
+__device__ __forceinline__ float select16(const f32x16& z, int e) {
+    const uint32_t m0 = lane_bit_mask(e, 0), m1 = lane_bit_mask(e, 1), m2 = lane_bit_mask(e, 2),
+                   m3 = lane_bit_mask(e, 3);
+    float v8[8], v4[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v8[i] = sel_bits(m0, z[2 * i], z[2 * i + 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v4[i] = sel_bits(m1, v8[2 * i], v8[2 * i + 1]);
+    const float v0 = sel_bits(m2, v4[0], v4[1]), v1 = sel_bits(m2, v4[2], v4[3]);
+    return sel_bits(m3, v0, v1);
+}
+
 // Epilogue of one 32-column block for one parent row: z holds the row's 16 values of this
 // lane (columns c0 + 8(e/4) + 4h + e%4).  Updates the online log-sum-exp, then offers the
 // values that can still rank among the KT best to the ranked list.  Any lane's KT-th list
@@ -296,12 +322,17 @@ __device__ __forceinline__ void expand_epilogue(const BuildArgs& a, f32x16& z, i
         for (int e = 0; e < 16; ++e) ps += __builtin_amdgcn_exp2f(z[e] * a.y2scale - st.m);
         st.s += ps;
     }
-    // lanes l and l ^ 32 hold the same row: each takes the better of the two KT-th entries
+    // lanes l and l ^ 32 hold the same row: each takes the better of the two KT-th entries.
+    // A swap of the wavefront's halves leaves the entries of lanes l % 32 and l % 32 + 32 in
+    // the two results (a VALU exchange, no LDS round trip).
     uint64_t kth = top.k[KT - 1];
     {
-        const uint32_t lo = __shfl_xor((uint32_t)kth, 32), hi = __shfl_xor((uint32_t)(kth >> 32), 32);
-        const uint64_t pk = ((uint64_t)hi << 32) | lo;
-        kth = pk > kth ? pk : kth;
+        const uint32_t lo = (uint32_t)kth, hi = (uint32_t)(kth >> 32);
+        const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        const uint64_t e0 = ((uint64_t)sh[0] << 32) | sl[0], e1 = ((uint64_t)sh[1] << 32) | sl[1];
+        kth = e0 > kth ? e0 : kth;
+        kth = e1 > kth ? e1 : kth;
     }
     if (!live) return;
     if (row_kth) kth = kth > *row_kth ? kth : *row_kth;
@@ -317,33 +348,48 @@ __device__ __forceinline__ void expand_epilogue(const BuildArgs& a, f32x16& z, i
         if (top.k[KT - 1] == 0) thr = fmaxf(thr, kth_largest16<KT>(*(const float(*)[16]) & z));
     }
     thr = fmaxf(thr, -3.402823466e38f);
+    // Candidates are offered one at a time per lane, lowest index first: the wavefront loops
+    // while any of its lanes has one left, which is one or two rounds once the lists are
+    // warm (instead of 16 predicated insertions whenever any lane has a candidate).
+    // Insertion order does not change the list (push keeps the KT largest entries).
     if constexpr (SAMPLE) {
+        uint32_t gm = 0;  // 4-column groups with a candidate
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const bool any = z[4 * j] >= thr || z[4 * j + 1] >= thr || z[4 * j + 2] >= thr ||
                              z[4 * j + 3] >= thr;
-            if (any) {
-                const int cg = c0 + 8 * j + 4 * h;
-                const uint4 w = rand4((uint32_t)(cg >> 2), STREAM_GUMBEL, hh, a.seed_lo, a.seed_hi);
-                const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+            gm |= any ? (1u << j) : 0u;
+        }
+        if (gm == 0u) return;
+        while (gm != 0u) {
+            const int j = __builtin_ctz(gm);
+            gm &= gm - 1u;
+            float zg[4];
+            {
+                const uint32_t m0 = lane_bit_mask(j, 0), m1 = lane_bit_mask(j, 1);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (z[4 * j + i] >= thr) {
-                        const float zi = z[4 * j + i];
-                        top.push(pack_entry(zi * a.invT + gumbel(wv[i]), cg + i), zi * a.y2scale);
-                        if (top.k[KT - 1])
-                            thr = fmaxf(thr, (entry_key(top.k[KT - 1]) - kGumbelMax) / a.invT);
-                    }
-                }
+                for (int i = 0; i < 4; ++i)
+                    zg[i] = sel_bits(m1, sel_bits(m0, z[i], z[4 + i]), sel_bits(m0, z[8 + i], z[12 + i]));
+            }
+            const int cg = c0 + 8 * j + 4 * h;
+            const uint4 w = rand4((uint32_t)(cg >> 2), STREAM_GUMBEL, hh, a.seed_lo, a.seed_hi);
+            const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (zg[i] >= thr)
+                    top.push(pack_entry(zg[i] * a.invT + gumbel(wv[i]), cg + i), zg[i] * a.y2scale);
             }
         }
     } else {
+        uint32_t mask = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if (z[e] >= thr) {
-                top.push(pack_entry(z[e], c0 + 8 * (e >> 2) + 4 * h + (e & 3)), z[e] * a.y2scale);
-                if (top.k[KT - 1]) thr = fmaxf(thr, entry_key(top.k[KT - 1]));
-            }
+        for (int e = 0; e < 16; ++e) mask |= (z[e] >= thr) ? (1u << e) : 0u;
+        if (mask == 0u) return;
+        while (mask != 0u) {
+            const int e = __builtin_ctz(mask);
+            mask &= mask - 1u;
+            const float v = select16(z, e);
+            top.push(pack_entry(v, c0 + 8 * (e >> 2) + 4 * h + (e & 3)), v * a.y2scale);
         }
     }
     if (row_kth && top.k[KT - 1] != 0)
@@ -585,17 +631,18 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
     for (int blk = b_beg; blk < b_end; ++blk) {
         wait_vm();
         __syncthreads();  // block blk staged by every wavefront; block blk-1 fully consumed
+        // All 16 A fragments are read from LDS before the next block's copy is issued: a read
+        // of LDS placed after a global->LDS copy waits for every global load in flight, which
+        // would expose the whole latency of the prefetch on every block.
+        const uint4* wb = sm.u.wst[(blk - b_beg) & 1] + p0 * 32;
+        uint4 wf[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) wf[s] = wb[(2 * s + h) ^ p0];
         lcur = lnext;
         if (blk + 1 < b_end) {
             stage_wblock(a, blk + 1, sm.u.wst[(blk + 1 - b_beg) & 1]);
             load_lgroups<L_BF16>(a, lb, (blk + 1) * kBlockCols, h, lvec, lnext);
         }
-        const uint4* wb = sm.u.wst[(blk - b_beg) & 1] + p0 * 32;
-        // all 16 A fragments are read before the MFMA chain so that the LDS latency is paid
-        // once per block, not once per step
-        uint4 wf[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) wf[s] = wb[(2 * s + h) ^ p0];
         f32x16 acc;
         lgroups_to_acc<L_BF16>(lcur, acc);
 #pragma unroll

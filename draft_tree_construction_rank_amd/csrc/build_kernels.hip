@@ -446,6 +446,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
             const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
             const FrontEntry* fe = a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi;
             tok = (int)(uint32_t)(cld64(fe) >> 32);
+            tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
             hh = cld64((const char*)fe + 16);
             lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
         }
@@ -607,6 +608,7 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
         const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
         const FrontEntry* fe = a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi;
         tok = (int)(uint32_t)(cld64(fe) >> 32);
+        tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
         hh = cld64((const char*)fe + 16);
         lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
     }
@@ -748,8 +750,10 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
                 c.pad = 0;
                 c.hash = child_hash(par.hash, c.token);
                 st_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j, c);
+                // a list shorter than k (possible only with non-finite logits) leaves the
+                // missing children token -1 and key 0: never selected
                 cst64(a.ckeys + (size_t)req * a.Ncap * a.k + fi * a.k + j,
-                      make_key(c.s, level, fi, j));
+                      top.k[j] != 0 ? make_key(c.s, level, fi, j) : 0);
             }
         }
     }

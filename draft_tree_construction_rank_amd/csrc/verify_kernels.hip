@@ -296,7 +296,8 @@ __global__ __launch_bounds__(256) void k_vs_rows(const VsArgs a) {
     __syncthreads();
     if (!sAny) return;
     load_a_tile<HEAD_BF16>(a.U, a.r, nrows, [&](int row) {
-        return sLive[row] ? a.state[m0 + row].token : 0;
+        const int t = sLive[row] ? a.state[m0 + row].token : 0;
+        return (uint32_t)t < (uint32_t)a.V ? t : 0;  // never index U out of range
     }, sA, sAf);
     __syncthreads();
 

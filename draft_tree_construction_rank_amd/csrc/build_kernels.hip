@@ -34,20 +34,27 @@ namespace dt {
 // ---------------------------------------------------------------------------------------
 // Workgroup helpers (256 threads).
 // ---------------------------------------------------------------------------------------
+// Exclusive prefix sum over the workgroup: a shuffle scan inside each wavefront, then the
+// wavefront totals through LDS (two barriers).  sh needs one int per wavefront.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-    const int t = threadIdx.x, n = blockDim.x;
-    sh[t] = v;
-    __syncthreads();
-    for (int off = 1; off < n; off <<= 1) {
-        const int add = (t >= off) ? sh[t - off] : 0;
-        __syncthreads();
-        sh[t] += add;
-        __syncthreads();
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    const int incl = sh[t];
-    if (total) *total = sh[n - 1];
+    if (lane == 63) sh[w] = x;
     __syncthreads();
-    return incl - v;
+    int base = 0, tot = 0;
+    for (int i = 0; i < nw; ++i) {
+        const int si = sh[i];
+        base += i < w ? si : 0;
+        tot += si;
+    }
+    if (total) *total = tot;
+    __syncthreads();  // sh is free for the caller again
+    return base + x - v;
 }
 
 __device__ __forceinline__ int block_sum(int v, int* sh) {
@@ -436,6 +443,12 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     const int b_beg = (int)((long long)split * NB / S);
     const int b_end = (int)((long long)(split + 1) * NB / S);
+    // The first W block of this wavefront does not depend on the parent rows: its loads are
+    // in flight during the row set-up below.
+    bf16x8 wf[16];
+    if constexpr (HEAD_BF16) {
+        if (b_beg + wave < b_end) load_wfrag(a.Wt, a.V, a.r, (b_beg + wave) * kBlockCols, wf);
+    }
 
     if (tid < kTileRows) {
         int tok = 0;
@@ -478,10 +491,8 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         // Software pipeline: the W fragments and block logits of block b + 4 are in flight
         // while block b's epilogue runs.
         int blk = b_beg + wave;
-        bf16x8 wf[16];
         LGroups<L_BF16> n0, n1;
         if (blk < b_end) {
-            load_wfrag(a.Wt, a.V, a.r, blk * kBlockCols, wf);
             load_lgroups<L_BF16>(a, lb0, blk * kBlockCols, h, lvec, n0);
             if (two) load_lgroups<L_BF16>(a, lb1, blk * kBlockCols, h, lvec, n1);
         }

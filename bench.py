@@ -207,7 +207,7 @@ def main():
     ms = res["ms_per_step"]
     value = inst.R / (ms * 1e-3)
     # roofline of the dominant kernel: the persistent construction kernel k_build (one
-    # cooperative launch per round), timed with HIP events on the launch stream
+    # launch per round), timed with HIP events on the launch stream
     launches_per_step = res["expand_launches"] / args.steps
     avg_us = res["expand_ms"] * 1e3 / max(1, res["expand_launches"])
     round_bytes = algorithmic_bytes(inst, res["levels_used"], res["n_expand"])

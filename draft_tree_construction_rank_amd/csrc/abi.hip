@@ -27,8 +27,8 @@ Layout make_layout(const dt_params* p) {
     L.G = kMaxGrid;
     const size_t tmax = (R * N + kTileRows - 1) / kTileRows;
     // records: (parent row, vocabulary split) pairs; a level of T row groups of g rows uses
-    // at most g * max(G, T) of them (g = 64 in tile mode, 128 in group mode)
-    const size_t cap_rows = (size_t)128 * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
+    // at most g * max(G, T) of them (g = kTileRows in tile mode, kGroupRows in group mode)
+    const size_t cap_rows = (size_t)kGroupRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
     L.sync = take(kSyncWords * sizeof(unsigned));
     L.tdone = take((size_t)max_tiles((int)R, (int)N) * sizeof(unsigned));
     L.rdone = take(R * sizeof(unsigned));

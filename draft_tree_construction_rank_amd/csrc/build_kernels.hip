@@ -31,8 +31,12 @@
 
 namespace dt {
 
+// The persistent construction kernel runs one workgroup of kWaves wavefronts per CU.
+constexpr int kWaves = kBuildWaves;
+constexpr int kThreads = 64 * kWaves;
+
 // ---------------------------------------------------------------------------------------
-// Workgroup helpers (256 threads).
+// Workgroup helpers.
 // ---------------------------------------------------------------------------------------
 // Exclusive prefix sum over the workgroup: a shuffle scan inside each wavefront, then the
 // wavefront totals through LDS (two barriers).  sh needs one int per wavefront.
@@ -130,8 +134,8 @@ struct BuildSmem {
         uint64_t keys[kSelectSlots];        // select
         EmitSmem em;                        // emit
     } u;
-    float xrec[4][kTileRows][rec_floats(KT)];  // per-wavefront lists of an expansion item
-    float mrec[4][rec_floats(KT)];             // per-wavefront lists of a merged row
+    float xrec[kWaves][kTileRows][rec_floats(KT)];  // per-wavefront lists of an expansion item
+    float mrec[kWaves][rec_floats(KT)];             // per-wavefront lists of a merged row
     size_t lbase[kTileRows];
     uint64_t hash[kTileRows];
     uint64_t rkth[128];  // per parent row of an item: the largest KT-th list entry seen so far
@@ -430,7 +434,7 @@ __device__ __forceinline__ void get_list(const float* v, TopK<KT>& t, Lse2& s) {
 }
 
 // One item: tile `tile` of the level's parent rows x vocabulary split `split`.  Wavefront w
-// takes the split's 32-column blocks w, w+4, ...; the four wavefronts' lists are combined in
+// takes the split's 32-column blocks w, w+kWaves, ...; the wavefronts' lists are combined in
 // LDS and one record per parent row is published.
 template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
 __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M, int S, int tile,
@@ -470,9 +474,9 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
     }
     __syncthreads();
     if constexpr (HEAD_BF16)
-        load_a_tile<true>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, sm.u.sA, nullptr);
+        load_a_tile<true, kThreads>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, sm.u.sA, nullptr);
     else
-        load_a_tile<false>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, nullptr, sm.u.sAf);
+        load_a_tile<false, kThreads>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, nullptr, sm.u.sAf);
     __syncthreads();
 
     const bool two = nrows > 32;
@@ -496,22 +500,22 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
             load_lgroups<L_BF16>(a, lb0, blk * kBlockCols, h, lvec, n0);
             if (two) load_lgroups<L_BF16>(a, lb1, blk * kBlockCols, h, lvec, n1);
         }
-        for (; blk < b_end; blk += 4) {
+        for (; blk < b_end; blk += kWaves) {
             const int c0 = blk * kBlockCols;
             f32x16 acc0, acc1;
             lgroups_to_acc<L_BF16>(n0, acc0);
             if (two) lgroups_to_acc<L_BF16>(n1, acc1);
             mma_wfrag(wf, two, sm.u.sA, acc0, acc1);
-            if (blk + 4 < b_end) {
-                load_wfrag(a.Wt, a.V, a.r, c0 + 4 * kBlockCols, wf);
-                load_lgroups<L_BF16>(a, lb0, c0 + 4 * kBlockCols, h, lvec, n0);
-                if (two) load_lgroups<L_BF16>(a, lb1, c0 + 4 * kBlockCols, h, lvec, n1);
+            if (blk + kWaves < b_end) {
+                load_wfrag(a.Wt, a.V, a.r, c0 + kWaves * kBlockCols, wf);
+                load_lgroups<L_BF16>(a, lb0, c0 + kWaves * kBlockCols, h, lvec, n0);
+                if (two) load_lgroups<L_BF16>(a, lb1, c0 + kWaves * kBlockCols, h, lvec, n1);
             }
             expand_epilogue<KT, SAMPLE>(a, acc0, c0, h, hh0, live0, sm.rkth + p0, t0, s0);
             if (two) expand_epilogue<KT, SAMPLE>(a, acc1, c0, h, hh1, live1, sm.rkth + 32 + p0, t1, s1);
         }
     } else {
-        for (int blk = b_beg + wave; blk < b_end; blk += 4) {
+        for (int blk = b_beg + wave; blk < b_end; blk += kWaves) {
             const int c0 = blk * kBlockCols;
             LGroups<L_BF16> l0, l1;
             load_lgroups<L_BF16>(a, lb0, c0, h, lvec, l0);
@@ -537,14 +541,16 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
     }
     __syncthreads();
     {
-        const int row = tid >> 2, w = tid & 3;
+        // kWaves consecutive threads per parent row combine the wavefronts' lists
+        const int row = tid / kWaves, w = tid % kWaves;
         TopK<KT> t;
         Lse2 s;
         get_list<KT>(sm.xrec[w][row], t, s);
-        s.merge_xor(1);
-        s.merge_xor(2);
-        t.merge_xor(1);
-        t.merge_xor(2);
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            s.merge_xor(off);
+            t.merge_xor(off);
+        }
         if (w == 0 && row < nrows) {
             float v[RS];
 #pragma unroll
@@ -562,23 +568,24 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
 
 // ---------------------------------------------------------------------------------------
 // Group-mode expansion (levels with more than kTileRows parent rows, bf16 heads): an item is
-// a group of kGroupRows = 128 parent rows x a vocabulary split.  Wavefront w owns rows
+// a group of kGroupRows = 256 parent rows x a vocabulary split.  Wavefront w owns rows
 // 32w .. 32w+31 of the group and keeps their U rows as MFMA B fragments in registers for the
 // whole item; each 32-column block of W (32 rows of Wt, 16 KB at r = 256) is copied once per
 // workgroup into LDS with coalesced global->LDS loads, double-buffered so that block b+1
-// arrives while block b is multiplied, and read by all four wavefronts.  W is thus read once
-// per 128 parent rows.  The LDS copy stores row j's 16-byte chunk c at slot
-// 32j + (c ^ (j & 31)), so the fragment reads of 16 consecutive lanes hit distinct banks.
+// arrives while block b is multiplied, and read by all eight wavefronts.  W is thus read
+// once per 256 parent rows (once per level up to 256 rows).  The LDS copy stores row j's
+// 16-byte chunk c at slot 32j + (c ^ (j & 31)), so the fragment reads of 16 consecutive
+// lanes hit distinct banks.
 // ---------------------------------------------------------------------------------------
-constexpr int kGroupRows = 128;
 
-// Issue this wavefront's quarter of the global->LDS copy of block `blk` (4 loads of 1 KB).
+// Issue this wavefront's share of the global->LDS copy of block `blk` (16 / kWaves loads of
+// 1 KB).
 __device__ __forceinline__ void stage_wblock(const BuildArgs& a, int blk, uint4* dst) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int chunks = a.r >> 3;  // 16-byte chunks per row of Wt
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int j = 4 * wave + q;            // 1 KB piece j = LDS slots 64j .. 64j+63
+    for (int q = 0; q < 16 / kWaves; ++q) {
+        const int j = (16 / kWaves) * wave + q;  // 1 KB piece j = LDS slots 64j .. 64j+63
         const int row = 2 * j + (lane >> 5);   // W row within the block
         int c = (lane & 31) ^ (row & 31);      // chunk that belongs in this slot
         c = c < chunks ? c : 0;                // past r: any finite data (U is zero there)
@@ -720,13 +727,12 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
     Lse2 acc;
     acc.init();
     const float* base = a.partials + (size_t)m * S * RS;
-    const int s0 = tid < S ? tid : S - 1, s1 = tid + 256 < S ? tid + 256 : S - 1;
-    uint64_t w0[RS / 2], w1[RS / 2];
+    static_assert(kThreads >= kMaxSplits, "one split record per thread");
+    const int s0 = tid < S ? tid : S - 1;
+    uint64_t w0[RS / 2];
     fetch_record<KT>(base + (size_t)s0 * RS, w0);
-    fetch_record<KT>(base + (size_t)s1 * RS, w1);
     const uint64_t rq = cld64(a.rows + m);
     if (tid < S) merge_fetched<KT>(w0, top, acc);
-    if (tid + 256 < S) merge_fetched<KT>(w1, top, acc);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         acc.merge_xor(off);
@@ -736,11 +742,12 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
     __syncthreads();
     const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
     if (wave == 0) {
-        get_list<KT>(sm.mrec[lane & 3], top, acc);
-        acc.merge_xor(1);
-        acc.merge_xor(2);
-        top.merge_xor(1);
-        top.merge_xor(2);
+        get_list<KT>(sm.mrec[lane % kWaves], top, acc);
+#pragma unroll
+        for (int off = 1; off < kWaves; off <<= 1) {
+            acc.merge_xor(off);
+            top.merge_xor(off);
+        }
         const float lse2 = acc.m + log2f(acc.s);
         const int lvl = level - 1;
         const FrontEntry par = ld_front(a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi);
@@ -1026,7 +1033,7 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a, int tiles
 // resident at once).  Every wait is bounded, so a grid that cannot be completed ends with
 // DT_REQ_SYNC_TIMEOUT instead of hanging.
 template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
-__global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     __shared__ __attribute__((aligned(16))) BuildSmem<KT> sm;
     const int tid = threadIdx.x;
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
@@ -1040,7 +1047,7 @@ __global__ __launch_bounds__(256, 2) void k_build(const BuildArgs a) {
         if (level > a.B) break;
         const int M = (int)cld32(a.sync + kSyncRows + level);
         if (M == 0) break;
-        // tile mode (<= kTileRows rows, or float32 heads) or group mode (128-row groups)
+        // tile mode (<= kTileRows rows, or float32 heads) or group mode (kGroupRows-row groups)
         const bool grp_mode = HEAD_BF16 && M > kTileRows;
         const int GR = grp_mode ? kGroupRows : kTileRows;
         const int T = (M + GR - 1) / GR;
@@ -1114,7 +1121,7 @@ static int resident_grid(const void* f) {
     for (int i = 0; i < n; ++i)
         if (keys[i] == f && devs[i] == dev) return vals[i];
     int per = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, 256, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, f, kThreads, 0) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
     int g = per * cus;
@@ -1137,7 +1144,7 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     if (a.timing_hook) a.timing_hook(st, 0);
     // a plain launch: the loop needs no co-residency guarantee (see k_build), and a
     // cooperative launch costs about 18 us more per round on this stack
-    hipLaunchKernelGGL((k_build<KT, SAMPLE, HEAD_BF16, L_BF16>), dim3(G), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_build<KT, SAMPLE, HEAD_BF16, L_BF16>), dim3(G), dim3(kThreads), 0, st, a);
     if (a.timing_hook) a.timing_hook(st, 1);
     return hipGetLastError();
 }

@@ -18,6 +18,8 @@ constexpr int kSelectSlots = 1024;  // >= Ncap + Ncap * k
 constexpr int kMaxSplits = 512;     // vocabulary splits per parent row (merge work bound)
 constexpr int kMaxGrid = 1024;      // largest grid of the persistent construction kernel
 constexpr int kBlockCols = 32;      // vocabulary columns per MFMA block of the expansion
+constexpr int kBuildWaves = 8;      // wavefronts per workgroup of the construction kernel
+constexpr int kGroupRows = 32 * kBuildWaves;  // parent rows per group-mode expansion item
 
 // A frontier entry: a node that is (or was) expanded at some level.  self = the low word of
 // its selection key (0xFFFFFFFF for the root).

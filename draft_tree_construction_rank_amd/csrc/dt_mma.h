@@ -26,8 +26,8 @@ __device__ __forceinline__ int opaque_zero() {
 }
 
 // A tile: rows < nrows take U[token_of(row)], other rows and columns >= r are zero.
-// 256 threads.  Ends with the caller's __syncthreads().
-template <bool HEAD_BF16, typename TokFn>
+// NT threads (the workgroup size).  Ends with the caller's __syncthreads().
+template <bool HEAD_BF16, int NT = 256, typename TokFn>
 __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, TokFn token_of,
                                             uint16_t* sA, float* sAf) {
     const int tid = threadIdx.x + opaque_zero();
@@ -35,11 +35,11 @@ __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, Tok
         // 64 rows x 33 16-byte segments: every address is clamped into the row so that all
         // loads of a thread are unconditional and can be in flight together.
         constexpr int segs = kAStride / 8;
-        constexpr int per = (kTileRows * segs + 255) / 256;
+        constexpr int per = (kTileRows * segs + NT - 1) / NT;
         uint4 v[per];
 #pragma unroll
         for (int q = 0; q < per; ++q) {
-            const int i = tid + q * 256;
+            const int i = tid + q * NT;
             const int row = i / segs, seg = i % segs;
             const bool ok = i < kTileRows * segs && row < nrows && seg * 8 < r;
             const int tok = (i < kTileRows * segs && row < nrows) ? token_of(row) : 0;
@@ -49,11 +49,11 @@ __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, Tok
         }
 #pragma unroll
         for (int q = 0; q < per; ++q) {
-            const int i = tid + q * 256;
+            const int i = tid + q * NT;
             if (i < kTileRows * segs) *(uint4*)(sA + (i / segs) * kAStride + (i % segs) * 8) = v[q];
         }
     } else {
-        for (int i = tid; i < kTileRows * kAfStride; i += 256) {
+        for (int i = tid; i < kTileRows * kAfStride; i += NT) {
             const int row = i / kAfStride, kk = i % kAfStride;
             float v = 0.0f;
             if (row < nrows && kk < r) v = ((const float*)U)[(size_t)token_of(row) * r + kk];

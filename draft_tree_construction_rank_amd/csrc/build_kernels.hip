@@ -551,16 +551,18 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
             s.merge_xor(off);
             t.merge_xor(off);
         }
-        if (w == 0 && row < nrows) {
+        if (row < nrows) {
+            // the row's kWaves lanes write one 16-byte piece of its record each
             float v[RS];
 #pragma unroll
             for (int i = 0; i < RS; ++i) v[i] = 0.0f;
             put_list<KT>(v, t, s);
-            char* rec = (char*)(a.partials + ((size_t)(m0 + row) * S + split) * RS);
+            uint4* rec = (uint4*)(a.partials + ((size_t)(m0 + row) * S + split) * RS);
 #pragma unroll
-            for (int q = 0; q < RS / 2; ++q)
-                cst64(rec + 8 * q, (uint64_t)__float_as_uint(v[2 * q]) |
-                                       ((uint64_t)__float_as_uint(v[2 * q + 1]) << 32));
+            for (int c = 0; c < RS / 4; ++c)
+                if (c % kWaves == w)
+                    cst128(rec + c, make_uint4(__float_as_uint(v[4 * c]), __float_as_uint(v[4 * c + 1]),
+                                               __float_as_uint(v[4 * c + 2]), __float_as_uint(v[4 * c + 3])));
         }
     }
     __syncthreads();
@@ -674,16 +676,18 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
     }
     st.merge_xor(32);
     top.merge_xor(32);
-    if (h == 0 && live) {
+    if (live) {
+        // lanes l and l ^ 32 split the row's record into alternate 16-byte pieces
         float v[RS];
 #pragma unroll
         for (int i = 0; i < RS; ++i) v[i] = 0.0f;
         put_list<KT>(v, top, st);
-        char* rec = (char*)(a.partials + ((size_t)row * S + split) * RS);
+        uint4* rec = (uint4*)(a.partials + ((size_t)row * S + split) * RS);
 #pragma unroll
-        for (int q = 0; q < RS / 2; ++q)
-            cst64(rec + 8 * q, (uint64_t)__float_as_uint(v[2 * q]) |
-                                   ((uint64_t)__float_as_uint(v[2 * q + 1]) << 32));
+        for (int c = 0; c < RS / 4; ++c)
+            if ((c & 1) == h)
+                cst128(rec + c, make_uint4(__float_as_uint(v[4 * c]), __float_as_uint(v[4 * c + 1]),
+                                           __float_as_uint(v[4 * c + 2]), __float_as_uint(v[4 * c + 3])));
     }
     wait_vm();
     __syncthreads();  // no copy into the staging buffers is left in flight

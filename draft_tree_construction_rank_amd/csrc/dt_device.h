@@ -113,6 +113,14 @@ __device__ __forceinline__ void cst32(void* p, uint32_t v) {
 __device__ __forceinline__ void cst64(void* p, uint64_t v) {
     __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte agent-coherent store (the same write-through cache policy as cst64, which the
+// compiler emits for agent-scope relaxed atomic stores; there is no 16-byte atomic).  Its
+// completion is covered by publish(): vector memory counters drain in issue order.
+__device__ __forceinline__ void cst128(void* p, uint4 v) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 d = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(d) : "memory");
+}
 __device__ __forceinline__ uint32_t cadd32(void* p, uint32_t v) {
     return __hip_atomic_fetch_add((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -733,9 +733,14 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
     const float* base = a.partials + (size_t)m * S * RS;
     static_assert(kThreads >= kMaxSplits, "one split record per thread");
     const int s0 = tid < S ? tid : S - 1;
+    const uint64_t rq = cld64(a.rows + m);
     uint64_t w0[RS / 2];
     fetch_record<KT>(base + (size_t)s0 * RS, w0);
-    const uint64_t rq = cld64(a.rows + m);
+    const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
+    const int lvl = level - 1;
+    // the parent's frontier entry is loaded while the split records are combined
+    FrontEntry par;
+    if (wave == 0) par = ld_front(a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi);
     if (tid < S) merge_fetched<KT>(w0, top, acc);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -744,7 +749,6 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
     }
     if (lane == 0) put_list<KT>(sm.mrec[wave], top, acc);
     __syncthreads();
-    const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
     if (wave == 0) {
         get_list<KT>(sm.mrec[lane % kWaves], top, acc);
 #pragma unroll
@@ -753,8 +757,6 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
             top.merge_xor(off);
         }
         const float lse2 = acc.m + log2f(acc.s);
-        const int lvl = level - 1;
-        const FrontEntry par = ld_front(a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi);
 #pragma unroll
         for (int j = 0; j < KT; ++j) {
             if (j < a.k && lane == j) {

@@ -68,6 +68,9 @@ Layout make_layout(const dt_params* p) {
         L.gsplits = (int)s;
         L.gpart = take(R * s * 8);
     }
+#ifdef DT_TRACE
+    L.trace = take((size_t)kMaxGrid * kTraceLevels * 8 * sizeof(uint64_t));
+#endif
     L.total = off;
     return L;
 }
@@ -188,6 +191,9 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     a.rstat = (int*)(ws + lay.rstat);
     a.partials = (float*)(ws + lay.partials);
     a.out = *out;
+#ifdef DT_TRACE
+    a.trace = (uint64_t*)(ws + lay.trace);
+#endif
     a.R = p->R;
     a.B = p->B;
     a.k = p->k;

@@ -35,6 +35,22 @@ namespace dt {
 constexpr int kWaves = kBuildWaves;
 constexpr int kThreads = 64 * kWaves;
 
+// Phase timestamps (DT_TRACE builds only): thread 0 of a workgroup records the wall clock
+// for (level, slot).  Slots: 0 woke for the level, 1 first expansion item set up, 2
+// expansion items done, 3 merge loop done, 4 a select done, 5 release done, 6 first merge
+// task started.  Level 0 slot 0 = kernel start; the last level's slots 0/1 = emit start/end.
+#ifdef DT_TRACE
+#define DT_STAMP(lv, sl)                                                                    \
+    do {                                                                                    \
+        if (threadIdx.x == 0)                                                               \
+            a.trace[((size_t)blockIdx.x * kTraceLevels + (lv)) * 8 + (sl)] = wall_clock64(); \
+    } while (0)
+#else
+#define DT_STAMP(lv, sl) \
+    do {                 \
+    } while (0)
+#endif
+
 // ---------------------------------------------------------------------------------------
 // Workgroup helpers.
 // ---------------------------------------------------------------------------------------
@@ -125,18 +141,27 @@ struct EmitSmem {
 // ---------------------------------------------------------------------------------------
 // Shared memory of the persistent kernel (one workgroup; phases reuse the first region).
 // ---------------------------------------------------------------------------------------
+// Group-mode staging ring: kStages slots, each one 32-column block of W (32 rows of Wt, 16 KB
+// at r = 256) and the matching 64-byte segments of the block logits of the group's 256 rows
+// (16 KB).
+constexpr int kStages = 4;
+
 template <int KT>
 struct BuildSmem {
     union {
         uint16_t sA[kTileRows * kAStride];  // bf16 parent rows of U (tile-mode expand)
-        uint4 wst[2][kBlockCols * 32];      // two staged 32-column blocks of W (group-mode expand)
-        float sAf[kTileRows * kAfStride];   // f32 parent rows of U (expand)
-        uint64_t keys[kSelectSlots];        // select
-        EmitSmem em;                        // emit
+        float sAf[kTileRows * kAfStride];   // f32 parent rows of U (tile-mode expand)
+        struct {
+            uint4 w[kStages][kBlockCols * 32];
+            uint4 l[kStages][kGroupRows * 4];
+        } g;                                            // group-mode staging ring
+        float xrec[kWaves][kTileRows][rec_floats(KT)];  // per-wavefront lists of a tile item
+        uint64_t keys[kSelectSlots];                    // select
+        EmitSmem em;                                    // emit
     } u;
-    float xrec[kWaves][kTileRows][rec_floats(KT)];  // per-wavefront lists of an expansion item
-    float mrec[kWaves][rec_floats(KT)];             // per-wavefront lists of a merged row
+    float mrec[kWaves][rec_floats(KT)];  // per-wavefront lists of a merged row
     size_t lbase[kTileRows];
+    size_t glbase[kGroupRows];  // group mode: block-logit row offset of each row of the group
     uint64_t hash[kTileRows];
     uint64_t rkth[128];  // per parent row of an item: the largest KT-th list entry seen so far
     int tok[kTileRows];
@@ -447,13 +472,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     const int b_beg = (int)((long long)split * NB / S);
     const int b_end = (int)((long long)(split + 1) * NB / S);
-    // The first W block of this wavefront does not depend on the parent rows: its loads are
-    // in flight during the row set-up below.
     bf16x8 wf[16];
-    if constexpr (HEAD_BF16) {
-        if (b_beg + wave < b_end) load_wfrag(a.Wt, a.V, a.r, (b_beg + wave) * kBlockCols, wf);
-    }
-
     if (tid < kTileRows) {
         int tok = 0;
         size_t lb = 0;
@@ -478,7 +497,13 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
     else
         load_a_tile<false, kThreads>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, nullptr, sm.u.sAf);
     __syncthreads();
+    // The first W block is loaded only once the parent rows are staged: issued earlier, the
+    // whole grid's first blocks (32 MB) queue ahead of the set-up loads.
+    if constexpr (HEAD_BF16) {
+        if (b_beg + wave < b_end) load_wfrag(a.Wt, a.V, a.r, (b_beg + wave) * kBlockCols, wf);
+    }
 
+    DT_STAMP(level, 1);
     const bool two = nrows > 32;
     const int p0 = lane & 31;
     const size_t lb0 = sm.lbase[p0], lb1 = sm.lbase[32 + p0];
@@ -535,9 +560,10 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         s1.merge_xor(32);
         t1.merge_xor(32);
     }
+    __syncthreads();  // the lists below overwrite the U tile
     if (h == 0) {
-        put_list<KT>(sm.xrec[wave][p0], t0, s0);
-        if (two) put_list<KT>(sm.xrec[wave][32 + p0], t1, s1);
+        put_list<KT>(sm.u.xrec[wave][p0], t0, s0);
+        if (two) put_list<KT>(sm.u.xrec[wave][32 + p0], t1, s1);
     }
     __syncthreads();
     {
@@ -545,7 +571,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         const int row = tid / kWaves, w = tid % kWaves;
         TopK<KT> t;
         Lse2 s;
-        get_list<KT>(sm.xrec[w][row], t, s);
+        get_list<KT>(sm.u.xrec[w][row], t, s);
 #pragma unroll
         for (int off = 1; off < kWaves; off <<= 1) {
             s.merge_xor(off);
@@ -569,57 +595,155 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
 }
 
 // ---------------------------------------------------------------------------------------
-// Group-mode expansion (levels with more than kTileRows parent rows, bf16 heads): an item is
-// a group of kGroupRows = 256 parent rows x a vocabulary split.  Wavefront w owns rows
-// 32w .. 32w+31 of the group and keeps their U rows as MFMA B fragments in registers for the
-// whole item; each 32-column block of W (32 rows of Wt, 16 KB at r = 256) is copied once per
-// workgroup into LDS with coalesced global->LDS loads, double-buffered so that block b+1
-// arrives while block b is multiplied, and read by all eight wavefronts.  W is thus read
-// once per 256 parent rows (once per level up to 256 rows).  The LDS copy stores row j's
-// 16-byte chunk c at slot 32j + (c ^ (j & 31)), so the fragment reads of 16 consecutive
-// lanes hit distinct banks.
+// Group-mode expansion (levels with more than kTileRows parent rows, bf16 heads and logits,
+// V a multiple of 8): an item is a group of kGroupRows = 256 parent rows x a vocabulary split.
+// Wavefront w owns rows 32w .. 32w+31 of the group and keeps their U rows as MFMA B fragments
+// in registers for the whole item.  Each 32-column block of W (32 rows of Wt, 16 KB at
+// r = 256) and the rows' 64-byte segments of block logits (16 KB) are copied once per
+// workgroup into an LDS ring of kStages slots with global->LDS loads, so that three blocks
+// are in flight while one is multiplied: with a single block in flight the copies' latency,
+// not HBM bandwidth, bounded the loop.  Every wavefront issues exactly four 1 KB copies per
+// block (two of W, two of logits) and nothing else in the loop, so "this wavefront's copies
+// of block b are done" is a vmcnt wait with the count of copies issued after them.
+//
+// LDS layouts (16-byte slots): W row j's chunk c sits at slot 32j + (c ^ (j & 31)), so the
+// fragment reads of 16 consecutive lanes hit distinct banks; the logits piece p (8 columns) of
+// group row i sits at slot 4i + (p ^ ((i >> 2) & 3)).
 // ---------------------------------------------------------------------------------------
 
-// Issue this wavefront's share of the global->LDS copy of block `blk` (16 / kWaves loads of
-// 1 KB).
-__device__ __forceinline__ void stage_wblock(const BuildArgs& a, int blk, uint4* dst) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int chunks = a.r >> 3;  // 16-byte chunks per row of Wt
-#pragma unroll
-    for (int q = 0; q < 16 / kWaves; ++q) {
-        const int j = (16 / kWaves) * wave + q;  // 1 KB piece j = LDS slots 64j .. 64j+63
-        const int row = 2 * j + (lane >> 5);   // W row within the block
-        int c = (lane & 31) ^ (row & 31);      // chunk that belongs in this slot
-        c = c < chunks ? c : 0;                // past r: any finite data (U is zero there)
-        int col = blk * kBlockCols + row;
-        col = col < a.V ? col : a.V - 1;
-        const uint16_t* src = (const uint16_t*)a.Wt + (size_t)col * a.r + c * 8;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(dst + 64 * j),
-                                         16, 0, 0);
-    }
+// vmcnt(N) with expcnt and lgkmcnt unconstrained (gfx9 encoding: vmcnt in bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Wait for this wavefront's outstanding global loads (including global->LDS copies).
-__device__ __forceinline__ void wait_vm() {
+__device__ __forceinline__ void wait_vm() { wait_vmcnt<0>(); }
+
+// Per-item source addresses of this wavefront's copies: its two W chunks (as an offset
+// within a block of Wt rows) and its two logit pieces (row offset into L, piece column).
+struct GroupCopy {
+    size_t wofs[16 / kWaves];
+    size_t lofs[(kGroupRows * 4 / 64) / kWaves];
+    int lcol[(kGroupRows * 4 / 64) / kWaves];
+};
+constexpr int kCopiesPerBlock = 16 / kWaves + (kGroupRows * 4 / 64) / kWaves;
+
+template <int KT>
+__device__ __forceinline__ GroupCopy group_copy_setup(const BuildArgs& a, const BuildSmem<KT>& sm) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int chunks = a.r >> 3;  // 16-byte chunks per row of Wt
+    GroupCopy gc;
+#pragma unroll
+    for (int q = 0; q < 16 / kWaves; ++q) {
+        const int j = (16 / kWaves) * wave + q;  // 1 KB piece j = LDS slots 64j .. 64j+63
+        const int row = 2 * j + (lane >> 5);     // W row within the block
+        int c = (lane & 31) ^ (row & 31);        // chunk that belongs in this slot
+        c = c < chunks ? c : 0;                  // past r: any finite data (U is zero there)
+        gc.wofs[q] = (size_t)row * a.r + c * 8;
+    }
+#pragma unroll
+    for (int q = 0; q < (kGroupRows * 4 / 64) / kWaves; ++q) {
+        const int j = ((kGroupRows * 4 / 64) / kWaves) * wave + q;
+        const int sl = 64 * j + lane;
+        const int row = sl >> 2, piece = (sl & 3) ^ ((row >> 2) & 3);
+        gc.lofs[q] = sm.glbase[row];
+        gc.lcol[q] = 8 * piece;
+    }
+    return gc;
+}
+
+// Issue this wavefront's copies of block `blk` into ring slot `slot` (kCopiesPerBlock
+// global->LDS loads of 16 bytes per lane; every address clamped into its array).
+template <int KT>
+__device__ __forceinline__ void stage_block(const BuildArgs& a, const GroupCopy& gc, int blk, int slot,
+                                            BuildSmem<KT>& sm) {
+    const int wave = threadIdx.x >> 6;
+    const int c0 = blk * kBlockCols;
+    // rows of the block past V read the last row of Wt (their columns are masked)
+    const int wlast = a.V - kBlockCols;
+#pragma unroll
+    for (int q = 0; q < 16 / kWaves; ++q) {
+        const int j = (16 / kWaves) * wave + q;
+        size_t off = (size_t)c0 * a.r + gc.wofs[q];
+        if (c0 > wlast) {
+            const int row = (int)(gc.wofs[q] / a.r);
+            const int col = c0 + row < a.V ? c0 + row : a.V - 1;
+            off = (size_t)col * a.r + (gc.wofs[q] - (size_t)row * a.r);
+        }
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)((const uint16_t*)a.Wt + off),
+            (__attribute__((address_space(3))) void*)(sm.u.g.w[slot] + 64 * j), 16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < (kGroupRows * 4 / 64) / kWaves; ++q) {
+        const int j = ((kGroupRows * 4 / 64) / kWaves) * wave + q;
+        int col = c0 + gc.lcol[q];
+        col = col <= a.V - 8 ? col : a.V - 8;  // past V: any data (masked in the epilogue)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)((const uint16_t*)a.L + gc.lofs[q] + col),
+            (__attribute__((address_space(3))) void*)(sm.u.g.l[slot] + 64 * j), 16, 0, 0);
+    }
+}
+
+// LDS reads of the staging ring, written as asm that waits for its own results: the compiler
+// would otherwise drain every global->LDS copy in flight before each read (it cannot tell
+// the slot being read from the slots still being filled).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void lds_read4_b128(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                               u32x4_t& r0, u32x4_t& r1, u32x4_t& r2, u32x4_t& r3) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+__device__ __forceinline__ void lds_read4_b64(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                              u32x2_t& r0, u32x2_t& r1, u32x2_t& r2, u32x2_t& r3) {
+    asm volatile(
+        "ds_read_b64 %0, %4\n\t"
+        "ds_read_b64 %1, %5\n\t"
+        "ds_read_b64 %2, %6\n\t"
+        "ds_read_b64 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+        : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), which would also wait for
+// every global load in flight; the callers order LDS themselves.
+__device__ __forceinline__ void bare_barrier() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
+    __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-template <int KT, bool SAMPLE, bool L_BF16>
+template <int KT, bool SAMPLE>
 __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int M, int S, int grp,
                                              int split, BuildSmem<KT>& sm) {
     constexpr int RS = rec_floats(KT);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, p0 = lane & 31;
     const int lvl = level - 1;
-    const int row = grp * kGroupRows + 32 * wave + p0;
+    const int rl = 32 * wave + p0;  // row within the group
+    const int row = grp * kGroupRows + rl;
     const bool live = row < M;
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     const int b_beg = (int)((long long)split * NB / S);
     const int b_end = (int)((long long)(split + 1) * NB / S);
 
-    if (b_beg < b_end) stage_wblock(a, b_beg, sm.u.wst[0]);
     int tok = 0;
     size_t lb = 0;
     uint64_t hh = 0;
@@ -643,34 +767,58 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
             uf[s] = __builtin_bit_cast(bf16x8, kk < a.r ? v : make_uint4(0, 0, 0, 0));
         }
     }
-    const bool lvec = (a.V & 3) == 0;
-    LGroups<L_BF16> lcur, lnext;
-    if (b_beg < b_end) load_lgroups<L_BF16>(a, lb, b_beg * kBlockCols, h, lvec, lnext);
+    if (h == 0) sm.glbase[rl] = lb;
+    DT_STAMP(level, 1);
+    __syncthreads();
+    const GroupCopy gc = group_copy_setup<KT>(a, sm);
+    // prologue: blocks b_beg .. b_beg + kStages - 2 in flight
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+        if (b_beg + i < b_end) stage_block<KT>(a, gc, b_beg + i, (b_beg + i) % kStages, sm);
     TopK<KT> top;
     Lse2 st;
     top.init();
     st.init();
+    const int swz = (rl >> 2) & 3;
+    static_assert(kStages - 2 <= 2, "the wait counts below cover two blocks in flight");
     for (int blk = b_beg; blk < b_end; ++blk) {
-        wait_vm();
-        __syncthreads();  // block blk staged by every wavefront; block blk-1 fully consumed
-        // All 16 A fragments are read from LDS before the next block's copy is issued: a read
-        // of LDS placed after a global->LDS copy waits for every global load in flight, which
-        // would expose the whole latency of the prefetch on every block.
-        const uint4* wb = sm.u.wst[(blk - b_beg) & 1] + p0 * 32;
-        uint4 wf[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) wf[s] = wb[(2 * s + h) ^ p0];
-        lcur = lnext;
-        if (blk + 1 < b_end) {
-            stage_wblock(a, blk + 1, sm.u.wst[(blk + 1 - b_beg) & 1]);
-            load_lgroups<L_BF16>(a, lb, (blk + 1) * kBlockCols, h, lvec, lnext);
-        }
+        // this wavefront's copies of block blk are done once at most the copies of the
+        // blocks issued after it are outstanding
+        const int after = min(kStages - 2, b_end - 1 - blk);
+        if (after >= 2) wait_vmcnt<2 * kCopiesPerBlock>();
+        else if (after == 1) wait_vmcnt<kCopiesPerBlock>();
+        else wait_vmcnt<0>();
+        bare_barrier();  // block blk staged by every wavefront; slot (blk - 1) read by all
+        if (blk + kStages - 1 < b_end)
+            stage_block<KT>(a, gc, blk + kStages - 1, (blk + kStages - 1) % kStages, sm);
+        const int slot = blk % kStages;
+        const uint32_t wb = lds_addr(sm.u.g.w[slot] + p0 * 32);
+        const uint32_t lb0 = lds_addr(sm.u.g.l[slot] + 4 * rl) + 8 * h;
         f32x16 acc;
-        lgroups_to_acc<L_BF16>(lcur, acc);
+        {
+            u32x2_t l0, l1, l2, l3;
+            lds_read4_b64(lb0 + 16 * (0 ^ swz), lb0 + 16 * (1 ^ swz), lb0 + 16 * (2 ^ swz),
+                          lb0 + 16 * (3 ^ swz), l0, l1, l2, l3);
+            const u32x2_t lv[4] = {l0, l1, l2, l3};
 #pragma unroll
-        for (int s = 0; s < 16; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[s]), uf[s],
-                                                          acc, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                acc[4 * j + 0] = bf16_lo(lv[j].x);
+                acc[4 * j + 1] = bf16_hi(lv[j].x);
+                acc[4 * j + 2] = bf16_lo(lv[j].y);
+                acc[4 * j + 3] = bf16_hi(lv[j].y);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            u32x4_t w0, w1, w2, w3;
+            lds_read4_b128(wb + 16 * ((8 * g + 0 + h) ^ p0), wb + 16 * ((8 * g + 2 + h) ^ p0),
+                           wb + 16 * ((8 * g + 4 + h) ^ p0), wb + 16 * ((8 * g + 6 + h) ^ p0),
+                           w0, w1, w2, w3);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w0), uf[4 * g + 0], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w1), uf[4 * g + 1], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w2), uf[4 * g + 2], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w3), uf[4 * g + 3], acc, 0, 0, 0);
+        }
         // each row lives in two lanes of one wavefront: no workgroup-shared bound
         expand_epilogue<KT, SAMPLE>(a, acc, blk * kBlockCols, h, hh, live, nullptr, top, st);
     }
@@ -690,7 +838,7 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
                                            __float_as_uint(v[4 * c + 2]), __float_as_uint(v[4 * c + 3])));
     }
     wait_vm();
-    __syncthreads();  // no copy into the staging buffers is left in flight
+    __syncthreads();  // no copy into the staging ring is left in flight
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1044,6 +1192,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     const int tid = threadIdx.x;
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     bool failed = false;
+    DT_STAMP(0, 0);
     for (int level = 1;; ++level) {
         // the previous level's selects are complete once the generation reaches level - 1
         if (!wait_at_least(a.sync, a.sync + kSyncGen, (unsigned)(level - 1), sm.bcast)) {
@@ -1051,10 +1200,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
             break;
         }
         if (level > a.B) break;
+        DT_STAMP(level, 0);
         const int M = (int)cld32(a.sync + kSyncRows + level);
         if (M == 0) break;
         // tile mode (<= kTileRows rows, or float32 heads) or group mode (kGroupRows-row groups)
-        const bool grp_mode = HEAD_BF16 && M > kTileRows;
+        const bool grp_mode = HEAD_BF16 && L_BF16 && (a.V & 7) == 0 && M > kTileRows;
         const int GR = grp_mode ? kGroupRows : kTileRows;
         const int T = (M + GR - 1) / GR;
         const int S = splits_for(T, (int)gridDim.x, NB);
@@ -1063,8 +1213,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
         // so when S and G are multiples of 8 split j of every row tile runs on one XCD, and a
         // W block read for one tile is an L2 hit for the others.
         for (int item = blockIdx.x; item < T * S; item += gridDim.x) {
-            if constexpr (HEAD_BF16) {
-                if (grp_mode) expand_group<KT, SAMPLE, L_BF16>(a, level, M, S, item / S, item % S, sm);
+            if constexpr (HEAD_BF16 && L_BF16) {
+                if (grp_mode) expand_group<KT, SAMPLE>(a, level, M, S, item / S, item % S, sm);
                 else expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
             } else {
                 expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
@@ -1072,6 +1222,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
             publish_wg();
             if (tid == 0) cadd32(a.tdone + item / S, 1u);
         }
+        DT_STAMP(level, 2);
+        bool first_task = true;
         // merge tasks: parent rows in order, each once its tile's splits are all in
         for (;;) {
             if (tid == 0) sm.bcast[1] = (int)cadd32(a.sync + kSyncTask + level, 1u);
@@ -1083,6 +1235,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
                 failed = true;
                 break;
             }
+            if (first_task) DT_STAMP(level, 6);
+            first_task = false;
             const int req = merge_row<KT>(a, level, S, m, sm);
             publish_wg();
             if (tid == 0) {
@@ -1093,24 +1247,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
             if (sm.bcast[2]) {
                 select_request(a, level, req, sm.u.keys, sm.sh);
                 publish_wg();
+                DT_STAMP(level, 4);
                 if (tid == 0) sm.bcast[3] = (cadd32(a.sync + kSyncDone + level, 1u) + 1u == nreq) ? 1 : 0;
                 __syncthreads();
                 if (sm.bcast[3]) {
                     release_rows(a, level, T, sm.sh);
                     publish_wg();
                     if (tid == 0) cst32(a.sync + kSyncGen, (unsigned)level);
+                    DT_STAMP(level, 5);
                 }
             }
             __syncthreads();
         }
+        DT_STAMP(level, 3);
         if (failed) break;
     }
+    DT_STAMP(kTraceLevels - 1, 0);
     if (failed) cst32(a.sync + kSyncErr, 1u);
     for (int req = blockIdx.x; req < a.R; req += gridDim.x)
         emit_request(a, req, failed || cld32(a.sync + kSyncErr) != 0u, sm.u.em);
     if (blockIdx.x == 0 && a.out.level_rows)
         for (int l = tid; l < a.B; l += blockDim.x)
             a.out.level_rows[l] = (int)cld32(a.sync + kSyncRows + l + 1);
+    DT_STAMP(kTraceLevels - 1, 1);
 }
 
 // ---------------------------------------------------------------------------------------

@@ -60,6 +60,7 @@ struct Layout {
     size_t vstate;    // VState [R]
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
     size_t gpart;     // (float, int) [R][gsplits]: greedy verify, split argmax of the root rows
+    size_t trace;     // u64 [kMaxGrid][kTraceLevels][8]: phase timestamps (DT_TRACE builds only)
     size_t total;
     int G;            // largest grid of the construction kernel (sizes the partial records)
     int NC;           // vocabulary chunks of 128 columns
@@ -92,6 +93,10 @@ constexpr int kSyncTask = 88;      // [level]: merge-task counter
 constexpr int kSyncDone = 128;     // [level]: requests whose select is done
 constexpr int kSyncWords = 192;
 
+// Phase timestamps of the construction kernel, written only by builds compiled with
+// DT_TRACE: per workgroup and level, eight wall-clock stamps (slot meanings at DT_STAMP).
+constexpr int kTraceLevels = 40;
+
 // Arguments of the tree-construction kernels (passed by value).
 struct BuildArgs {
     void (*timing_hook)(hipStream_t, int);  // host-only: brackets each expansion launch
@@ -115,6 +120,7 @@ struct BuildArgs {
     int* rstat;
     float* partials;
     dt_tree out;
+    uint64_t* trace;  // phase timestamps (DT_TRACE builds only; null otherwise)
     int R, B, k, V, r, Ncap, NC;
     float y2scale;  // log2(e) / T' : converts z to log2-unit tempered logits
     float invT;     // 1 / T' (sample ranking key)

@@ -30,13 +30,12 @@ Layout make_layout(const dt_params* p) {
     // at most g * max(G, T) of them (g = kTileRows in tile mode, kGroupRows in group mode)
     const size_t cap_rows = (size_t)kGroupRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
     L.sync = take(kSyncWords * sizeof(unsigned));
-    L.tdone = take((size_t)max_tiles((int)R, (int)N) * sizeof(unsigned));
-    L.rdone = take(R * sizeof(unsigned));
-    L.rows = take(R * N * sizeof(int2));
+    L.tdone = take((B + 2) * (size_t)max_tiles((int)R, (int)N) * sizeof(unsigned));
+    L.rdone = take((B + 2) * R * sizeof(unsigned));
+    L.rows = take(2 * R * N * sizeof(RowRec));
     L.front = take(R * (B + 1) * N * sizeof(FrontEntry));
     L.fcount = take(R * (B + 1) * sizeof(int));
     L.arena = take(R * B * N * k * sizeof(ChildRec));
-    L.ckeys = take(R * N * k * sizeof(uint64_t));
     L.skeys = take(R * N * sizeof(uint64_t));
     L.scount = take(R * sizeof(int));
     L.nbeff = take(R * sizeof(int));
@@ -69,7 +68,7 @@ Layout make_layout(const dt_params* p) {
         L.gpart = take(R * s * 8);
     }
 #ifdef DT_TRACE
-    L.trace = take((size_t)kMaxGrid * kTraceLevels * 8 * sizeof(uint64_t));
+    L.trace = take((size_t)kMaxGrid * kTraceLevels * 16 * sizeof(uint64_t));
 #endif
     L.total = off;
     return L;
@@ -178,13 +177,12 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     a.n_budget = n_budget;
     a.tau = tau;
     a.sync = (unsigned*)(ws + lay.sync);
-    a.rows = (int2*)(ws + lay.rows);
+    a.rows = (RowRec*)(ws + lay.rows);
     a.tdone = (unsigned*)(ws + lay.tdone);
     a.rdone = (unsigned*)(ws + lay.rdone);
     a.front = (FrontEntry*)(ws + lay.front);
     a.fcount = (int*)(ws + lay.fcount);
     a.arena = (ChildRec*)(ws + lay.arena);
-    a.ckeys = (uint64_t*)(ws + lay.ckeys);
     a.skeys = (uint64_t*)(ws + lay.skeys);
     a.scount = (int*)(ws + lay.scount);
     a.nbeff = (int*)(ws + lay.nbeff);
@@ -201,6 +199,7 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     a.r = p->r;
     a.Ncap = p->Ncap;
     a.NC = lay.NC;
+    a.Tmax = max_tiles(p->R, p->Ncap);
     a.y2scale = (float)(1.4426950408889634 / (double)Teff);
     a.invT = (float)(1.0 / (double)Teff);
     a.seed_lo = (uint32_t)p->seed;

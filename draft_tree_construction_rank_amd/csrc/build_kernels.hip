@@ -36,14 +36,14 @@ constexpr int kWaves = kBuildWaves;
 constexpr int kThreads = 64 * kWaves;
 
 // Phase timestamps (DT_TRACE builds only): thread 0 of a workgroup records the wall clock
-// for (level, slot).  Slots: 0 woke for the level, 1 first expansion item set up, 2
-// expansion items done, 3 merge loop done, 4 a select done, 5 release done, 6 first merge
-// task started.  Level 0 slot 0 = kernel start; the last level's slots 0/1 = emit start/end.
+// for (level, slot), 16 slots per level.  Slots: 0 woke for the level, 1 first expansion item set up, 2
+// expansion items done, 3 merge loop done, 4 a select done, 5 a merge published, 6 first
+// merge task started, 7 a select's candidates loaded, 8 tile-mode parent rows read.  Level 0 slot 0 = kernel start; the last level's slots 0/1 = emit start/end.
 #ifdef DT_TRACE
 #define DT_STAMP(lv, sl)                                                                    \
     do {                                                                                    \
         if (threadIdx.x == 0)                                                               \
-            a.trace[((size_t)blockIdx.x * kTraceLevels + (lv)) * 8 + (sl)] = wall_clock64(); \
+            a.trace[((size_t)blockIdx.x * kTraceLevels + (lv)) * 16 + (sl)] = wall_clock64(); \
     } while (0)
 #else
 #define DT_STAMP(lv, sl) \
@@ -115,6 +115,37 @@ __device__ __forceinline__ bool wait_at_least(unsigned* sync, const unsigned* p,
     return ok;
 }
 
+// Thread 0 waits until the generation word's level reaches `level` (or the error flag is
+// set); the word is broadcast to the workgroup.  Returns false on error or time-out.
+__device__ __forceinline__ bool wait_gen(unsigned* sync, int level, int* bcast, uint64_t* gen) {
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        uint32_t it = 0;
+        uint64_t g;
+        while ((int)((g = cld64(sync + kSyncGen)) & 0xFFu) < level) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it > kSpinLimit) {
+                cst32(sync + kSyncErr, 1u);
+                ok = 0;
+                break;
+            }
+            if ((it & 63u) == 0u && cld32(sync + kSyncErr) != 0u) {
+                ok = 0;
+                break;
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        bcast[0] = ok;
+        bcast[1] = (int)(uint32_t)g;
+        bcast[2] = (int)(uint32_t)(g >> 32);
+    }
+    __syncthreads();
+    const bool ok = bcast[0] != 0;
+    *gen = (uint64_t)(uint32_t)bcast[1] | ((uint64_t)(uint32_t)bcast[2] << 32);
+    __syncthreads();
+    return ok;
+}
+
 // Vocabulary splits for T tiles on a grid of G workgroups: about one item per workgroup,
 // at most kMaxSplits (so that one workgroup can merge a row's records in one pass), and a
 // multiple of 8 when >= 8 so that all tiles of one split run on the same XCD (blocks are
@@ -126,6 +157,12 @@ __device__ __forceinline__ int splits_for(int T, int G, int NB) {
     if (s > NB) s = NB;
     if (s < 1) s = 1;
     return s;
+}
+
+// Parent rows of a level (two buffers: a level's selects write the next level's rows while
+// other requests' merges still read the current ones).
+__device__ __forceinline__ RowRec* level_rows(const BuildArgs& a, int level) {
+    return a.rows + (size_t)(level & 1) * a.R * a.Ncap;
 }
 
 // Staging of one request's emit (see emit_request).
@@ -141,6 +178,14 @@ struct EmitSmem {
 // ---------------------------------------------------------------------------------------
 // Shared memory of the persistent kernel (one workgroup; phases reuse the first region).
 // ---------------------------------------------------------------------------------------
+// Staging of one request's select (see select_request).
+struct SelSmem {
+    uint64_t keys[kSelectSlots];
+    uint64_t sorted[kMaxNcap];
+    int ctok[kMaxNcap * kMaxK];
+    uint64_t chash[kMaxNcap * kMaxK];
+};
+
 // Group-mode staging ring: kStages slots, each one 32-column block of W (32 rows of Wt, 16 KB
 // at r = 256) and the matching 64-byte segments of the block logits of the group's 256 rows
 // (16 KB).
@@ -156,7 +201,7 @@ struct BuildSmem {
             uint4 l[kStages][kGroupRows * 4];
         } g;                                            // group-mode staging ring
         float xrec[kWaves][kTileRows][rec_floats(KT)];  // per-wavefront lists of a tile item
-        uint64_t keys[kSelectSlots];                    // select
+        SelSmem sel;                                    // select
         EmitSmem em;                                    // emit
     } u;
     float mrec[kWaves][rec_floats(KT)];  // per-wavefront lists of a merged row
@@ -167,6 +212,7 @@ struct BuildSmem {
     int tok[kTileRows];
     int sh[256];
     int bcast[4];
+    int lrows[kMaxB + 2];  // parent rows of each level (as read from the generation word)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -478,12 +524,12 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         size_t lb = 0;
         uint64_t hh = 0;
         if (tid < nrows) {
-            const uint64_t rq = cld64(a.rows + m0 + tid);
-            const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
-            const FrontEntry* fe = a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi;
-            tok = (int)(uint32_t)(cld64(fe) >> 32);
+            const RowRec* rr = level_rows(a, level) + m0 + tid;
+            const uint64_t w0 = cld64(rr), w1 = cld64((const char*)rr + 8);
+            hh = cld64((const char*)rr + 16);
+            const int req = (int)(uint32_t)w0;
+            tok = (int)(uint32_t)w1;
             tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
-            hh = cld64((const char*)fe + 16);
             lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
         }
         sm.tok[tid] = tok;
@@ -492,6 +538,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         sm.rkth[tid] = 0;
     }
     __syncthreads();
+    DT_STAMP(level, 8);
     if constexpr (HEAD_BF16)
         load_a_tile<true, kThreads>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, sm.u.sA, nullptr);
     else
@@ -748,12 +795,12 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
     size_t lb = 0;
     uint64_t hh = 0;
     if (live) {
-        const uint64_t rq = cld64(a.rows + row);
-        const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
-        const FrontEntry* fe = a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi;
-        tok = (int)(uint32_t)(cld64(fe) >> 32);
+        const RowRec* rr = level_rows(a, level) + row;
+        const uint64_t w0 = cld64(rr), w1 = cld64((const char*)rr + 8);
+        hh = cld64((const char*)rr + 16);
+        const int req = (int)(uint32_t)w0;
+        tok = (int)(uint32_t)w1;
         tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
-        hh = cld64((const char*)fe + 16);
         lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
     }
     // B fragments: U[tok][16 s + 8 h .. +8], zero past r
@@ -869,9 +916,10 @@ __device__ __forceinline__ void merge_fetched(const uint64_t (&w)[rec_floats(KT)
     top.merge(o.k, o.y);
 }
 
+// Returns the row's request and its rows at this level (F) through *req / *F.
 template <int KT>
-__device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, int m,
-                                         BuildSmem<KT>& sm) {
+__device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, int m,
+                                          BuildSmem<KT>& sm, int* req_out, int* F_out) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     constexpr int RS = rec_floats(KT);
     TopK<KT> top;
@@ -881,14 +929,18 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
     const float* base = a.partials + (size_t)m * S * RS;
     static_assert(kThreads >= kMaxSplits, "one split record per thread");
     const int s0 = tid < S ? tid : S - 1;
-    const uint64_t rq = cld64(a.rows + m);
+    // the parent row is loaded with the split records (one round trip)
+    const RowRec* rr = level_rows(a, level) + m;
+    const uint64_t r0 = cld64(rr), r1 = cld64((const char*)rr + 8), r2 = cld64((const char*)rr + 16),
+                   r3 = cld64((const char*)rr + 24);
     uint64_t w0[RS / 2];
     fetch_record<KT>(base + (size_t)s0 * RS, w0);
-    const int req = (int)(uint32_t)rq, fi = (int)(uint32_t)(rq >> 32);
+    const int req = (int)(uint32_t)r0, fi = (int)(uint32_t)(r0 >> 32);
+    const float par_s = __uint_as_float((uint32_t)(r1 >> 32));
+    const uint64_t par_hash = r2;
+    *req_out = req;
+    *F_out = (int)(uint32_t)r3;
     const int lvl = level - 1;
-    // the parent's frontier entry is loaded while the split records are combined
-    FrontEntry par;
-    if (wave == 0) par = ld_front(a.front + ((size_t)req * (a.B + 1) + lvl) * a.Ncap + fi);
     if (tid < S) merge_fetched<KT>(w0, top, acc);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -916,123 +968,154 @@ __device__ __forceinline__ int merge_row(const BuildArgs& a, int level, int S, i
 #pragma unroll
                 for (int ii = 1; ii < 16; ++ii) cv = (bin == ii) ? a.cal[ii] : cv;
                 ChildRec c;
-                c.token = entry_tok(top.k[j]);
-                c.s = par.s * cv;
+                // a list shorter than k (possible only with non-finite logits) leaves the
+                // missing children token -1: never selected
+                c.token = top.k[j] != 0 ? entry_tok(top.k[j]) : -1;
+                c.s = par_s * cv;
                 c.logq = l2 * 0.69314718055994530942f;
                 c.pad = 0;
-                c.hash = child_hash(par.hash, c.token);
+                c.hash = child_hash(par_hash, c.token);
                 st_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j, c);
-                // a list shorter than k (possible only with non-finite logits) leaves the
-                // missing children token -1 and key 0: never selected
-                cst64(a.ckeys + (size_t)req * a.Ncap * a.k + fi * a.k + j,
-                      top.k[j] != 0 ? make_key(c.s, level, fi, j) : 0);
             }
         }
     }
-    return req;
 }
 
 // ---------------------------------------------------------------------------------------
-// Select, one workgroup per request: candidates = the kept set + this level's children;
-// drop survival < tau; bitonic sort (descending key) in LDS; keep min(n_budget, #left).
-// The kept nodes of depth `level` become the next frontier in canonical order.
+// Select, one workgroup per request, run by the workgroup that merged the request's last
+// row: candidates = the kept set + this level's children (read as child records, with the
+// kept count, budget and threshold, in one round of loads); drop survival < tau; bitonic
+// sort (descending key) in LDS; keep min(n_budget, #left).  The kept nodes of depth `level`
+// become the next frontier in canonical order: their frontier entries (for the emit) and
+// their parent rows of the next level, at rows allocated with one atomic that also counts
+// the requests.  The last request to finish publishes the next level's sizes in the
+// generation word.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ void select_request(const BuildArgs& a, int level, int req,
-                                               uint64_t* keys, int* sh) {
+
+__device__ __forceinline__ void select_request(const BuildArgs& a, int level, int req, int F,
+                                               unsigned nreq, SelSmem& ss, int* sh, int* bcast) {
     const int tid = threadIdx.x;
     const int lvl = level - 1;
-    const int F = cldi(a.fcount + req * (a.B + 1) + lvl);
+    const int Ncap = a.Ncap, k = a.k;
+    const int nchild = F * k;
     const int nprev = cldi(a.scount + req);
     const int nbudget = cldi(a.nbeff + req);
-    const int ncand = nprev + F * a.k;
     const float tau = a.tau[req];
-    int P = 2;
-    while (P < ncand) P <<= 1;
-    for (int i = tid; i < P; i += blockDim.x) {
-        uint64_t key = 0;
-        if (i < nprev) key = cld64(a.skeys + (size_t)req * a.Ncap + i);
-        else if (i < ncand) key = cld64(a.ckeys + (size_t)req * a.Ncap * a.k + (i - nprev));
-        if (key != 0 && key_surv(key) < tau) key = 0;
-        keys[i] = key;
-    }
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < P / 2; i += blockDim.x) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = ((lo & size) == 0);
-                const uint64_t x = keys[lo], y = keys[hi];
-                if ((x < y) == desc) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __syncthreads();
+    // slot i < Ncap: kept node i (valid if i < nprev); slot Ncap + c: child c of this level
+    const ChildRec* crow = a.arena + ((size_t)req * a.B + lvl) * Ncap * k;
+    uint64_t kk[2], cw0[2], cw2[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = tid + q * kThreads;
+        kk[q] = 0;
+        cw0[q] = 0;
+        cw2[q] = 0;
+        if (i < Ncap) kk[q] = cld64(a.skeys + (size_t)req * Ncap + i);
+        else if (i < Ncap + nchild) {
+            cw0[q] = cld64(crow + (i - Ncap));
+            cw2[q] = cld64((const char*)(crow + (i - Ncap)) + 16);
         }
     }
+    const int ncand = nprev + nchild;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = tid + q * kThreads;
+        if (i < Ncap) {
+            if (i < nprev) ss.keys[i] = (key_surv(kk[q]) < tau) ? 0 : kk[q];
+        } else if (i < Ncap + nchild) {
+            const int c = i - Ncap;
+            const int tok = (int)(uint32_t)cw0[q];
+            const float sv = __uint_as_float((uint32_t)(cw0[q] >> 32));
+            uint64_t key = tok >= 0 ? make_key(sv, level, c / k, c % k) : 0;
+            if (key != 0 && sv < tau) key = 0;
+            ss.keys[nprev + c] = key;
+            ss.ctok[c] = tok;
+            ss.chash[c] = cw2[q];
+        }
+    }
+    const int ncand8 = (ncand + 7) & ~7;  // zero padding (zero keys never count)
+    for (int i = ncand + tid; i < ncand8; i += blockDim.x) ss.keys[i] = 0;
+    __syncthreads();
+    DT_STAMP(level, 7);
+    // Nonzero keys are distinct (the low word names the node), so a key's position in the
+    // descending order is the number of larger keys: one pass, no sorting network.  The
+    // count reads eight keys per step so that their LDS latencies overlap.
     int nz = 0;
-    for (int i = tid; i < P; i += blockDim.x) nz += keys[i] != 0 ? 1 : 0;
-    nz = block_sum(nz, sh);
+    for (int i = tid; i < ncand; i += blockDim.x) {
+        const uint64_t key = ss.keys[i];
+        if (key == 0) continue;
+        ++nz;
+        int rank = 0;
+        for (int m = 0; m < ncand8; m += 8) {
+            uint64_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = ss.keys[m + q];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) rank += v[q] > key ? 1 : 0;
+        }
+        if (rank < nbudget) ss.sorted[rank] = key;
+    }
+    nz = block_sum(nz, sh);  // includes a barrier: ss.sorted is complete
     const int nkept = min(nbudget, nz);
-    for (int i = tid; i < nkept; i += blockDim.x) cst64(a.skeys + (size_t)req * a.Ncap + i, keys[i]);
-    if (tid == 0) csti(a.scount + req, nkept);
-    int fnext = 0;
-    if (level < a.B) {
+    int cnt = 0;
+    if (level < a.B)
+        for (int i = tid; i < nkept; i += blockDim.x) cnt += (low_depth((uint32_t)ss.sorted[i]) == level) ? 1 : 0;
+    const int fnext = block_sum(cnt, sh);
+    // rows of the next level, allocated with one atomic
+    if (tid == 0) {
+        unsigned base = 0;
+        if (fnext > 0) {
+            uint64_t* alloc = (uint64_t*)(a.sync + kSyncAlloc) + level + 1;
+            base = (unsigned)__hip_atomic_fetch_add(alloc, (uint64_t)fnext, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        }
+        bcast[0] = (int)base;
+    }
+    for (int i = tid; i < nkept; i += blockDim.x) cst64(a.skeys + (size_t)req * Ncap + i, ss.sorted[i]);
+    if (tid == 0) {
+        csti(a.scount + req, nkept);
+        csti(a.fcount + req * (a.B + 1) + level, fnext);
+    }
+    __syncthreads();
+    const int base = bcast[0];
+    if (fnext > 0) {
+        RowRec* nrows = level_rows(a, level + 1) + base;
         for (int i = tid; i < nkept; i += blockDim.x) {
-            const uint32_t low = (uint32_t)keys[i];
+            const uint32_t low = (uint32_t)ss.sorted[i];
             if (low_depth(low) != level) continue;
             int rank = 0;
             for (int m = 0; m < nkept; ++m) {
-                const uint32_t lm = (uint32_t)keys[m];
+                const uint32_t lm = (uint32_t)ss.sorted[m];
                 if (low_depth(lm) == level && lm > low) ++rank;
             }
-            const int fi = low_fi(low), j = low_rank(low);
-            const ChildRec c = ld_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j);
+            const int c = low_fi(low) * k + low_rank(low);
+            const int tok = ss.ctok[c];
+            const float sv = key_surv(ss.sorted[i]);
+            const uint64_t hh = ss.chash[c];
             FrontEntry e;
             e.self = low;
-            e.token = c.token;
-            e.s = c.s;
+            e.token = tok;
+            e.s = sv;
             e.pad = 0;
-            e.hash = c.hash;
-            st_front(a.front + ((size_t)req * (a.B + 1) + level) * a.Ncap + rank, e);
+            e.hash = hh;
+            st_front(a.front + ((size_t)req * (a.B + 1) + level) * Ncap + rank, e);
+            RowRec* rr = nrows + rank;
+            cst64(rr, (uint64_t)(uint32_t)req | ((uint64_t)(uint32_t)rank << 32));
+            cst64((char*)rr + 8, (uint64_t)(uint32_t)tok | ((uint64_t)__float_as_uint(sv) << 32));
+            cst64((char*)rr + 16, hh);
+            cst64((char*)rr + 24, (uint64_t)(uint32_t)fnext);
         }
-        int cnt = 0;
-        for (int i = tid; i < nkept; i += blockDim.x)
-            cnt += (low_depth((uint32_t)keys[i]) == level) ? 1 : 0;
-        fnext = block_sum(cnt, sh);
     }
-    if (tid == 0) csti(a.fcount + req * (a.B + 1) + level, fnext);
-}
-
-// Lays out the parent rows of level `level + 1` from the frontier sizes fcount[.][level],
-// in request order, with the row and request counts, and clears the counters of level
-// `level` (every increment of them has happened).  One workgroup.
-__device__ __forceinline__ void release_rows(const BuildArgs& a, int level, int Tcur, int* sh) {
-    const int R = a.R, B = a.B;
-    const int per = (R + blockDim.x - 1) / blockDim.x;
-    const int r0 = threadIdx.x * per;
-    int cnt = 0, nreq = 0, f0 = 0;
-    for (int r = r0; r < r0 + per && r < R; ++r) {
-        const int f = level < B ? cldi(a.fcount + r * (B + 1) + level) : 0;
-        if (r == r0) f0 = f;
-        cnt += f;
-        nreq += f > 0 ? 1 : 0;
-    }
-    int total;
-    int off = block_exclusive_scan(cnt, sh, &total);
-    const int rtotal = block_sum(nreq, sh);
-    for (int r = r0; r < r0 + per && r < R; ++r) {
-        const int f = r == r0 ? f0 : (level < B ? cldi(a.fcount + r * (B + 1) + level) : 0);
-        for (int i = 0; i < f; ++i)
-            cst64(a.rows + off + i, (uint64_t)(uint32_t)r | ((uint64_t)(uint32_t)i << 32));
-        off += f;
-    }
-    for (int t = threadIdx.x; t < Tcur; t += blockDim.x) cst32(a.tdone + t, 0u);
-    for (int r = threadIdx.x; r < R; r += blockDim.x) cst32(a.rdone + r, 0u);
-    if (threadIdx.x == 0) {
-        cst32(a.sync + kSyncRows + level + 1, (unsigned)total);
-        cst32(a.sync + kSyncReqs + level + 1, (unsigned)rtotal);
+    publish_wg();
+    if (tid == 0) {
+        // (selects done << 48) | (requests with rows at the next level << 32) | rows: the
+        // select that completes the level learns the next level's sizes from the same atomic
+        const uint64_t inc = (1ull << 48) | ((uint64_t)(fnext > 0) << 32) | (uint64_t)fnext;
+        const uint64_t old = __hip_atomic_fetch_add((uint64_t*)(a.sync + kSyncDone) + level, inc,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t now = old + inc;
+        if ((unsigned)(now >> 48) == nreq)
+            cst64(a.sync + kSyncGen, pack_gen(level, (int)((now >> 32) & 0xFFFFu), (int)(uint32_t)now));
     }
 }
 
@@ -1133,13 +1216,20 @@ __device__ __forceinline__ void emit_request(const BuildArgs& a, int req, bool f
 // ---------------------------------------------------------------------------------------
 // Kernels.
 // ---------------------------------------------------------------------------------------
-// Round set-up (one workgroup): control words and counters, roots, budgets, status bits,
-// and the level-1 parent rows (one per request with a valid root).
-__global__ __launch_bounds__(256) void k_build_init(const BuildArgs a, int tiles) {
+// Round set-up: control words and per-level counters (all workgroups), then roots, budgets,
+// status bits and the level-1 parent rows, one per request with a valid root (workgroup 0).
+__global__ __launch_bounds__(256) void k_build_init(const BuildArgs a) {
     __shared__ int sh[256];
     const int tid = threadIdx.x;
+    {
+        const size_t nt = (size_t)(a.B + 2) * a.Tmax, nr = (size_t)(a.B + 2) * a.R;
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + tid; i < nt + nr; i += (size_t)gridDim.x * blockDim.x) {
+            if (i < nt) a.tdone[i] = 0u;
+            else a.rdone[i - nt] = 0u;
+        }
+    }
+    if (blockIdx.x != 0) return;
     for (int i = tid; i < kSyncWords; i += blockDim.x) a.sync[i] = 0u;
-    for (int t = tid; t < tiles; t += blockDim.x) a.tdone[t] = 0u;
     const int R = a.R;
     const int per = (R + blockDim.x - 1) / blockDim.x;
     const int r0 = tid * per;
@@ -1166,19 +1256,27 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a, int tiles
         a.scount[r] = 0;
         a.nbeff[r] = nb;
         a.rstat[r] = st;
-        a.rdone[r] = 0u;
         cnt += ok ? 1 : 0;
     }
     int total;
     int off = block_exclusive_scan(cnt, sh, &total);
+    RowRec* rows = level_rows(a, 1);
     for (int r = r0; r < r0 + per && r < R; ++r) {
         const int32_t root = a.root_token[r];
-        if (root >= 0 && root < a.V) a.rows[off++] = make_int2(r, 0);
+        if (root >= 0 && root < a.V) {
+            RowRec rr;
+            rr.req = r;
+            rr.fi = 0;
+            rr.token = root;
+            rr.s = 1.0f;
+            rr.hash = root_hash(a.round, r, root);
+            rr.F = 1;
+            rr.pad = 0;
+            rows[off++] = rr;
+        }
     }
-    if (tid == 0) {
-        a.sync[kSyncRows + 1] = (unsigned)total;
-        a.sync[kSyncReqs + 1] = (unsigned)total;
-    }
+    __syncthreads();  // sync[] is cleared before the generation word is written
+    if (tid == 0) *(uint64_t*)(a.sync + kSyncGen) = pack_gen(0, total, total);
 }
 
 // The level loop.  The grid is the kernel's resident capacity, launched plainly: workgroups
@@ -1193,22 +1291,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     bool failed = false;
     DT_STAMP(0, 0);
+    if (tid < kMaxB + 2) sm.lrows[tid] = 0;  // levels never reached expand no rows
     for (int level = 1;; ++level) {
-        // the previous level's selects are complete once the generation reaches level - 1
-        if (!wait_at_least(a.sync, a.sync + kSyncGen, (unsigned)(level - 1), sm.bcast)) {
+        // the previous level's selects are complete once the generation reaches level - 1;
+        // the generation word also carries this level's row and request counts
+        uint64_t gen;
+        if (!wait_gen(a.sync, level - 1, sm.bcast, &gen)) {
             failed = true;
             break;
         }
         if (level > a.B) break;
         DT_STAMP(level, 0);
-        const int M = (int)cld32(a.sync + kSyncRows + level);
+        const int M = (int)(gen >> 32);
+        const unsigned nreq = ((uint32_t)gen) >> 8;
+        if (tid == 0) sm.lrows[level] = M;
         if (M == 0) break;
         // tile mode (<= kTileRows rows, or float32 heads) or group mode (kGroupRows-row groups)
         const bool grp_mode = HEAD_BF16 && L_BF16 && (a.V & 7) == 0 && M > kTileRows;
         const int GR = grp_mode ? kGroupRows : kTileRows;
         const int T = (M + GR - 1) / GR;
         const int S = splits_for(T, (int)gridDim.x, NB);
-        const unsigned nreq = cld32(a.sync + kSyncReqs + level);
+        unsigned* tdone = a.tdone + (size_t)level * a.Tmax;
         // item i runs on workgroup i mod G.  Workgroups are dealt to the 8 XCDs round-robin,
         // so when S and G are multiples of 8 split j of every row tile runs on one XCD, and a
         // W block read for one tile is an L2 hit for the others.
@@ -1220,42 +1323,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
                 expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
             }
             publish_wg();
-            if (tid == 0) cadd32(a.tdone + item / S, 1u);
+            if (tid == 0) cadd32(tdone + item / S, 1u);
         }
         DT_STAMP(level, 2);
         bool first_task = true;
-        // merge tasks: parent rows in order, each once its tile's splits are all in
-        for (;;) {
-            if (tid == 0) sm.bcast[1] = (int)cadd32(a.sync + kSyncTask + level, 1u);
-            __syncthreads();
-            const int m = sm.bcast[1];
-            __syncthreads();
-            if (m >= M) break;
-            if (!wait_at_least(a.sync, a.tdone + m / GR, (unsigned)S, sm.bcast)) {
+        // merges: parent row m on workgroup m mod G, once all splits of its tile are in
+        for (int m = blockIdx.x; m < M; m += gridDim.x) {
+            if (!wait_at_least(a.sync, tdone + m / GR, (unsigned)S, sm.bcast)) {
                 failed = true;
                 break;
             }
             if (first_task) DT_STAMP(level, 6);
             first_task = false;
-            const int req = merge_row<KT>(a, level, S, m, sm);
+            int req, F;
+            merge_row<KT>(a, level, S, m, sm, &req, &F);
             publish_wg();
-            if (tid == 0) {
-                const int F = cldi(a.fcount + req * (a.B + 1) + level - 1);
-                sm.bcast[2] = (cadd32(a.rdone + req, 1u) + 1u == (unsigned)F) ? 1 : 0;
-            }
+            DT_STAMP(level, 5);
+            if (tid == 0)
+                sm.bcast[2] = (cadd32(a.rdone + (size_t)level * a.R + req, 1u) + 1u == (unsigned)F) ? 1 : 0;
             __syncthreads();
             if (sm.bcast[2]) {
-                select_request(a, level, req, sm.u.keys, sm.sh);
-                publish_wg();
+                select_request(a, level, req, F, nreq, sm.u.sel, sm.sh, sm.bcast + 3);
                 DT_STAMP(level, 4);
-                if (tid == 0) sm.bcast[3] = (cadd32(a.sync + kSyncDone + level, 1u) + 1u == nreq) ? 1 : 0;
-                __syncthreads();
-                if (sm.bcast[3]) {
-                    release_rows(a, level, T, sm.sh);
-                    publish_wg();
-                    if (tid == 0) cst32(a.sync + kSyncGen, (unsigned)level);
-                    DT_STAMP(level, 5);
-                }
             }
             __syncthreads();
         }
@@ -1266,9 +1355,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     if (failed) cst32(a.sync + kSyncErr, 1u);
     for (int req = blockIdx.x; req < a.R; req += gridDim.x)
         emit_request(a, req, failed || cld32(a.sync + kSyncErr) != 0u, sm.u.em);
-    if (blockIdx.x == 0 && a.out.level_rows)
-        for (int l = tid; l < a.B; l += blockDim.x)
-            a.out.level_rows[l] = (int)cld32(a.sync + kSyncRows + l + 1);
+    if (blockIdx.x == 0 && a.out.level_rows) {
+        __syncthreads();
+        for (int l = tid; l < a.B; l += blockDim.x) a.out.level_rows[l] = sm.lrows[l + 1];
+    }
     DT_STAMP(kTraceLevels - 1, 1);
 }
 
@@ -1305,7 +1395,13 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     const void* f = (const void*)k_build<KT, SAMPLE, HEAD_BF16, L_BF16>;
     const int G = resident_grid(f);
     if (G < 1) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(k_build_init, dim3(1), dim3(256), 0, st, a, max_tiles(a.R, a.Ncap));
+    {
+        // enough workgroups to clear the per-level counters in a few stores per thread
+        const size_t words = (size_t)(a.B + 2) * (a.Tmax + a.R);
+        int g = (int)((words + 256 * 16 - 1) / (256 * 16));
+        g = g < 1 ? 1 : (g > 256 ? 256 : g);
+        hipLaunchKernelGGL(k_build_init, dim3(g), dim3(256), 0, st, a);
+    }
     if (a.timing_hook) a.timing_hook(st, 0);
     // a plain launch: the loop needs no co-residency guarantee (see k_build), and a
     // cooperative launch costs about 18 us more per round on this stack

@@ -31,7 +31,8 @@ struct alignas(8) FrontEntry {
     uint64_t hash;
 };
 
-// A generated child.
+// A generated child (also what the select reads to rank it: token and survival in the first
+// word, the random-stream hash in the third).
 struct alignas(8) ChildRec {
     int32_t token;
     float s;
@@ -40,16 +41,27 @@ struct alignas(8) ChildRec {
     uint64_t hash;
 };
 
+// A parent row of a level: written by the select that kept the node (by k_build_init for the
+// roots) and read by the expansion (token, hash, request) and the merge (survival, hash, F).
+struct alignas(16) RowRec {
+    int32_t req;
+    int32_t fi;     // the node's index in the request's frontier at this level (canonical)
+    int32_t token;
+    float s;        // the node's survival
+    uint64_t hash;  // the node's random stream
+    int32_t F;      // parent rows of this request at this level
+    int32_t pad;
+};
+
 // Offsets (bytes) of every workspace region; sizes depend only on the parameters.
 struct Layout {
-    size_t rows;      // int2 [R*Ncap]: (request, frontier index) of every parent row
+    size_t rows;      // RowRec [2][R*Ncap]: parent rows of a level (double-buffered by level)
     size_t sync;      // unsigned [kSyncWords]: generation, error flag, per-level counters
-    size_t tdone;     // unsigned [tiles]: expansion items finished per row tile
-    size_t rdone;     // unsigned [R]: parent rows merged per request
+    size_t tdone;     // unsigned [B+2][tiles]: expansion items finished per level and row tile
+    size_t rdone;     // unsigned [B+2][R]: parent rows merged per level and request
     size_t front;     // FrontEntry [R][B+1][Ncap]
     size_t fcount;    // int [R][B+1]: frontier size per level (level 0 = the root)
     size_t arena;     // ChildRec [R][B][Ncap][k]
-    size_t ckeys;     // u64 [R][Ncap*k]: keys of the children generated at this level
     size_t skeys;     // u64 [R][Ncap]: the selected set, best first
     size_t scount;    // int [R]
     size_t nbeff;     // int [R]: budget after clamping
@@ -60,7 +72,7 @@ struct Layout {
     size_t vstate;    // VState [R]
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
     size_t gpart;     // (float, int) [R][gsplits]: greedy verify, split argmax of the root rows
-    size_t trace;     // u64 [kMaxGrid][kTraceLevels][8]: phase timestamps (DT_TRACE builds only)
+    size_t trace;     // u64 [kMaxGrid][kTraceLevels][16]: phase timestamps (DT_TRACE builds only)
     size_t total;
     int G;            // largest grid of the construction kernel (sizes the partial records)
     int NC;           // vocabulary chunks of 128 columns
@@ -85,16 +97,19 @@ struct alignas(8) VState {
 
 // Control words at the start of the workspace.  Per-level words are indexed by the level
 // (1..B+1) so that a late workgroup never reads the next level's value.
-constexpr int kSyncGen = 0;        // last level whose select is complete (0 after set-up)
-constexpr int kSyncErr = 1;        // set when a bounded wait gives up
-constexpr int kSyncRows = 8;       // [level]: parent rows expanded at that level
-constexpr int kSyncReqs = 48;      // [level]: requests with at least one parent row
-constexpr int kSyncTask = 88;      // [level]: merge-task counter
-constexpr int kSyncDone = 128;     // [level]: requests whose select is done
-constexpr int kSyncWords = 192;
+constexpr int kSyncGen = 0;     // u64: (parent rows of the next level << 32) | (requests with rows
+                                // at the next level << 8) | last level whose selects are done
+constexpr int kSyncErr = 2;     // set when a bounded wait gives up
+constexpr int kSyncAlloc = 8;   // u64 [level]: rows allocated for that level
+constexpr int kSyncDone = 80;   // u64 [level]: (selects done << 48) | (requests with rows at
+                                // the next level << 32) | rows of the next level
+constexpr int kSyncWords = 160;
+__host__ __device__ constexpr uint64_t pack_gen(int level, int nreq, int rows) {
+    return ((uint64_t)(uint32_t)rows << 32) | ((uint64_t)(uint32_t)nreq << 8) | (uint64_t)level;
+}
 
 // Phase timestamps of the construction kernel, written only by builds compiled with
-// DT_TRACE: per workgroup and level, eight wall-clock stamps (slot meanings at DT_STAMP).
+// DT_TRACE: per workgroup and level, sixteen wall-clock stamps (slot meanings at DT_STAMP).
 constexpr int kTraceLevels = 40;
 
 // Arguments of the tree-construction kernels (passed by value).
@@ -109,11 +124,10 @@ struct BuildArgs {
     unsigned* sync;
     unsigned* tdone;
     unsigned* rdone;
-    int2* rows;
+    RowRec* rows;
     FrontEntry* front;
     int* fcount;
     ChildRec* arena;
-    uint64_t* ckeys;
     uint64_t* skeys;
     int* scount;
     int* nbeff;
@@ -122,6 +136,7 @@ struct BuildArgs {
     dt_tree out;
     uint64_t* trace;  // phase timestamps (DT_TRACE builds only; null otherwise)
     int R, B, k, V, r, Ncap, NC;
+    int Tmax;  // row tiles of kTileRows for R * Ncap rows (stride of tdone per level)
     float y2scale;  // log2(e) / T' : converts z to log2-unit tempered logits
     float invT;     // 1 / T' (sample ranking key)
     uint32_t seed_lo, seed_hi, round;

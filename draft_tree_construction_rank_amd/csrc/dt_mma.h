@@ -149,7 +149,9 @@ __device__ __forceinline__ void mma_chunk(const void* Wt, int V, int r, int col0
 __device__ __forceinline__ void load_wfrag(const void* Wt, int V, int r, int c0, bf16x8 (&wf)[16]) {
     const int lane = threadIdx.x & 63;
     const int col = c0 + (lane & 31);
-    const int khalf = (lane >> 5) * 8;
+    // recomputed at every call: hoisted out of the persistent loop, the sixteen offsets were
+    // spilled and reloaded one round trip at a time
+    const int khalf = (lane >> 5) * 8 + opaque_zero();
     const uint16_t* wrow = (const uint16_t*)Wt + (size_t)(col < V ? col : V - 1) * r;
 #pragma unroll
     for (int s = 0; s < 16; ++s) {

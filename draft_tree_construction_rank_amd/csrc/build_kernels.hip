@@ -54,10 +54,21 @@ constexpr int kThreads = 64 * kWaves;
 // ---------------------------------------------------------------------------------------
 // Workgroup helpers.
 // ---------------------------------------------------------------------------------------
-// Exclusive prefix sum over the workgroup: a shuffle scan inside each wavefront, then the
-// wavefront totals through LDS (two barriers).  sh needs one int per wavefront.
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for every global load,
+// store and atomic this wavefront has in flight (one memory round trip after a store);
+// exchanges of global data between workgroups use publish_wg() instead.
+__device__ __forceinline__ void lds_sync() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Exclusive prefix sum over a workgroup of NW wavefronts: a shuffle scan inside each
+// wavefront, then the wavefront totals through LDS (two barriers).  sh needs NW ints.
+template <int NW = kWaves>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) {
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     int x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -65,15 +76,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* sh, int* total) 
         if (lane >= off) x += y;
     }
     if (lane == 63) sh[w] = x;
-    __syncthreads();
+    lds_sync();
     int base = 0, tot = 0;
-    for (int i = 0; i < nw; ++i) {
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
         const int si = sh[i];
         base += i < w ? si : 0;
         tot += si;
     }
     if (total) *total = tot;
-    __syncthreads();  // sh is free for the caller again
+    lds_sync();  // sh is free for the caller again
     return base + x - v;
 }
 
@@ -109,9 +121,9 @@ __device__ __forceinline__ bool wait_at_least(unsigned* sync, const unsigned* p,
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         bcast[0] = ok;
     }
-    __syncthreads();
+    lds_sync();
     const bool ok = bcast[0] != 0;
-    __syncthreads();
+    lds_sync();
     return ok;
 }
 
@@ -139,10 +151,10 @@ __device__ __forceinline__ bool wait_gen(unsigned* sync, int level, int* bcast, 
         bcast[1] = (int)(uint32_t)g;
         bcast[2] = (int)(uint32_t)(g >> 32);
     }
-    __syncthreads();
+    lds_sync();
     const bool ok = bcast[0] != 0;
     *gen = (uint64_t)(uint32_t)bcast[1] | ((uint64_t)(uint32_t)bcast[2] << 32);
-    __syncthreads();
+    lds_sync();
     return ok;
 }
 
@@ -168,11 +180,11 @@ __device__ __forceinline__ RowRec* level_rows(const BuildArgs& a, int level) {
 // Staging of one request's emit (see emit_request).
 struct EmitSmem {
     uint64_t keys[kMaxNcap];
-    uint32_t lowc[kMaxNcap];
+    uint32_t lowc[kMaxNcap];  // canonical order (zero-padded to a multiple of 8)
     int parc[kMaxNcap];
     int fcnt[kMaxB + 1];
     int n;
-    uint32_t fself[kMaxB * kMaxNcap];  // front[d][m].self for d = 1..B-1
+    uint32_t fself[kMaxB * kMaxNcap + 8];  // front[d][m].self for d = 1..B-1 (0 = no node)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -213,6 +225,7 @@ struct BuildSmem {
     int sh[256];
     int bcast[4];
     int lrows[kMaxB + 2];  // parent rows of each level (as read from the generation word)
+    uint64_t mchild[2][kMaxK];  // children of the row just merged (see select_request)
 };
 
 // ---------------------------------------------------------------------------------------
@@ -537,13 +550,13 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         sm.hash[tid] = hh;
         sm.rkth[tid] = 0;
     }
-    __syncthreads();
+    lds_sync();
     DT_STAMP(level, 8);
     if constexpr (HEAD_BF16)
         load_a_tile<true, kThreads>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, sm.u.sA, nullptr);
     else
         load_a_tile<false, kThreads>(a.U, a.r, nrows, [&](int row) { return sm.tok[row]; }, nullptr, sm.u.sAf);
-    __syncthreads();
+    lds_sync();
     // The first W block is loaded only once the parent rows are staged: issued earlier, the
     // whole grid's first blocks (32 MB) queue ahead of the set-up loads.
     if constexpr (HEAD_BF16) {
@@ -607,12 +620,12 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         s1.merge_xor(32);
         t1.merge_xor(32);
     }
-    __syncthreads();  // the lists below overwrite the U tile
+    lds_sync();  // the lists below overwrite the U tile
     if (h == 0) {
         put_list<KT>(sm.u.xrec[wave][p0], t0, s0);
         if (two) put_list<KT>(sm.u.xrec[wave][32 + p0], t1, s1);
     }
-    __syncthreads();
+    lds_sync();
     {
         // kWaves consecutive threads per parent row combine the wavefronts' lists
         const int row = tid / kWaves, w = tid % kWaves;
@@ -638,7 +651,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
                                                __float_as_uint(v[4 * c + 2]), __float_as_uint(v[4 * c + 3])));
         }
     }
-    __syncthreads();
+    lds_sync();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -816,7 +829,7 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
     }
     if (h == 0) sm.glbase[rl] = lb;
     DT_STAMP(level, 1);
-    __syncthreads();
+    lds_sync();
     const GroupCopy gc = group_copy_setup<KT>(a, sm);
     // prologue: blocks b_beg .. b_beg + kStages - 2 in flight
 #pragma unroll
@@ -885,7 +898,7 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
                                            __float_as_uint(v[4 * c + 2]), __float_as_uint(v[4 * c + 3])));
     }
     wait_vm();
-    __syncthreads();  // no copy into the staging ring is left in flight
+    lds_sync();  // no copy into the staging ring is left in flight
 }
 
 // ---------------------------------------------------------------------------------------
@@ -942,13 +955,15 @@ __device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, 
     *F_out = (int)(uint32_t)r3;
     const int lvl = level - 1;
     if (tid < S) merge_fetched<KT>(w0, top, acc);
+    DT_STAMP(level, 9);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         acc.merge_xor(off);
         top.merge_xor(off);
     }
     if (lane == 0) put_list<KT>(sm.mrec[wave], top, acc);
-    __syncthreads();
+    lds_sync();
+    DT_STAMP(level, 10);
     if (wave == 0) {
         get_list<KT>(sm.mrec[lane % kWaves], top, acc);
 #pragma unroll
@@ -976,6 +991,8 @@ __device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, 
                 c.pad = 0;
                 c.hash = child_hash(par_hash, c.token);
                 st_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j, c);
+                sm.mchild[0][j] = (uint64_t)(uint32_t)c.token | ((uint64_t)__float_as_uint(c.s) << 32);
+                sm.mchild[1][j] = c.hash;
             }
         }
     }
@@ -992,8 +1009,11 @@ __device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, 
 // generation word.
 // ---------------------------------------------------------------------------------------
 
+// `mine` (or null): the children of a single-row request, just merged by this workgroup and
+// still in LDS as (token | survival << 32, hash) pairs.
 __device__ __forceinline__ void select_request(const BuildArgs& a, int level, int req, int F,
-                                               unsigned nreq, SelSmem& ss, int* sh, int* bcast) {
+                                               unsigned nreq, SelSmem& ss, int* sh, int* bcast,
+                                               const uint64_t (*mine)[kMaxK]) {
     const int tid = threadIdx.x;
     const int lvl = level - 1;
     const int Ncap = a.Ncap, k = a.k;
@@ -1012,8 +1032,13 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
         cw2[q] = 0;
         if (i < Ncap) kk[q] = cld64(a.skeys + (size_t)req * Ncap + i);
         else if (i < Ncap + nchild) {
-            cw0[q] = cld64(crow + (i - Ncap));
-            cw2[q] = cld64((const char*)(crow + (i - Ncap)) + 16);
+            if (mine) {
+                cw0[q] = mine[0][i - Ncap];
+                cw2[q] = mine[1][i - Ncap];
+            } else {
+                cw0[q] = cld64(crow + (i - Ncap));
+                cw2[q] = cld64((const char*)(crow + (i - Ncap)) + 16);
+            }
         }
     }
     const int ncand = nprev + nchild;
@@ -1035,16 +1060,17 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
     }
     const int ncand8 = (ncand + 7) & ~7;  // zero padding (zero keys never count)
     for (int i = ncand + tid; i < ncand8; i += blockDim.x) ss.keys[i] = 0;
-    __syncthreads();
+    lds_sync();
     DT_STAMP(level, 7);
     // Nonzero keys are distinct (the low word names the node), so a key's position in the
     // descending order is the number of larger keys: one pass, no sorting network.  The
     // count reads eight keys per step so that their LDS latencies overlap.
-    int nz = 0;
+    // A candidate is kept iff its rank is below the budget; one workgroup sum counts the kept
+    // nodes (low half) and the kept nodes of this level's depth, the next frontier (high half).
+    int cnt = 0;
     for (int i = tid; i < ncand; i += blockDim.x) {
         const uint64_t key = ss.keys[i];
         if (key == 0) continue;
-        ++nz;
         int rank = 0;
         for (int m = 0; m < ncand8; m += 8) {
             uint64_t v[8];
@@ -1053,18 +1079,21 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
 #pragma unroll
             for (int q = 0; q < 8; ++q) rank += v[q] > key ? 1 : 0;
         }
-        if (rank < nbudget) ss.sorted[rank] = key;
+        if (rank < nbudget) {
+            ss.sorted[rank] = key;
+            cnt += 1 + ((level < a.B && low_depth((uint32_t)key) == level) ? (1 << 16) : 0);
+        }
     }
-    nz = block_sum(nz, sh);  // includes a barrier: ss.sorted is complete
-    const int nkept = min(nbudget, nz);
-    int cnt = 0;
-    if (level < a.B)
-        for (int i = tid; i < nkept; i += blockDim.x) cnt += (low_depth((uint32_t)ss.sorted[i]) == level) ? 1 : 0;
-    const int fnext = block_sum(cnt, sh);
+    cnt = block_sum(cnt, sh);  // includes barriers: ss.sorted is complete
+    const int nkept = cnt & 0xFFFF;
+    const int fnext = cnt >> 16;
+    const int nk8 = (nkept + 7) & ~7;
+    for (int i = nkept + tid; i < nk8; i += blockDim.x) ss.sorted[i] = 0;  // depth 63: never counted
+    lds_sync();
     // rows of the next level, allocated with one atomic
     if (tid == 0) {
         unsigned base = 0;
-        if (fnext > 0) {
+        if (fnext > 0 && a.R > 1) {  // a single request's rows always start at 0
             uint64_t* alloc = (uint64_t*)(a.sync + kSyncAlloc) + level + 1;
             base = (unsigned)__hip_atomic_fetch_add(alloc, (uint64_t)fnext, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
@@ -1076,7 +1105,7 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
         csti(a.scount + req, nkept);
         csti(a.fcount + req * (a.B + 1) + level, fnext);
     }
-    __syncthreads();
+    lds_sync();
     const int base = bcast[0];
     if (fnext > 0) {
         RowRec* nrows = level_rows(a, level + 1) + base;
@@ -1084,9 +1113,12 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
             const uint32_t low = (uint32_t)ss.sorted[i];
             if (low_depth(low) != level) continue;
             int rank = 0;
-            for (int m = 0; m < nkept; ++m) {
-                const uint32_t lm = (uint32_t)ss.sorted[m];
-                if (low_depth(lm) == level && lm > low) ++rank;
+            for (int m = 0; m < nk8; m += 8) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t lm = (uint32_t)ss.sorted[m + q];
+                    rank += (low_depth(lm) == level && lm > low) ? 1 : 0;
+                }
             }
             const int c = low_fi(low) * k + low_rank(low);
             const int tok = ss.ctok[c];
@@ -1107,7 +1139,10 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
         }
     }
     publish_wg();
-    if (tid == 0) {
+    if (tid == 0 && a.R == 1) {
+        // a single request's select is the level's last
+        cst64(a.sync + kSyncGen, pack_gen(level, fnext > 0 ? 1 : 0, fnext));
+    } else if (tid == 0) {
         // (selects done << 48) | (requests with rows at the next level << 32) | rows: the
         // select that completes the level learns the next level's sizes from the same atomic
         const uint64_t inc = (1ull << 48) | ((uint64_t)(fnext > 0) << 32) | (uint64_t)fnext;
@@ -1130,53 +1165,100 @@ __device__ __forceinline__ void emit_request(const BuildArgs& a, int req, bool f
                                              EmitSmem& e) {
     const int tid = threadIdx.x;
     const int B = a.B, k = a.k, Ncap = a.Ncap;
-    if (tid < Ncap) e.keys[tid] = cld64(a.skeys + (size_t)req * Ncap + tid);
-    if (tid <= B) e.fcnt[tid] = failed ? 0 : cldi(a.fcount + req * (B + 1) + tid);
-    if (tid == 0) e.n = failed ? 0 : cldi(a.scount + req);
-    __syncthreads();
-    for (int i = tid; i < (B - 1) * Ncap; i += blockDim.x) {
-        const int d = 1 + i / Ncap, m = i % Ncap;
-        if (m < e.fcnt[d])
-            e.fself[i] = (uint32_t)cld64(a.front + ((size_t)req * (B + 1) + d) * Ncap + m);
+    // One round of loads: the error flag, the kept keys and their count, the frontier sizes
+    // and every frontier identity (invalid slots are zeroed once the sizes are in LDS).  A
+    // failed round (this workgroup's or another's wait gave up) emits empty trees.
+    const uint32_t err = cld32(a.sync + kSyncErr);
+    const int rst = cldi(a.rstat + req);
+    int n = cldi(a.scount + req);
+    uint64_t key = 0;
+    if (tid < Ncap) key = cld64(a.skeys + (size_t)req * Ncap + tid);
+    int fc = 0;
+    if (tid <= B) fc = cldi(a.fcount + req * (B + 1) + tid);
+    constexpr int kFs = (kMaxB * kMaxNcap + kThreads - 1) / kThreads;
+    uint32_t fs[kFs];
+#pragma unroll
+    for (int q = 0; q < kFs; ++q) {
+        const int i = tid + q * kThreads;
+        fs[q] = i < (B - 1) * Ncap
+                    ? (uint32_t)cld64(a.front + ((size_t)req * (B + 1) + 1 + i / Ncap) * Ncap + i % Ncap)
+                    : 0u;
     }
-    const int n = e.n;
+    failed = failed || err != 0u;
+    n = failed ? 0 : n;
+    if (tid < kMaxNcap) e.keys[tid] = tid < n ? key : 0;  // zero padding: never counted
+    if (tid <= B) e.fcnt[tid] = failed ? 0 : fc;
+    lds_sync();
+    DT_STAMP(kTraceLevels - 2, 0);
+#pragma unroll
+    for (int q = 0; q < kFs; ++q) {
+        const int i = tid + q * kThreads;
+        if (i < (B - 1) * Ncap) e.fself[i] = (i % Ncap) < e.fcnt[1 + i / Ncap] ? fs[q] : 0u;
+    }
+    // The LDS scans below read eight entries per step so that their latencies overlap; the
+    // arrays are zero-padded to a multiple of eight (a node's low word is never zero).
+    const int n8 = (n + 7) & ~7;
     if (tid < n) {
         const uint32_t mylow = (uint32_t)e.keys[tid];
         int canon = 0;
-        for (int m = 0; m < n; ++m) canon += ((uint32_t)e.keys[m] > mylow) ? 1 : 0;
+        for (int m = 0; m < n8; m += 8) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) canon += ((uint32_t)e.keys[m + q] > mylow) ? 1 : 0;
+        }
         e.lowc[canon] = mylow;
+    } else if (tid < n8) {
+        e.lowc[tid] = 0u;
     }
-    __syncthreads();
+    lds_sync();
+    DT_STAMP(kTraceLevels - 2, 1);
     const size_t ob = (size_t)req * Ncap;
     int par = -2;
     if (tid < n) {
         const uint32_t low = e.lowc[tid];
         const int depth = low_depth(low);
         const int fi = low_fi(low), j = low_rank(low);
-        const ChildRec c = ld_child(a.arena + (((size_t)req * B + (depth - 1)) * Ncap + fi) * k + j);
         par = -1;
         if (depth > 1) {
             const uint32_t pid = e.fself[(depth - 2) * Ncap + fi];
-            for (int m = 0; m < n; ++m)
-                if (e.lowc[m] == pid) par = m;
+            for (int m = 0; m < n8; m += 8) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) par = (e.lowc[m + q] == pid) ? m + q : par;
+            }
         }
         int slot = -1;
         if (depth < B) {
             const int F = e.fcnt[depth];
-            for (int m = 0; m < F; ++m)
-                if (e.fself[(depth - 1) * Ncap + m] == low) slot = m;
+            const uint32_t* row = e.fself + (depth - 1) * Ncap;
+            for (int m = 0; m < F; m += 8) {
+                uint32_t v[8];  // read unconditionally (padded row), then compared
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = row[m + q];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) slot = (v[q] == low && m + q < F) ? m + q : slot;
+            }
         }
+        // The candidate row and the node's record are loaded together, unconditionally (from
+        // clamped addresses inside the arena), before any store.
+        const ChildRec* crow = a.arena + (((size_t)req * B + (slot >= 0 ? depth : 0)) * Ncap + (slot >= 0 ? slot : 0)) * k;
+        uint64_t cw[kMaxK];
+#pragma unroll
+        for (int jj = 0; jj < kMaxK; ++jj) cw[jj] = cld64(crow + (jj < k ? jj : k - 1));
+        const ChildRec c = ld_child(a.arena + (((size_t)req * B + (depth - 1)) * Ncap + fi) * k + j);
+        int cv[kMaxK];
+#pragma unroll
+        for (int jj = 0; jj < kMaxK; ++jj) cv[jj] = slot >= 0 ? (int)(uint32_t)cw[jj] : -1;
         a.out.token[ob + tid] = c.token;
         a.out.depth[ob + tid] = (uint8_t)depth;
         a.out.surv[ob + tid] = c.s;
         a.out.logq[ob + tid] = c.logq;
         const size_t cb = ((size_t)req * (Ncap + 1) + tid + 1) * k;
-        const ChildRec* crow = a.arena + (((size_t)req * B + depth) * Ncap + (slot >= 0 ? slot : 0)) * k;
-        for (int jj = 0; jj < k; ++jj)
-            a.out.cand[cb + jj] = slot >= 0 ? (int)(uint32_t)cld64(crow + jj) : -1;
+#pragma unroll
+        for (int jj = 0; jj < kMaxK; ++jj)
+            if (jj < k) a.out.cand[cb + jj] = cv[jj];
     }
     if (tid < kMaxNcap) e.parc[tid] = par;
-    __syncthreads();
+    lds_sync();
+    DT_STAMP(kTraceLevels - 2, 2);
     if (tid < n) {
         uint64_t m = 0;
         int x = tid;
@@ -1203,14 +1285,14 @@ __device__ __forceinline__ void emit_request(const BuildArgs& a, int req, bool f
     }
     if (tid == 0) {
         a.out.n_nodes[req] = n;
-        a.out.status[req] = cldi(a.rstat + req) | (failed ? DT_REQ_SYNC_TIMEOUT : 0);
+        a.out.status[req] = rst | (failed ? DT_REQ_SYNC_TIMEOUT : 0);
         if (a.out.n_expand) {
             int ex = 0;
             for (int l = 0; l < B; ++l) ex += e.fcnt[l];
             a.out.n_expand[req] = ex;
         }
     }
-    __syncthreads();
+    lds_sync();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1259,7 +1341,7 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a) {
         cnt += ok ? 1 : 0;
     }
     int total;
-    int off = block_exclusive_scan(cnt, sh, &total);
+    int off = block_exclusive_scan<4>(cnt, sh, &total);
     RowRec* rows = level_rows(a, 1);
     for (int r = r0; r < r0 + per && r < R; ++r) {
         const int32_t root = a.root_token[r];
@@ -1337,16 +1419,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
             first_task = false;
             int req, F;
             merge_row<KT>(a, level, S, m, sm, &req, &F);
-            publish_wg();
-            DT_STAMP(level, 5);
-            if (tid == 0)
-                sm.bcast[2] = (cadd32(a.rdone + (size_t)level * a.R + req, 1u) + 1u == (unsigned)F) ? 1 : 0;
-            __syncthreads();
-            if (sm.bcast[2]) {
-                select_request(a, level, req, F, nreq, sm.u.sel, sm.sh, sm.bcast + 3);
+            if (F == 1) {
+                // the request's only row: its select follows at once, with the children from
+                // LDS (its closing publish also covers the child records)
+                lds_sync();
+                DT_STAMP(level, 5);
+                select_request(a, level, req, F, nreq, sm.u.sel, sm.sh, sm.bcast + 3, sm.mchild);
                 DT_STAMP(level, 4);
+            } else {
+                publish_wg();
+                DT_STAMP(level, 5);
+                if (tid == 0)
+                    sm.bcast[2] = (cadd32(a.rdone + (size_t)level * a.R + req, 1u) + 1u == (unsigned)F) ? 1 : 0;
+                lds_sync();
+                if (sm.bcast[2]) {
+                    select_request(a, level, req, F, nreq, sm.u.sel, sm.sh, sm.bcast + 3, nullptr);
+                    DT_STAMP(level, 4);
+                }
             }
-            __syncthreads();
+            lds_sync();
         }
         DT_STAMP(level, 3);
         if (failed) break;
@@ -1354,9 +1445,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     DT_STAMP(kTraceLevels - 1, 0);
     if (failed) cst32(a.sync + kSyncErr, 1u);
     for (int req = blockIdx.x; req < a.R; req += gridDim.x)
-        emit_request(a, req, failed || cld32(a.sync + kSyncErr) != 0u, sm.u.em);
+        emit_request(a, req, failed, sm.u.em);
     if (blockIdx.x == 0 && a.out.level_rows) {
-        __syncthreads();
+        lds_sync();
         for (int l = tid; l < a.B; l += blockDim.x) a.out.level_rows[l] = sm.lrows[l + 1];
     }
     DT_STAMP(kTraceLevels - 1, 1);

@@ -59,6 +59,20 @@ def _greedy_case(rt, inst, rows=None, margin=None):
     return inst, ref, got, gv
 
 
+def _check_expansions(inst, got, rows):
+    """Expansion counts: per request equal to the oracle's level-synchronous build (the same
+    schedule: every frontier node kept at a level is expanded at the next), and the per-level
+    row counts add up to them and are zero past the last level reached."""
+    lref = oracle.build_tree(inst, requests=rows, method=1)
+    assert np.array_equal(lref["n_expand"], got["n_expand"][rows]), (lref["n_expand"], got["n_expand"][rows])
+    lr = got["level_rows"]
+    assert int(lr.sum()) == int(got["n_expand"].sum())
+    used = np.nonzero(lr)[0]
+    if len(used):
+        last = int(used.max())
+        assert (lr[:last + 1] > 0).all() and (lr[last + 1:] == 0).all(), lr
+
+
 def _one_request(inst, rq):
     """View of request rq alone (for target generation, which is keyed by request)."""
     import dataclasses
@@ -88,7 +102,8 @@ def test_small_instances(rt, cfg):
     tau = c.pop("tau", 0.0)
     inst = instance("tiny", strong=True, cal="monotone", rho=0.5, **c)
     inst.tau = np.full(inst.R, tau, np.float32)
-    _greedy_case(rt, inst, margin=STRESS_MARGIN)
+    inst, ref, got, _ = _greedy_case(rt, inst, margin=STRESS_MARGIN)
+    _check_expansions(inst, got, list(range(inst.R)))
 
 
 def test_tiny_config(rt):
@@ -101,7 +116,8 @@ def test_b7_config(rt):
 
 @pytest.mark.parametrize("strong", [False, True])
 def test_b16_headline(rt, strong):
-    _greedy_case(rt, instance("b16", strong=strong))
+    inst, ref, got, _ = _greedy_case(rt, instance("b16", strong=strong))
+    _check_expansions(inst, got, [0])
 
 
 def test_b16_sharp_peaks(rt):
@@ -129,7 +145,8 @@ def test_b16_sweep(rt, k, N):
 def test_batched_config(rt, tau):
     inst = instance("batched", tau=tau)
     rows = [0, 17, 38, 63] if tau > 0 else [5, 40]
-    _greedy_case(rt, inst, rows=rows)
+    inst, ref, got, _ = _greedy_case(rt, inst, rows=rows)
+    _check_expansions(inst, got, rows)
 
 
 # ------------------------------------------------------------------ edge cases -------------

@@ -146,6 +146,36 @@ def build_latency(inst, torch, rt, steps=30, warmup=5):
     return s.elapsed_time(e) * 1e3 / steps
 
 
+def sample_round_us(torch, rt, inputs, temperature, steps=20, warmup=3):
+    """Microseconds per lossless-sampling round on the sample workload (R=32, B=16, k=4,
+    N=64, V=151936): tree_build in sample mode (Gumbel-top-k siblings) followed by
+    tree_verify_sample (recursive rejection) against rho=0.7 targets; also the two parts."""
+    inst = inputs.make_instance("sample", temperature=temperature)
+    d = rt.to_device(inst, "cuda")
+    rnd = rt.Round(inst)
+    rnd.build(d)
+    torch.cuda.synchronize()
+    tgt = gpu_targets(inst, rnd.tree, inst.rho, 4321, torch)
+    for _ in range(warmup):
+        rnd.build(d)
+        rnd.verify_sample(d, tgt)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tb = tv = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        rnd.build(d)
+        ev[1].record()
+        rnd.verify_sample(d, tgt)
+        ev[2].record()
+        torch.cuda.synchronize()
+        tb += ev[0].elapsed_time(ev[1])
+        tv += ev[1].elapsed_time(ev[2])
+    acc = float(rnd.vout["accept_len"].float().mean())
+    return {"round_us": round((tb + tv) * 1e3 / steps, 2), "build_us": round(tb * 1e3 / steps, 2),
+            "verify_us": round(tv * 1e3 / steps, 2), "mean_accept_len": round(acc, 3)}
+
+
 def cpu_baseline(inst, tau, res, budget_s=20.0):
     """The oracle, as it stands, on a bounded sample: build + greedy verify of the first
     requests of the same workload until ~budget_s of CPU time (single thread)."""
@@ -246,6 +276,7 @@ def main():
             if t != args.tau:
                 r2 = run_workload(inst, t, 20, 3, torch, rt, B, timing=False)
                 extras["batched_tau%g_trees_per_s" % t] = round(inst.R / (r2["ms_per_step"] * 1e-3), 1)
+        extras["sample_T1.0_R32"] = sample_round_us(torch, rt, inputs, 1.0)
         line["extras"] = extras
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inst, args.tau, res)

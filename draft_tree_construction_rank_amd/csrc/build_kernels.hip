@@ -3,24 +3,24 @@
 // The round walks block positions d = 1..B (PCTree summary: every position's logits come
 // from one backbone forward, so a level needs no new drafter pass).  Per level, inside the
 // persistent kernel k_build:
-//   expand  - every workgroup takes (tile of 64 parent rows, vocabulary split) items: the
-//             Markov bias of the tile's parents over the split (bf16 MFMA 32x32x16, fp32
-//             accumulate, W as the A operand so that each lane holds one parent row) is added
-//             to the block logits, tempered, and folded into that row's online log-sum-exp
-//             and top-k (or Gumbel-top-k) in registers; z never reaches memory;
-//   merge   - as soon as all splits of a tile are in, workgroups take its parent rows from a
-//             task counter and combine the split records; each child's probability is
-//             calibrated to an edge estimate and multiplied into the path survival
-//             (TreeSpark core idea);
+//   expand  - every workgroup takes (row tile or group, vocabulary split) items: the Markov
+//             bias of the parents over the split (bf16 MFMA 32x32x16, fp32 accumulate, W as
+//             the A operand so that each lane holds one parent row) is added to the block
+//             logits, tempered, and folded into that row's online log-sum-exp and top-k (or
+//             Gumbel-top-k) in registers; z never reaches memory;
+//   merge   - once all splits of a tile are in, parent row m is merged by workgroup m mod G:
+//             the split records are combined, each child's probability is calibrated to an
+//             edge estimate and multiplied into the path survival (TreeSpark core idea);
 //   select  - the workgroup that merges a request's last row keeps the best n_budget nodes
 //             with survival >= tau (best-first with per-round stopping equals this
-//             expand-then-select because survival never increases along a path) and defines
-//             the next frontier;
-//   release - the workgroup that finishes the last request lays out the next level's rows
-//             and bumps the generation word every workgroup waits on.
+//             expand-then-select because survival never increases along a path), writes the
+//             next frontier and its parent-row records, and the select that completes the
+//             level publishes the next level's sizes in the generation word every workgroup
+//             waits on.
 // A level with no parent rows ends the loop at once (per-round stopping), and the kernel
 // emits the trees.  Workgroups hand data to each other only through agent-coherent accesses
-// (dt_device.h) and counters; every wait is bounded and raises an error flag on time-out.
+// (dt_device.h), counters and the generation word; every wait is bounded and raises an
+// error flag on time-out.
 #include <hip/hip_runtime.h>
 
 #include <mutex>

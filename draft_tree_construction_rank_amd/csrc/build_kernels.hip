@@ -972,28 +972,35 @@ __device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, 
             top.merge_xor(off);
         }
         const float lse2 = acc.m + log2f(acc.s);
+        // lane j < k computes child j (every lane holds the whole merged list; each picks
+        // its own entry with selects, so the k children are computed side by side)
+        uint64_t kj = top.k[0];
+        float yj = top.y[0];
 #pragma unroll
-        for (int j = 0; j < KT; ++j) {
-            if (j < a.k && lane == j) {
-                const float l2 = top.y[j] - lse2;
-                const float q = exp2f(l2);
-                int bin = (int)floorf(16.0f * q);
-                bin = bin > 15 ? 15 : (bin < 0 ? 0 : bin);
-                float cv = a.cal[0];
+        for (int j = 1; j < KT; ++j) {
+            kj = lane == j ? top.k[j] : kj;
+            yj = lane == j ? top.y[j] : yj;
+        }
+        if (lane < a.k) {
+            const int j = lane;
+            const float l2 = yj - lse2;
+            const float q = exp2f(l2);
+            int bin = (int)floorf(16.0f * q);
+            bin = bin > 15 ? 15 : (bin < 0 ? 0 : bin);
+            float cv = a.cal[0];
 #pragma unroll
-                for (int ii = 1; ii < 16; ++ii) cv = (bin == ii) ? a.cal[ii] : cv;
-                ChildRec c;
-                // a list shorter than k (possible only with non-finite logits) leaves the
-                // missing children token -1: never selected
-                c.token = top.k[j] != 0 ? entry_tok(top.k[j]) : -1;
-                c.s = par_s * cv;
-                c.logq = l2 * 0.69314718055994530942f;
-                c.pad = 0;
-                c.hash = child_hash(par_hash, c.token);
-                st_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j, c);
-                sm.mchild[0][j] = (uint64_t)(uint32_t)c.token | ((uint64_t)__float_as_uint(c.s) << 32);
-                sm.mchild[1][j] = c.hash;
-            }
+            for (int ii = 1; ii < 16; ++ii) cv = (bin == ii) ? a.cal[ii] : cv;
+            ChildRec c;
+            // a list shorter than k (possible only with non-finite logits) leaves the
+            // missing children token -1: never selected
+            c.token = kj != 0 ? entry_tok(kj) : -1;
+            c.s = par_s * cv;
+            c.logq = l2 * 0.69314718055994530942f;
+            c.pad = 0;
+            c.hash = child_hash(par_hash, c.token);
+            st_child(a.arena + (((size_t)req * a.B + lvl) * a.Ncap + fi) * a.k + j, c);
+            sm.mchild[0][j] = (uint64_t)(uint32_t)c.token | ((uint64_t)__float_as_uint(c.s) << 32);
+            sm.mchild[1][j] = c.hash;
         }
     }
 }

@@ -471,8 +471,17 @@ __device__ __forceinline__ void expand_epilogue(const BuildArgs& a, f32x16& z, i
             const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if (zg[i] >= thr)
-                    top.push(pack_entry(zg[i] * a.invT + gumbel(wv[i]), cg + i), zg[i] * a.y2scale);
+                if (zg[i] >= thr) {
+                    // Exact pre-test before the key is formed: y + G(u) >= tk, with
+                    // G(u) = -log(-log u) increasing in u, holds iff u >= exp(-e^(y - tk)).
+                    // The 2^-16 margin in u (worth > 4e-5 in key units, since G' >= e) covers
+                    // the float error of both sides, so no column whose key could reach the
+                    // list is skipped; push() still compares the exact keys.  An empty list
+                    // (tk = -inf) gives a bound of 0.
+                    const float ustar = __expf(-__expf(zg[i] * a.invT - tk));
+                    if (u01(wv[i]) >= ustar - 1.52587890625e-05f)
+                        top.push(pack_entry(zg[i] * a.invT + gumbel(wv[i]), cg + i), zg[i] * a.y2scale);
+                }
             }
         }
     } else {

@@ -93,6 +93,10 @@ SMALL = [
     dict(seed=5, V=257, r=8, B=8, k=1, Ncap=6, R=2, dtype="bf16"),
     dict(seed=6, V=130, r=32, B=4, k=5, Ncap=33, R=6, dtype="bf16", tau=0.02),
     dict(seed=7, V=2048, r=256, B=3, k=4, Ncap=64, R=2, dtype="bf16"),
+    # group mode (a level of more than 64 rows, bf16, V a multiple of 8) with a ragged last
+    # 32-column block: the copy clamps of the staging ring
+    dict(seed=8, V=1000, r=64, B=4, k=4, Ncap=32, R=8, dtype="bf16"),
+    dict(seed=9, V=1736, r=256, B=3, k=3, Ncap=40, R=12, dtype="bf16", tau=0.01),
 ]
 
 

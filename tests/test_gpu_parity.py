@@ -97,6 +97,9 @@ SMALL = [
     # 32-column block: the copy clamps of the staging ring
     dict(seed=8, V=1000, r=64, B=4, k=4, Ncap=32, R=8, dtype="bf16"),
     dict(seed=9, V=1736, r=256, B=3, k=3, Ncap=40, R=12, dtype="bf16", tau=0.01),
+    # a wide batch: several 256-row groups per level (the last one ragged) and many merges
+    # and selects per workgroup
+    dict(seed=10, V=2048, r=32, B=3, k=4, Ncap=32, R=200, dtype="bf16"),
 ]
 
 

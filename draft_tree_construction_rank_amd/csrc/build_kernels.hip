@@ -546,7 +546,7 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         size_t lb = 0;
         uint64_t hh = 0;
         if (tid < nrows) {
-            const RowRec* rr = level_rows(a, level) + m0 + tid;
+            const RowRec* rr = level_rows(a, level) + m0 + tid + opaque_zero();
             const uint64_t w0 = cld64(rr), w1 = cld64((const char*)rr + 8);
             hh = cld64((const char*)rr + 16);
             const int req = (int)(uint32_t)w0;
@@ -942,7 +942,7 @@ __device__ __forceinline__ void merge_fetched(const uint64_t (&w)[rec_floats(KT)
 template <int KT>
 __device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, int m,
                                           BuildSmem<KT>& sm, int* req_out, int* F_out) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x + opaque_zero(), lane = tid & 63, wave = threadIdx.x >> 6;
     constexpr int RS = rec_floats(KT);
     TopK<KT> top;
     top.init();
@@ -1030,7 +1030,9 @@ __device__ __forceinline__ void merge_row(const BuildArgs& a, int level, int S, 
 __device__ __forceinline__ void select_request(const BuildArgs& a, int level, int req, int F,
                                                unsigned nreq, SelSmem& ss, int* sh, int* bcast,
                                                const uint64_t (*mine)[kMaxK]) {
-    const int tid = threadIdx.x;
+    // per-thread values below are recomputed at every call: hoisted out of the persistent
+    // loop they were spilled and reloaded one round trip at a time
+    const int tid = threadIdx.x + opaque_zero();
     const int lvl = level - 1;
     const int Ncap = a.Ncap, k = a.k;
     const int nchild = F * k;
@@ -1179,7 +1181,7 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
 
 __device__ __forceinline__ void emit_request(const BuildArgs& a, int req, bool failed,
                                              EmitSmem& e) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x + opaque_zero();
     const int B = a.B, k = a.k, Ncap = a.Ncap;
     // One round of loads: the error flag, the kept keys and their count, the frontier sizes
     // and every frontier identity (invalid slots are zeroed once the sizes are in LDS).  A

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(1024) void k_verify_greedy(int B, int V, int Ncap, 
     __shared__ int s_child;
     const int req = blockIdx.x, tid = threadIdx.x;
     const int n = tree.n_nodes[req];
-    const bool bad = (tree.status[req] & DT_REQ_BAD_ROOT) != 0;
+    // a bad root or a build whose internal wait gave up: nothing is emitted
+    const bool bad = (tree.status[req] & (DT_REQ_BAD_ROOT | DT_REQ_SYNC_TIMEOUT)) != 0;
     if (tid < Ncap) {
         s_tok[tid] = tree.token[(size_t)req * Ncap + tid];
         s_par[tid] = tree.parent[(size_t)req * Ncap + tid];
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(256) void k_vs_init(int R, int B, uint32_t round,
     const int req = blockIdx.x * blockDim.x + threadIdx.x;
     if (req >= R) return;
     VState s;
-    s.active = (tree.status[req] & DT_REQ_BAD_ROOT) ? 0 : 1;
+    s.active = (tree.status[req] & (DT_REQ_BAD_ROOT | DT_REQ_SYNC_TIMEOUT)) ? 0 : 1;
     s.v = -1;
     s.row = 0;
     s.depth = 0;
@@ -467,6 +468,9 @@ __global__ __launch_bounds__(1024) void k_vs_chain(const ChainArgs a) {
         float alpha = 0.0f, S = 1.0f, c = 1.0f;
         for (int j = 0; j < a.k; ++j) {
             const int x = cand[j];
+            // an empty slot (a ranked list shorter than k, only possible with non-finite
+            // draft logits) is no drawn sibling
+            if (x < 0 || x >= a.V) continue;
             const float qx = q[x], px = p[x];
             const uint4 w = rand4((uint32_t)(j >> 2), STREAM_ACCEPT, st.hash, a.seed_lo, a.seed_hi);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};

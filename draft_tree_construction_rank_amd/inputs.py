@@ -32,6 +32,8 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Sequence
 
 import numpy as np
@@ -42,6 +44,7 @@ __all__ = [
     "make_instance",
     "target_rows",
     "target_for_tree",
+    "make_tie_instance",
     "CONFIGS",
 ]
 
@@ -239,7 +242,8 @@ def target_for_tree(inst: Instance, token: np.ndarray, parent: np.ndarray,
     """
     Ncap = inst.Ncap if Ncap is None else Ncap
     out = np.empty((inst.R, Ncap + 1, inst.V), dtype=np.float32)
-    for req in range(inst.R):
+
+    def one(req):
         n = int(n_nodes[req])
         paths = [()]
         for i in range(n):
@@ -249,4 +253,47 @@ def target_for_tree(inst: Instance, token: np.ndarray, parent: np.ndarray,
         rows = target_rows(inst, req, paths)
         out[req, : n + 1] = rows
         out[req, n + 1:] = rows[0]
+
+    # requests are independent draws (each keyed by its own path seeds): threads only
+    # overlap numpy's generator work
+    if inst.R > 1:
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, inst.R)) as ex:
+            list(ex.map(one, range(inst.R)))
+    else:
+        one(0)
     return out
+
+
+def make_tie_instance(*, seed: int, R: int, B: int, k: int, V: int, r: int, Ncap: int,
+                      dtype: str = "bf16", tau: float = 0.0, cal: str = "monotone",
+                      grid: float = 0.25) -> Instance:
+    """Exact ties at the top-k cutoff.  U = 0 (no Markov bias: the logits a parent sees are
+    exactly its block row), Wt ~ N(0, r**-0.5) (multiplied by zero, never influencing z),
+    and block logits on a ``grid``-spaced lattice: N(0, 2) rounded to the grid and clipped to
+    [-8, 8], then per row two tokens share the value max + 2 and k + 1 further tokens share
+    max + 1, so the k-th child is chosen inside a group of equal values.  Distinct values
+    differ by at least one grid step; every value is exact in bf16 and float32."""
+    head_rng = np.random.default_rng([seed, 1])
+    U = np.zeros((V, r), np.float32)
+    Wt = _round(head_rng.normal(0.0, r ** -0.5, size=(V, r)), dtype)
+    if cal == "monotone":
+        cal_v = np.sort(np.random.default_rng([seed, 2]).uniform(0.05, 0.95, 16)).astype(np.float32)
+    else:
+        cal_v = ((np.arange(16) + 0.5) / 16.0).astype(np.float32)
+    srng = np.random.default_rng([seed, 4])
+    roots = srng.integers(0, V, size=R).astype(np.int32)
+    Lext = np.empty((R, B + 1, V), np.float32)
+    for i in range(R):
+        lrng = np.random.default_rng([seed, 5, i])
+        x = np.clip(np.rint(lrng.normal(0.0, 2.0, size=(B + 1, V)) / grid) * grid, -8.0, 8.0)
+        for d in range(B + 1):
+            ids = lrng.choice(V, size=min(V, k + 3), replace=False)
+            top = x[d].max()
+            x[d, ids[:2]] = top + 2.0
+            x[d, ids[2:]] = top + 1.0
+        Lext[i] = _round(x, dtype)
+    return Instance(name="ties", R=R, B=B, k=k, V=V, r=r, Ncap=Ncap, dtype=dtype,
+                    mode="greedy", temperature=1.0, cal=cal_v, seed=seed, round=0, Lext=Lext,
+                    U=U, Wt=Wt, root_token=roots, n_budget=np.full(R, Ncap, np.int32),
+                    tau=np.full(R, tau, np.float32), rho=0.0, peak="ties", target_peak="none",
+                    strength=np.zeros(R), subseed=np.arange(R, dtype=np.int64))

@@ -56,7 +56,9 @@ enum {
     DT_REQ_BAD_ROOT = 1,       /* root_token outside [0, V): empty tree, nothing emitted */
     DT_REQ_BUDGET_CLAMPED = 2, /* n_budget outside [0, Ncap]: clamped into range */
     DT_REQ_SYNC_TIMEOUT = 4    /* an internal wait between workgroups gave up (about two
-                                  seconds): the tree is reported empty */
+                                  seconds): the tree is reported empty and the verifiers
+                                  emit nothing for the request (n_out = 0), as for a bad
+                                  root */
 };
 
 /* Round parameters (host struct, read synchronously). */

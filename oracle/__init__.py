@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes as C
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
 import numpy as np
@@ -39,7 +40,7 @@ class Params(C.Structure):
     _fields_ = [("R", C.c_int32), ("B", C.c_int32), ("k", C.c_int32), ("V", C.c_int32),
                 ("r", C.c_int32), ("Ncap", C.c_int32), ("mode", C.c_int32),
                 ("temperature", C.c_double), ("cal", C.c_float * 16), ("seed", C.c_uint64),
-                ("round", C.c_uint32)]
+                ("round", C.c_uint32), ("req_base", C.c_int32)]
 
 
 class _Tree(C.Structure):
@@ -98,8 +99,10 @@ def _p(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
-def make_params(inst, *, R=None, mode=None, temperature=None, round_=None) -> Params:
+def make_params(inst, *, R=None, mode=None, temperature=None, round_=None,
+                req_base=0) -> Params:
     P = Params()
+    P.req_base = int(req_base)
     P.R = inst.R if R is None else R
     P.B, P.k, P.V, P.r, P.Ncap = inst.B, inst.k, inst.V, inst.r, inst.Ncap
     m = inst.mode if mode is None else mode
@@ -178,60 +181,61 @@ def new_margins(R: int) -> np.ndarray:
     return m
 
 
+def workers() -> int:
+    """Threads for per-request oracle calls (each call is single-threaded C; ctypes releases
+    the GIL).  DT_ORACLE_THREADS overrides; at most 16."""
+    env = os.environ.get("DT_ORACLE_THREADS")
+    n = int(env) if env else min(16, os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
+def _map(fn, items):
+    items = list(items)
+    if len(items) <= 1 or workers() == 1:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(max_workers=min(workers(), len(items))) as ex:
+        return list(ex.map(fn, items))
+
+
 def build_tree(inst, *, requests=None, method: int = 0, n_budget=None, tau=None,
                margins: Optional[np.ndarray] = None, mode=None, temperature=None,
                round_=None) -> dict:
     """Build trees for the listed requests (default all).  ``method`` 0 = best-first
     priority queue, 1 = level-synchronous.  Returns the tree dict (arrays over the listed
-    requests, in that order)."""
+    requests, in that order).  Each request is built by its own single-request call, keyed
+    by its true request id; the calls run on a thread pool."""
     reqs = list(range(inst.R)) if requests is None else list(requests)
     R = len(reqs)
-    P = make_params(inst, R=R, mode=mode, temperature=temperature, round_=round_)
-    L = _c32(inst.L[reqs])
-    roots = _c32(inst.root_token[reqs], np.int32)
-    nb = _c32((inst.n_budget if n_budget is None else np.broadcast_to(n_budget, inst.R))[reqs],
-              np.int32)
-    ta = _c32((inst.tau if tau is None else np.broadcast_to(np.float32(tau), inst.R))[reqs])
-    t = new_tree(R, inst.Ncap, inst.k)
-    ts = _tree_struct(t)
-    mg = margins if margins is not None else new_margins(R)
-    # request ids enter the random keys: pass the true id through a per-request call when
-    # the subset is not 0..R-1
-    if reqs == list(range(R)):
-        rc = lib().or_build(C.byref(P), _p(L), _p(_c32(inst.U)), _p(_c32(inst.Wt)), _p(roots),
-                            _p(nb), _p(ta), method, C.byref(ts), _p(mg))
+    nb = np.asarray(inst.n_budget if n_budget is None else np.broadcast_to(n_budget, inst.R),
+                    np.int64)
+    ta = np.asarray(inst.tau if tau is None else np.broadcast_to(np.float32(tau), inst.R),
+                    np.float32)
+    U, Wt = _c32(inst.U), _c32(inst.Wt)
+
+    def one(rq):
+        P = make_params(inst, R=1, mode=mode, temperature=temperature, round_=round_,
+                        req_base=rq)
+        L = _c32(inst.L[rq:rq + 1])
+        t = new_tree(1, inst.Ncap, inst.k)
+        ts = _tree_struct(t)
+        mg = new_margins(1)
+        rc = lib().or_build(C.byref(P), _p(L), _p(U), _p(Wt),
+                            _p(_c32(inst.root_token[rq:rq + 1], np.int32)),
+                            _p(_c32(nb[rq:rq + 1], np.int32)), _p(_c32(ta[rq:rq + 1])),
+                            method, C.byref(ts), _p(mg))
         assert rc == 0
-    else:
-        for i, rq in enumerate(reqs):
-            one = _build_one(inst, rq, method, int(nb[i]), float(ta[i]), mode, temperature,
-                             round_)
-            for f in t:
-                t[f][i] = one[0][f][rq]
-            mg[i] = one[1][rq]
+        return t, mg
+
+    res = _map(one, reqs)
+    t = new_tree(R, inst.Ncap, inst.k)
+    mg = margins if margins is not None else new_margins(R)
+    for i, (one_t, one_m) in enumerate(res):
+        for f in t:
+            t[f][i] = one_t[f][0]
+        mg[i] = one_m[0]
     t["margins"] = mg
     t["requests"] = reqs
     return t
-
-
-def _build_one(inst, rq, method, nb, tau, mode, temperature, round_):
-    """Build request rq alone but with its true request id (id enters the random keys)."""
-    R = rq + 1
-    P = make_params(inst, R=R, mode=mode, temperature=temperature, round_=round_)
-    L = np.zeros((R, inst.B, inst.V), np.float32)
-    L[rq] = inst.L[rq]
-    roots = np.full(R, -1, np.int32)
-    roots[rq] = inst.root_token[rq]
-    nbs = np.zeros(R, np.int32)
-    nbs[rq] = nb
-    taus = np.zeros(R, np.float32)
-    taus[rq] = tau
-    t = new_tree(R, inst.Ncap, inst.k)
-    ts = _tree_struct(t)
-    mg = new_margins(R)
-    rc = lib().or_build(C.byref(P), _p(L), _p(_c32(inst.U)), _p(_c32(inst.Wt)), _p(roots),
-                        _p(nbs), _p(taus), method, C.byref(ts), _p(mg))
-    assert rc == 0
-    return t, mg
 
 
 def _verify_struct(R: int, B: int):
@@ -243,59 +247,64 @@ def _verify_struct(R: int, B: int):
     return o, s
 
 
-def _subset_tree(tree: dict, reqs_needed: int, ids) -> dict:
-    """Place a tree over listed requests into arrays indexed by true request id."""
-    out = {}
-    for f, v in tree.items():
-        if f in ("margins", "requests"):
-            continue
-        a = np.zeros((reqs_needed,) + v.shape[1:], dtype=v.dtype)
-        if f == "status":
-            a[:] = STATUS_BAD_ROOT  # requests not listed are skipped by the verifiers
-        for i, rq in enumerate(ids):
-            a[rq] = v[i]
-        out[f] = a
-    return out
+def _tree_row(tree: dict, i: int) -> dict:
+    """Request i of a tree dict as a single-request tree (contiguous copies)."""
+    return {f: np.ascontiguousarray(v[i:i + 1]) for f, v in tree.items()
+            if f not in ("margins", "requests")}
+
+
+def _collect(outs, B):
+    R = len(outs)
+    o = dict(accept_len=np.zeros(R, np.int32), path=np.zeros((R, B), np.int32),
+             out_tokens=np.zeros((R, B + 1), np.int32), n_out=np.zeros(R, np.int32))
+    mg = new_margins(R)
+    for i, (oi, mi) in enumerate(outs):
+        for f in o:
+            o[f][i] = oi[f][0]
+        mg[i] = mi[0]
+    o["margins"] = mg
+    return o
 
 
 def verify_greedy(inst, tree: dict, target: np.ndarray, margins=None) -> dict:
     """Greedy accept-walk for the requests in ``tree['requests']``; target [len][Ncap+1][V]."""
     ids = tree["requests"]
-    R = max(ids) + 1
-    full = _subset_tree(tree, R, ids)
-    tg = np.zeros((R, inst.Ncap + 1, inst.V), np.float32)
-    tg[ids] = target
-    P = make_params(inst, R=R)
-    ts = _tree_struct(full)
-    o, os_ = _verify_struct(R, inst.B)
-    mg = new_margins(R)
-    lib().or_verify_greedy(C.byref(P), C.byref(ts), _p(tg), C.byref(os_), _p(mg))
-    res = {f: v[ids] for f, v in o.items()}
-    res["margins"] = mg[ids]
-    return res
+
+    def one(i):
+        P = make_params(inst, R=1, req_base=ids[i])
+        t1 = _tree_row(tree, i)
+        ts = _tree_struct(t1)
+        o, os_ = _verify_struct(1, inst.B)
+        mg = new_margins(1)
+        tg = _c32(target[i:i + 1])
+        lib().or_verify_greedy(C.byref(P), C.byref(ts), _p(tg), C.byref(os_), _p(mg))
+        return o, mg
+
+    return _collect(_map(one, range(len(ids))), inst.B)
 
 
 def verify_sample(inst, tree: dict, target: np.ndarray, *, temperature=None,
                   round_=None) -> dict:
     """Lossless sample verify for the requests in ``tree['requests']``."""
     ids = tree["requests"]
-    R = max(ids) + 1
-    full = _subset_tree(tree, R, ids)
-    tg = np.zeros((R, inst.Ncap + 1, inst.V), np.float32)
-    tg[ids] = target
-    L = np.zeros((R, inst.B, inst.V), np.float32)
-    L[ids] = inst.L[ids]
-    roots = np.zeros(R, np.int32)
-    roots[ids] = inst.root_token[ids]
-    P = make_params(inst, R=R, mode=SAMPLE, temperature=temperature, round_=round_)
-    ts = _tree_struct(full)
-    o, os_ = _verify_struct(R, inst.B)
-    mg = new_margins(R)
-    lib().or_verify_sample(C.byref(P), C.byref(ts), _p(L), _p(_c32(inst.U)), _p(_c32(inst.Wt)),
-                           _p(roots), _p(tg), C.byref(os_), _p(mg))
-    res = {f: v[ids] for f, v in o.items()}
-    res["margins"] = mg[ids]
-    return res
+    U, Wt = _c32(inst.U), _c32(inst.Wt)
+
+    def one(i):
+        rq = ids[i]
+        P = make_params(inst, R=1, mode=SAMPLE, temperature=temperature, round_=round_,
+                        req_base=rq)
+        t1 = _tree_row(tree, i)
+        ts = _tree_struct(t1)
+        o, os_ = _verify_struct(1, inst.B)
+        mg = new_margins(1)
+        L = _c32(inst.L[rq:rq + 1])
+        roots = _c32(inst.root_token[rq:rq + 1], np.int32)
+        tg = _c32(target[i:i + 1])
+        lib().or_verify_sample(C.byref(P), C.byref(ts), _p(L), _p(U), _p(Wt), _p(roots),
+                               _p(tg), C.byref(os_), _p(mg))
+        return o, mg
+
+    return _collect(_map(one, range(len(ids))), inst.B)
 
 
 def chain_probs(p: np.ndarray, q: np.ndarray, x) -> tuple:

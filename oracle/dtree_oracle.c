@@ -424,7 +424,7 @@ int or_build(const or_params* P, const float* L, const float* U, const float* Wt
             root.child0 = -1;
             root.s = 1.0f;
             root.logq = 0.0f;
-            root.hash = or_root_hash(P->round, req, root_token[req]);
+            root.hash = or_root_hash(P->round, P->req_base + req, root_token[req]);
             store_add(&st, root);
             if (method == 0)
                 nsel = build_heap(P, L_req, U, Wt, &st, nb, tau[req], sel, ybuf, mg, &nexp);
@@ -591,11 +591,13 @@ int or_verify_sample(const or_params* P, const or_tree* T, const float* L, const
             continue;
         }
         const float* L_req = L + (size_t)req * (size_t)B * (size_t)V;
-        int v = -1, row = 0, depth = 0, nacc = 0, nemit = 0;
+        int v = -1, row = 0, prow = 0, depth = 0, nacc = 0, nemit = 0;
         int32_t token = root_token[req];
-        uint64_t hash = or_root_hash(P->round, req, token);
+        uint64_t hash = or_root_hash(P->round, P->req_base + req, token);
         for (;;) {
-            const float* t = target + ((size_t)req * (Ncap + 1) + row) * (size_t)V;
+            /* fault 3 (negative control): the depth-B draw reads the parent's target row */
+            const int trow = (depth == B && g_fault == 3) ? prow : row;
+            const float* t = target + ((size_t)req * (Ncap + 1) + trow) * (size_t)V;
             for (int c = 0; c < V; ++c) yp[c] = (double)t[c] / Temp;
             double gap;
             if (depth == B) {
@@ -618,6 +620,10 @@ int or_verify_sample(const or_params* P, const or_tree* T, const float* L, const
             int accepted = -1;
             for (int j = 0; j < k; ++j) {
                 int32_t x = cand[j];
+                /* reading: a ranked list shorter than k (only possible when the draft row
+                 * holds non-finite values) leaves slot j empty (-1); an empty slot is no
+                 * drawn sibling and is skipped */
+                if (x < 0 || x >= V) continue;
                 double u = or_uniform(P->seed, hash, OR_STREAM_ACCEPT, (uint32_t)j);
                 if (mg && q[x] > 0.0) upd_min(&mg->accept, fabs(u - p[x] / q[x]));
                 if (u * q[x] < p[x]) {
@@ -635,6 +641,7 @@ int or_verify_sample(const or_params* P, const or_tree* T, const float* L, const
                 if (w < 0) break; /* accepted sibling outside the tree: ends the round */
                 out->path[(size_t)req * B + nacc++] = w;
                 v = w;
+                prow = row;
                 row = w + 1;
                 depth += 1;
                 token = accepted;

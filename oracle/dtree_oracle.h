@@ -39,6 +39,8 @@ typedef struct {
     float cal[16];        /* calibration table, values in [0, 1] */
     uint64_t seed;
     uint32_t round;
+    int32_t req_base;     /* request id of row 0 of every [R] array: request i's random
+                             streams are keyed by req_base + i */
 } or_params;
 
 /* Emitted trees, canonical (depth, path-lex) order; caller-owned host arrays. */
@@ -115,7 +117,7 @@ int or_sample_rounds(const or_params* P, const float* L, const float* U, const f
 
 /* Negative controls for the statistical pins (0 = faithful). 1: q is not reduced after a
  * rejection (the rejected sibling keeps its mass); 2: the target law is not replaced by the
- * residual after a rejection. */
+ * residual after a rejection; 3: the draw at a depth-B node uses its parent's target row. */
 void or_set_fault(int32_t mode);
 
 #ifdef __cplusplus

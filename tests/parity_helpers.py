@@ -13,6 +13,8 @@ from __future__ import annotations
 
 import dataclasses
 import functools
+import json
+import os
 
 import numpy as np
 
@@ -20,7 +22,7 @@ import oracle
 from draft_tree_construction_rank_amd import inputs
 
 GREEDY_MARGIN = 1e-3
-SAMPLE_MARGIN = 1e-4
+SAMPLE_MARGIN = 1e-3
 TREE_FIELDS = ("token", "parent", "depth", "mask", "n_nodes", "cand", "status", "surv")
 
 
@@ -66,21 +68,44 @@ def _ok(m, mode, margin=None) -> bool:
     return min(m["key_gap"], m["q_edge"]) >= thr
 
 
+def _fold_verify(margins, vm):
+    for f in ("accept", "draw_gap"):
+        margins[f] = np.minimum(margins[f], vm[f])
+
+
+GOLDEN_SUBSEEDS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                               "certified_subseeds.json")
+
+
+def stored_subseeds(key: str):
+    """Per-request block-logit sub-seeds found by certification for the case `key`
+    (tests/golden/certified_subseeds.json, written by tests/golden/make_certified_subseeds.py
+    from the oracle alone), or None."""
+    if not os.path.exists(GOLDEN_SUBSEEDS):
+        return None
+    with open(GOLDEN_SUBSEEDS) as fh:
+        return json.load(fh).get(key)
+
+
 def certified(inst: inputs.Instance, requests=None, max_tries: int = 60, verify_target=None,
-              margin=None):
+              margin=None, key: str = None):
     """Return (instance, oracle tree over `requests`) with every listed request certified.
 
-    Requests that miss the margin get a new block-logits sub-seed; the instance returned
-    carries the sub-seeds used.  `verify_target`, if given, is a callable (inst, tree) ->
-    margins of the verify step, folded into the certification."""
+    Requests that miss the margin get a new block-logits sub-seed (only those are rebuilt);
+    the instance returned carries the sub-seeds used.  `verify_target`, if given, is a
+    callable (inst, tree) -> margins of the verify step over tree["requests"], folded into
+    the certification.  With `key`, the sub-seeds stored for that case are applied first;
+    every margin is still measured, and requests that miss it are re-drawn as usual."""
+    if key is not None:
+        sub = stored_subseeds(key)
+        if sub is not None and len(sub) == inst.R:
+            inst = redraw(inst, np.asarray(sub, np.int64))
     reqs = list(range(inst.R)) if requests is None else list(requests)
     tree = oracle.build_tree(inst, requests=reqs)
+    margins = tree["margins"].copy()
+    if verify_target is not None:
+        _fold_verify(margins, verify_target(inst, tree))
     for attempt in range(max_tries):
-        margins = tree["margins"].copy()
-        if verify_target is not None:
-            vm = verify_target(inst, tree)
-            for f in ("accept", "draw_gap"):
-                margins[f] = np.minimum(margins[f], vm[f])
         bad = [i for i, m in enumerate(margins) if not _ok(m, inst.mode, margin)]
         if not bad:
             return inst, tree
@@ -88,8 +113,66 @@ def certified(inst: inputs.Instance, requests=None, max_tries: int = 60, verify_
         for i in bad:
             sub[reqs[i]] += 1000 * (attempt + 1)
         inst = redraw(inst, sub)
-        tree = oracle.build_tree(inst, requests=reqs)
+        part = oracle.build_tree(inst, requests=[reqs[i] for i in bad])
+        for f, v in tree.items():
+            if f != "requests":
+                v[bad] = part[f]
+        pm = part["margins"].copy()
+        if verify_target is not None:
+            _fold_verify(pm, verify_target(inst, part))
+        margins[bad] = pm
     raise AssertionError("could not certify margins for %s" % inst.name)
+
+
+def tree_targets(inst: inputs.Instance, tree: dict, rows) -> np.ndarray:
+    """Target logits [len(rows)][Ncap+1][V] for the trees of `tree` (request rows[i] is
+    tree entry i): row 0 = root, row j+1 = node j, keyed by each node's token path; empty
+    slots repeat the root row.  Requests are generated on a thread pool."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((len(rows), inst.Ncap + 1, inst.V), np.float32)
+
+    def one(i):
+        rq = rows[i]
+        n = int(tree["n_nodes"][i])
+        paths = [()]
+        for j in range(n):
+            pj = int(tree["parent"][i, j])
+            paths.append((() if pj < 0 else paths[pj + 1]) + (int(tree["token"][i, j]),))
+        r = inputs.target_rows(inst, rq, paths)
+        out[i, : n + 1] = r
+        out[i, n + 1:] = r[0]
+
+    with ThreadPoolExecutor(max_workers=oracle.workers()) as ex:
+        list(ex.map(one, range(len(rows))))
+    return out
+
+
+def tie_targets(inst: inputs.Instance, tree: dict, seed: int) -> np.ndarray:
+    """Greedy-verify targets [R][Ncap+1][V] with exact ties at every row's maximum.
+
+    Rows are N(0, 2) on a 0.25 grid, clipped to [-8, 8]; two tokens then share the value
+    10.  Where the row belongs to an expanded node (a candidate list in `tree`), the pair
+    is chosen so that the tie rule decides the walk: both from the candidate list, or a
+    candidate and a non-candidate token in either id order."""
+    rng = np.random.default_rng([seed, 77])
+    R, N1, V = inst.R, inst.Ncap + 1, inst.V
+    out = np.empty((R, N1, V), np.float32)
+    for i in range(R):
+        x = np.clip(np.rint(rng.normal(0.0, 2.0, size=(N1, V)) / 0.25) * 0.25, -8.0, 8.0)
+        for row in range(N1):
+            cand = [int(c) for c in tree["cand"][i, row] if c >= 0]
+            others = rng.choice(V, size=4, replace=False)
+            others = [int(o) for o in others if int(o) not in cand][:1]
+            kind = int(rng.integers(0, 3))
+            if len(cand) >= 2 and kind == 0:
+                pair = list(rng.choice(cand, size=2, replace=False))
+            elif cand and others:
+                pair = [int(rng.choice(cand)), others[0]]
+            else:
+                pair = [int(t) for t in rng.choice(V, size=2, replace=False)]
+            x[row, pair] = 10.0
+        out[i] = inputs._round(x, inst.dtype)
+    return out
 
 
 def redraw(inst: inputs.Instance, subseed: np.ndarray) -> inputs.Instance:
@@ -121,3 +204,45 @@ def compare_verify(ref: dict, got: dict, rows):
         for f in ("accept_len", "path", "out_tokens", "n_out"):
             assert np.array_equal(ref[f][i], got[f][rq]), "request %d %s: oracle %s gpu %s" % (
                 rq, f, ref[f][i], got[f][rq])
+
+
+def sample_verify_margins(inst, tree):
+    """Margins of the sample verifier over the trees of `tree` (accept tests, draws)."""
+    rows = tree["requests"]
+    return oracle.verify_sample(inst, tree, tree_targets(inst, tree, rows))["margins"]
+
+
+# Full-vocabulary parity cases (V = 151936): key -> instance arguments.  The key also names
+# the case's stored sub-seeds.
+def _full_cases():
+    c = {}
+    for strong in (False, True):
+        c["b7|strong=%d" % strong] = dict(name="b7", strong=strong)
+        c["b16|strong=%d" % strong] = dict(name="b16", strong=strong)
+    c["b16|sharp"] = dict(name="b16", strong=True, strength=24.0)
+    for k in (1, 2, 4, 8):
+        for N in (16, 32, 64):
+            c["b16|k=%d|N=%d" % (k, N)] = dict(name="b16", k=k, Ncap=N)
+    for tau in (0.05, 0.2, 0.5, 0.0):
+        c["batched|tau=%g|strong=0" % tau] = dict(name="batched", tau=tau)
+    for tau in (0.05, 0.0):
+        c["batched|tau=%g|strong=1" % tau] = dict(name="batched", strong=True, tau=tau)
+    for T in (0.6, 1.0, 1.5):
+        c["sample|T=%g|strong=0" % T] = dict(name="sample", temperature=T)
+    c["sample|T=1|strong=1"] = dict(name="sample", strong=True, temperature=1.0)
+    return c
+
+
+FULL_CASES = _full_cases()
+
+
+def case_instance(key: str) -> inputs.Instance:
+    kw = dict(FULL_CASES[key])
+    return instance(kw.pop("name"), **kw)
+
+
+def certify_case(key: str, requests=None):
+    """Certified (instance, oracle tree) of a full-vocabulary case."""
+    inst = case_instance(key)
+    vt = sample_verify_margins if inst.mode == "sample" else None
+    return certified(inst, requests, verify_target=vt, key=key)

@@ -10,8 +10,8 @@ import pytest
 import oracle
 from draft_tree_construction_rank_amd import inputs
 from oracle_helpers import check_structure, tree_paths
-from parity_helpers import (STRESS_MARGIN, certified, compare_trees, compare_verify,
-                            instance)
+from parity_helpers import (STRESS_MARGIN, case_instance, certified, compare_trees,
+                            compare_verify, instance, tie_targets, tree_targets)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,29 +33,36 @@ def _gpu_round(rt, inst, **pkw):
     return rnd, d, rt.tree_to_numpy(rnd.tree)
 
 
-def _greedy_case(rt, inst, rows=None, margin=None):
-    print("case", inst.name, "R=%d B=%d k=%d V=%d N=%d" % (inst.R, inst.B, inst.k, inst.V, inst.Ncap),
-          flush=True)
+def _greedy_case(rt, inst, rows=None, margin=None, key=None):
+    """Certify, build on the GPU, compare `rows` (default: every request) with the oracle,
+    check every request's structure, then greedy-verify against targets keyed by the
+    oracle trees' token paths and compare the walks.  `key` names a full-vocabulary case
+    (its instance and stored sub-seeds) instead of `inst`."""
+    if key is not None:
+        inst = case_instance(key)
+    print("case", key or inst.name, "R=%d B=%d k=%d V=%d N=%d" % (
+        inst.R, inst.B, inst.k, inst.V, inst.Ncap), flush=True)
     rows = list(range(inst.R)) if rows is None else rows
-    inst, ref = certified(inst, rows, margin=margin)
+    inst, ref = certified(inst, rows, margin=margin, key=key)
     rnd, d, got = _gpu_round(rt, inst)
     compare_trees(ref, got, rows)
     for i in range(inst.R):
         check_structure(inst, got, i)
-    # greedy verify on targets built from the oracle's trees (other requests: zero rows)
-    full_rows = rows
-    tgt = np.zeros((inst.R, inst.Ncap + 1, inst.V), np.float32)
-    for i, rq in enumerate(rows):
-        one = {f: ref[f][i:i + 1] for f in ("token", "parent", "n_nodes")}
-        sub = inputs.target_for_tree(_one_request(inst, rq), one["token"], one["parent"],
-                                     one["n_nodes"])
-        tgt[rq] = sub[0]
-    vres = oracle.verify_greedy(inst, ref, tgt[rows])
+    sub = tree_targets(inst, ref, rows)
+    vres = oracle.verify_greedy(inst, ref, sub)
+    if rows == list(range(inst.R)):
+        tgt = sub
+    else:
+        tgt = np.zeros((inst.R, inst.Ncap + 1, inst.V), np.float32)
+        tgt[rows] = sub
+    del sub
     out = rnd.verify_greedy(rt.target_to_device(inst, tgt))
     import torch
     torch.cuda.synchronize()
     gv = {k: v.cpu().numpy() for k, v in out.items()}
-    compare_verify(vres, gv, full_rows)
+    compare_verify(vres, gv, rows)
+    print("  compared %d requests: mean nodes %.1f, mean accept_len %.2f" % (
+        len(rows), float(ref["n_nodes"].mean()), float(vres["accept_len"].mean())), flush=True)
     return inst, ref, got, gv
 
 
@@ -71,17 +78,6 @@ def _check_expansions(inst, got, rows):
     if len(used):
         last = int(used.max())
         assert (lr[:last + 1] > 0).all() and (lr[last + 1:] == 0).all(), lr
-
-
-def _one_request(inst, rq):
-    """View of request rq alone (for target generation, which is keyed by request)."""
-    import dataclasses
-    sub = dataclasses.replace(inst)
-    sub.R = 1
-    sub.Lext = inst.Lext[rq:rq + 1]
-    sub.subseed = inst.subseed[rq:rq + 1]
-    sub.strength = inst.strength[rq:rq + 1]
-    return sub
 
 
 # ------------------------------------------------------------------ small, several tiles ----
@@ -117,27 +113,27 @@ def test_tiny_config(rt):
     _greedy_case(rt, instance("tiny"))
 
 
-def test_b7_config(rt):
-    _greedy_case(rt, instance("b7"))
+@pytest.mark.parametrize("strong", [0, 1])
+def test_b7_config(rt, strong):
+    _greedy_case(rt, None, key="b7|strong=%d" % strong)
 
 
-@pytest.mark.parametrize("strong", [False, True])
+@pytest.mark.parametrize("strong", [0, 1])
 def test_b16_headline(rt, strong):
-    inst, ref, got, _ = _greedy_case(rt, instance("b16", strong=strong))
+    inst, ref, got, _ = _greedy_case(rt, None, key="b16|strong=%d" % strong)
     _check_expansions(inst, got, [0])
 
 
 def test_b16_sharp_peaks(rt):
     """Planted boosts large enough that child probabilities spread over the calibration bins,
     so survival ordering (not only breadth-first order) decides the tree at full V."""
-    _greedy_case(rt, instance("b16", strength=24.0, strong=True))
+    _greedy_case(rt, None, key="b16|sharp")
 
 
 @pytest.mark.parametrize("k", [1, 2, 4, 8])
 @pytest.mark.parametrize("N", [16, 32, 64])
 def test_b16_sweep(rt, k, N):
-    inst = instance("b16", k=k, Ncap=N)
-    inst, ref, got, _ = _greedy_case(rt, inst)
+    inst, ref, got, _ = _greedy_case(rt, None, key="b16|k=%d|N=%d" % (k, N))
     if k == 1:
         # k = 1: the argmax chain of the parent-conditioned logits (PCTree: k = 1 = chain)
         t = int(inst.root_token[0])
@@ -150,10 +146,55 @@ def test_b16_sweep(rt, k, N):
 
 @pytest.mark.parametrize("tau", [0.05, 0.2, 0.5, 0.0])
 def test_batched_config(rt, tau):
-    inst = instance("batched", tau=tau)
-    rows = [0, 17, 38, 63] if tau > 0 else [5, 40]
-    inst, ref, got, _ = _greedy_case(rt, inst, rows=rows)
-    _check_expansions(inst, got, rows)
+    """The batched workload (64 requests, per-request peak strength): every request is
+    compared with the oracle; tau = 0 keeps full 64-node trees (65 expansions each)."""
+    inst, ref, got, _ = _greedy_case(rt, None, key="batched|tau=%g|strong=0" % tau)
+    _check_expansions(inst, got, list(range(inst.R)) if tau > 0 else list(range(8)))
+
+
+@pytest.mark.parametrize("tau", [0.05, 0.0])
+def test_batched_strong_head(rt, tau):
+    """Strong-head companion of the batched workload (U, W sd r^-1/4, bias sd 1), so that a
+    wrong parent row in the group-mode expansion changes the trees."""
+    inst, ref, got, _ = _greedy_case(rt, None, key="batched|tau=%g|strong=1" % tau)
+    _check_expansions(inst, got, list(range(inst.R)) if tau > 0 else list(range(8)))
+
+
+# ------------------------------------------------------------------ exact ties -------------
+TIES = [
+    # tile mode, full vocabulary, one request
+    dict(seed=31, R=1, B=16, k=4, V=151936, r=256, Ncap=64),
+    # group mode (levels of more than 64 rows), several requests
+    dict(seed=42, R=8, B=4, k=4, V=2048, r=64, Ncap=32),
+    dict(seed=58, R=6, B=5, k=3, V=4096, r=32, Ncap=48),
+    # k = 1: the argmax of two equal maxima is the lower id
+    dict(seed=34, R=2, B=8, k=1, V=1000, r=16, Ncap=8),
+]
+
+
+@pytest.mark.parametrize("cfg", TIES, ids=lambda c: "seed%d" % c["seed"])
+def test_exact_ties_lower_token_id(rt, cfg):
+    """Exact ties (U = 0, logits on a 0.25 grid with equal values planted across the top-k
+    cutoff): children and verify argmaxes must take the lower token id, bit for bit with the
+    oracle.  Only the calibration-bin margin is certified: ranking gaps are 0 or >= 0.25."""
+    import torch
+    inst = inputs.make_tie_instance(**cfg)
+    print("case ties", cfg, flush=True)
+    ref = oracle.build_tree(inst)
+    assert (ref["margins"]["q_edge"] >= 1e-3).all(), ref["margins"]["q_edge"]
+    assert (ref["margins"]["key_gap"] == 0).any()  # ties are really decided
+    rnd, d, got = _gpu_round(rt, inst)
+    rows = list(range(inst.R))
+    compare_trees(ref, got, rows)
+    for i in rows:
+        check_structure(inst, got, i)
+    tgt = tie_targets(inst, ref, cfg["seed"])
+    vres = oracle.verify_greedy(inst, ref, tgt)
+    assert (vres["margins"]["argmax_gap"] == 0).all()
+    out = rnd.verify_greedy(rt.target_to_device(inst, tgt))
+    torch.cuda.synchronize()
+    gv = {k: v.cpu().numpy() for k, v in out.items()}
+    compare_verify(vres, gv, rows)
 
 
 # ------------------------------------------------------------------ edge cases -------------
@@ -178,7 +219,7 @@ def test_edge_single_level_and_k_equals_v(rt):
 
 
 def test_deterministic_repeat(rt):
-    inst = instance("b7", strong=True)
+    inst = case_instance("b7|strong=1")
     rnd, d, a = _gpu_round(rt, inst)
     rnd.build(d)
     import torch

@@ -180,6 +180,57 @@ def test_chisq_negative_control_rejected():
     assert pval < 1e-9, pval
 
 
+def _depth_b_instance(T, seed=21, k=3):
+    """B = 1 with every drawn sibling kept: a round that accepts a sibling descends to a
+    depth-B node, so its second token is that node's terminal draw from p."""
+    inst = small_instance(seed, V=16, r=4, B=1, k=k, Ncap=k, mode="sample", temperature=T,
+                          cal="linear", peak="none")
+    rng = np.random.default_rng(300 + seed)
+    tab = rng.normal(0, 1.5, size=(inst.B + 1, inst.V, inst.V)).astype(np.float32)
+    # the root's target row follows the draft row, so most rounds accept a sibling
+    root = int(inst.root_token[0])
+    tab[0, root] = (node_dist(inst, 0, 0, root, 1.0) + rng.normal(0, 0.3, inst.V)).astype(np.float32)
+    return inst, tab
+
+
+def _depth_b_pvalue(inst, tab, T, n):
+    """Chi-square of the second token given the first against p of the depth-B node
+    (softmax of its own target row at temperature T)."""
+    first, second = oracle.sample_rounds(inst, tab, n, temperature=T)
+    stat, dof = 0.0, 0
+    for x in range(inst.V):
+        sel = second[(first == x) & (second >= 0)]
+        if len(sel) < 200:
+            continue
+        px = softmax(tab[1, x].astype(np.float64) / T)
+        s, d = _chisq(np.bincount(sel, minlength=inst.V).astype(float), px)
+        stat += s
+        dof += d
+    return stats.chi2.sf(stat, dof), (second >= 0).mean(), dof
+
+
+@pytest.mark.parametrize("T", [0.6, 1.0, 1.5])
+def test_chisq_depth_b_terminal_draw(T):
+    """TreeSpark lossless section: at the last block position there is no draft row, so the
+    round ends with a draw from the target law p of that node."""
+    inst, tab = _depth_b_instance(T)
+    pval, frac2, dof = _depth_b_pvalue(inst, tab, T, 600_000)
+    assert frac2 > 0.2 and dof >= 60  # many depth-B draws under test
+    assert pval > 1e-4, pval
+
+
+def test_chisq_depth_b_negative_control_rejected():
+    """A depth-B draw taken from the parent's target row must fail the same test."""
+    T = 1.0
+    inst, tab = _depth_b_instance(T)
+    oracle.set_fault(3)
+    try:
+        pval, _, _ = _depth_b_pvalue(inst, tab, T, 600_000)
+    finally:
+        oracle.set_fault(0)
+    assert pval < 1e-9, pval
+
+
 def test_single_draft_acceptance_rate():
     """k = 1: the root's draft is accepted with probability sum_x min(p(x), q(x)); an
     accepted draft is in the tree (N >= 1, tau = 0), so the round then emits a second token."""

@@ -20,8 +20,9 @@ DT_F32, DT_BF16 = 0, 1
 DT_GREEDY, DT_SAMPLE = 0, 1
 DT_REQ_BAD_ROOT, DT_REQ_BUDGET_CLAMPED = 1, 2
 
-EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_verify_greedy",
+EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_build_noalloc", "tree_verify_greedy",
             "tree_verify_sample", "dt_status_string", "dt_timing_enable", "dt_timing_read")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # DT_NOALLOC_SCRATCH_BYTES of include/dtree.h
 
 
 class DtError(RuntimeError):
@@ -67,6 +68,8 @@ def lib() -> C.CDLL:
         L.dt_build_workspace_bytes.restype = C.c_int
         L.tree_build.argtypes = [P, vp, vp, vp, vp, vp, vp, C.POINTER(dt_tree), vp, C.c_size_t, vp]
         L.tree_build.restype = C.c_int
+        L.tree_build_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, C.POINTER(dt_tree), vp]
+        L.tree_build_noalloc.restype = C.c_int
         L.tree_verify_greedy.argtypes = [P, C.POINTER(dt_tree), vp, C.POINTER(dt_verify_out), vp,
                                          C.c_size_t, vp]
         L.tree_verify_greedy.restype = C.c_int
@@ -171,6 +174,17 @@ def tree_build(p: dt_params, block_logits: torch.Tensor, U: torch.Tensor, Wt: to
                           workspace.numel(), _stream(stream))
     if rc != DT_OK:
         raise DtError("tree_build", rc)
+
+
+def tree_build_noalloc(p: dt_params, block_logits: torch.Tensor, U: torch.Tensor,
+                       Wt: torch.Tensor, root_token: torch.Tensor, n_budget: torch.Tensor,
+                       tau: torch.Tensor, out: dict, stream=None) -> None:
+    ts = _tree_struct(out)
+    rc = lib().tree_build_noalloc(C.byref(p), _ptr(block_logits), _ptr(U), _ptr(Wt),
+                                  _ptr(root_token), _ptr(n_budget), _ptr(tau), C.byref(ts),
+                                  _stream(stream))
+    if rc != DT_OK:
+        raise DtError("tree_build_noalloc", rc)
 
 
 def tree_verify_greedy(p: dt_params, tree: dict, target_logits: torch.Tensor, out: dict,

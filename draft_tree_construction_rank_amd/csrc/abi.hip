@@ -41,6 +41,10 @@ Layout make_layout(const dt_params* p) {
     L.nbeff = take(R * sizeof(int));
     L.rstat = take(R * sizeof(int));
     L.partials = take(cap_rows * rec_floats(L.KT) * sizeof(float));
+#ifdef DT_TRACE
+    L.trace = take((size_t)kMaxGrid * kTraceLevels * 16 * sizeof(uint64_t));
+#endif
+    L.build_total = off;  // everything below is used by the verifiers only
     L.vsplits = 0;
     L.vrow = L.vprow = L.vstate = L.vpart = 0;
     if (p->mode == DT_SAMPLE) {
@@ -67,9 +71,6 @@ Layout make_layout(const dt_params* p) {
         L.gsplits = (int)s;
         L.gpart = take(R * s * 8);
     }
-#ifdef DT_TRACE
-    L.trace = take((size_t)kMaxGrid * kTraceLevels * 16 * sizeof(uint64_t));
-#endif
     L.total = off;
     return L;
 }
@@ -127,49 +128,26 @@ static void timing_mark(hipStream_t st) {
 
 static void timing_hook(hipStream_t st, int) { timing_mark(st); }
 
-}  // namespace dt
-
-using namespace dt;
-
-extern "C" {
-
-const char* dt_status_string(dt_status s) {
-    switch (s) {
-        case DT_OK: return "DT_OK";
-        case DT_EINVAL: return "DT_EINVAL: invalid argument";
-        case DT_ENOSPC: return "DT_ENOSPC: workspace too small";
-        case DT_EDEVICE: return "DT_EDEVICE: HIP launch or device error";
-    }
-    return "unknown dt_status";
-}
-
-dt_status dt_build_workspace_bytes(const dt_params* p, size_t* bytes) {
+// ---- tree_build: argument checks and the enqueue shared by both entry points
+static dt_status check_build_args(const dt_params* p, const void* block_logits, const void* U,
+                                  const void* Wt, const int32_t* root_token,
+                                  const int32_t* n_budget, const float* tau, const dt_tree* out) {
     const dt_status v = validate(p);
     if (v != DT_OK) return v;
-    if (!bytes) return DT_EINVAL;
-    *bytes = make_layout(p).total;
+    if (!block_logits || !U || !Wt || !root_token || !n_budget || !tau || !tree_ptrs_ok(out))
+        return DT_EINVAL;
+    if (((uintptr_t)U & 15) || ((uintptr_t)Wt & 15) || ((uintptr_t)block_logits & 15))
+        return DT_EINVAL;
     return DT_OK;
 }
 
-dt_status tree_build(const dt_params* p, const void* block_logits, const void* U, const void* Wt,
-                     const int32_t* root_token, const int32_t* n_budget, const float* tau,
-                     const dt_tree* out, void* workspace, size_t ws_bytes, void* stream) {
-    const dt_status v = validate(p);
-    if (v != DT_OK) return v;
-    if (!block_logits || !U || !Wt || !root_token || !n_budget || !tau || !tree_ptrs_ok(out) ||
-        !workspace)
-        return DT_EINVAL;
-    if (((uintptr_t)U & 15) || ((uintptr_t)Wt & 15) || ((uintptr_t)block_logits & 15) ||
-        ((uintptr_t)workspace & 255))
-        return DT_EINVAL;
-    const Layout lay = make_layout(p);
-    if (ws_bytes < lay.total) return DT_ENOSPC;
-    hipStream_t st = (hipStream_t)stream;
-    char* ws = (char*)workspace;
-
+static dt_status enqueue_build(const dt_params* p, const Layout& lay, const void* block_logits,
+                               const void* U, const void* Wt, const int32_t* root_token,
+                               const int32_t* n_budget, const float* tau, const dt_tree* out,
+                               char* ws, hipStream_t st, bool timed) {
     const float Teff = (p->mode == DT_SAMPLE) ? p->temperature : 1.0f;
     BuildArgs a{};
-    a.timing_hook = g_timing.on ? timing_hook : nullptr;
+    a.timing_hook = timed ? timing_hook : nullptr;
     a.L = block_logits;
     a.U = U;
     a.Wt = Wt;
@@ -207,9 +185,82 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     a.round = p->round;
     a.logits_bf16 = p->logits_dtype == DT_BF16;
     for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
-
     if (launch_build(p, lay, a, st) != hipSuccess) return DT_EDEVICE;
     return DT_OK;
+}
+
+// ---- scratch of tree_build_noalloc: the construction workspace for callers that cannot
+// allocate.  One copy per device (each device that runs the library holds it until the
+// process ends).  In host code `scratch` only names the symbol: its device address is looked
+// up once per device with hipGetSymbolAddress and kept in g_scratch; kernels only ever get
+// that address.  Calls on one device share the array, so overlapping calls race.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchPtrs {
+    std::mutex mu;
+    char* ptr[kMaxDevices] = {};
+};
+static ScratchPtrs g_scratch;
+
+static char* scratch_ptr() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch.mu);
+    if (!g_scratch.ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch.ptr[dev] = (char*)ptr;
+    }
+    return g_scratch.ptr[dev];
+}
+
+}  // namespace dt
+
+using namespace dt;
+
+extern "C" {
+
+const char* dt_status_string(dt_status s) {
+    switch (s) {
+        case DT_OK: return "DT_OK";
+        case DT_EINVAL: return "DT_EINVAL: invalid argument";
+        case DT_ENOSPC: return "DT_ENOSPC: workspace too small";
+        case DT_EDEVICE: return "DT_EDEVICE: HIP launch or device error";
+    }
+    return "unknown dt_status";
+}
+
+dt_status dt_build_workspace_bytes(const dt_params* p, size_t* bytes) {
+    const dt_status v = validate(p);
+    if (v != DT_OK) return v;
+    if (!bytes) return DT_EINVAL;
+    *bytes = make_layout(p).total;
+    return DT_OK;
+}
+
+dt_status tree_build(const dt_params* p, const void* block_logits, const void* U, const void* Wt,
+                     const int32_t* root_token, const int32_t* n_budget, const float* tau,
+                     const dt_tree* out, void* workspace, size_t ws_bytes, void* stream) {
+    const dt_status v = check_build_args(p, block_logits, U, Wt, root_token, n_budget, tau, out);
+    if (v != DT_OK) return v;
+    if (!workspace || ((uintptr_t)workspace & 255)) return DT_EINVAL;
+    const Layout lay = make_layout(p);
+    if (ws_bytes < lay.total) return DT_ENOSPC;
+    return enqueue_build(p, lay, block_logits, U, Wt, root_token, n_budget, tau, out,
+                         (char*)workspace, (hipStream_t)stream, g_timing.on);
+}
+
+dt_status tree_build_noalloc(const dt_params* p, const void* block_logits, const void* U,
+                             const void* Wt, const int32_t* root_token, const int32_t* n_budget,
+                             const float* tau, const dt_tree* out, void* stream) {
+    const dt_status v = check_build_args(p, block_logits, U, Wt, root_token, n_budget, tau, out);
+    if (v != DT_OK) return v;
+    const Layout lay = make_layout(p);
+    if (lay.build_total > kScratchBytes) return DT_ENOSPC;
+    char* ws = scratch_ptr();
+    if (!ws) return DT_EDEVICE;
+    return enqueue_build(p, lay, block_logits, U, Wt, root_token, n_budget, tau, out, ws,
+                         (hipStream_t)stream, false);
 }
 
 dt_status tree_verify_greedy(const dt_params* p, const dt_tree* tree, const void* target_logits,

@@ -16,10 +16,13 @@ constexpr int kMaxB = 32;
 constexpr int kMaxK = 8;
 constexpr int kSelectSlots = 1024;  // >= Ncap + Ncap * k
 constexpr int kMaxSplits = 512;     // vocabulary splits per parent row (merge work bound)
-constexpr int kMaxGrid = 1024;      // largest grid of the persistent construction kernel
+constexpr int kMaxGrid = 256;       // largest grid of the persistent construction kernel
+                                    // (one workgroup per CU of an MI355X)
 constexpr int kBlockCols = 32;      // vocabulary columns per MFMA block of the expansion
 constexpr int kBuildWaves = 8;      // wavefronts per workgroup of the construction kernel
 constexpr int kGroupRows = 32 * kBuildWaves;  // parent rows per group-mode expansion item
+constexpr size_t kScratchBytes = DT_NOALLOC_SCRATCH_BYTES;  // device scratch of tree_build_noalloc
+constexpr int kMaxDevices = 64;
 
 // A frontier entry: a node that is (or was) expanded at some level.  self = the low word of
 // its selection key (0xFFFFFFFF for the root).
@@ -73,6 +76,7 @@ struct Layout {
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
     size_t gpart;     // (float, int) [R][gsplits]: greedy verify, split argmax of the root rows
     size_t trace;     // u64 [kMaxGrid][kTraceLevels][16]: phase timestamps (DT_TRACE builds only)
+    size_t build_total;  // extent of the regions tree_build uses (a prefix of the layout)
     size_t total;
     int G;            // largest grid of the construction kernel (sizes the partial records)
     int NC;           // vocabulary chunks of 128 columns

@@ -136,6 +136,23 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
                      const float* tau, const dt_tree* out, void* workspace, size_t ws_bytes,
                      void* stream);
 
+/* tree_build for callers that cannot allocate: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and results as tree_build without
+ * the workspace: the construction workspace is a fixed device array of
+ * DT_NOALLOC_SCRATCH_BYTES inside the library, one per device, reserved when the library's
+ * code is loaded on that device and kept until the process ends.  No device or host memory
+ * is allocated by the call (no hipMalloc, hipFree or allocating library routine), and
+ * timing (dt_timing_enable) does not apply to it.  DT_ENOSPC if dt_build_workspace_bytes()'s
+ * construction part for these parameters exceeds DT_NOALLOC_SCRATCH_BYTES (for example
+ * R = 64, B = 16, Ncap = 64 and k <= 8 fit).  Every call on one device uses the same array:
+ * calls that overlap on one device (concurrent streams or host threads) race and must be
+ * serialised by the caller; successive calls on one stream are fine (each clears what it
+ * needs at its start). */
+#define DT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dt_status tree_build_noalloc(const dt_params* p, const void* block_logits, const void* U,
+                             const void* Wt, const int32_t* root_token, const int32_t* n_budget,
+                             const float* tau, const dt_tree* out, void* stream);
+
 /* Greedy accept-walk (PCTree setup: greedy verification).
  *  tree          the dt_tree written by tree_build (device arrays; read only)
  *  target_logits [R][Ncap+1][V] (logits_dtype): row 0 = the root, row i+1 = node i

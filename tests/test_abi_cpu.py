@@ -106,3 +106,20 @@ def test_null_pointers_and_small_workspace_rejected(lib):
 def test_status_strings(lib):
     for code in range(4):
         assert B.status_string(code).startswith("DT_")
+
+
+def test_noalloc_rejects_rounds_beyond_its_scratch(lib):
+    """tree_build_noalloc checks its fixed scratch size on the host and returns DT_ENOSPC
+    (before touching the device) when the round's construction workspace would not fit;
+    bad parameters and null pointers are DT_EINVAL as for tree_build."""
+    t = B.dt_tree()
+    for f, _ in B.dt_tree._fields_:
+        setattr(t, f, 0x2000)
+    fake = 0x10000
+    big = _params(R=4096, B=32, Ncap=64, k=8)
+    assert lib.tree_build_noalloc(C.byref(big), fake, fake, fake, fake, fake, fake,
+                                  C.byref(t), None) == B.DT_ENOSPC
+    assert lib.tree_build_noalloc(C.byref(_params(R=0)), fake, fake, fake, fake, fake, fake,
+                                  C.byref(t), None) == B.DT_EINVAL
+    assert lib.tree_build_noalloc(C.byref(_params()), None, fake, fake, fake, fake, fake,
+                                  C.byref(t), None) == B.DT_EINVAL

@@ -1,0 +1,69 @@
+"""tree_build_noalloc (the construction workspace in the library's fixed device scratch)
+against tree_build with a caller workspace: two calls in a row on the same stream, the
+second with a smaller round, must give the same trees bit for bit; an oversized round is
+rejected with DT_ENOSPC."""
+import numpy as np
+import pytest
+
+from draft_tree_construction_rank_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("token", "parent", "depth", "anc_mask", "surv", "logq", "n_nodes", "cand", "status",
+          "n_expand", "level_rows")
+
+
+def _pair(inst, **pkw):
+    import torch
+    from draft_tree_construction_rank_amd import binding as B
+    from draft_tree_construction_rank_amd import runner as rt
+    rnd = rt.Round(inst, **pkw)
+    d = rt.to_device(inst)
+    rnd.build(d)
+    torch.cuda.synchronize()
+    ref = {f: rnd.tree[f].cpu().numpy().copy() for f in FIELDS}
+    out = B.alloc_tree(rnd.p, "cuda")
+    for v in out.values():
+        v.fill_(-7)  # every slot must be written by the call
+    B.tree_build_noalloc(rnd.p, d.L, d.U, d.Wt, d.root_token, d.n_budget, d.tau, out)
+    torch.cuda.synchronize()
+    got = {f: out[f].cpu().numpy() for f in FIELDS}
+    return ref, got
+
+
+def _same(ref, got):
+    for f in FIELDS:
+        assert np.array_equal(ref[f], got[f]), f
+
+
+def test_noalloc_equals_tree_build_two_calls():
+    import torch
+    assert torch.cuda.is_available()
+    # first call: the batched workload with full trees (group-mode levels, 64 requests)
+    big = inputs.make_instance("batched", tau=0.0)
+    print("noalloc call 1: batched R=64 B=16 k=4 N=64 V=151936 tau=0", flush=True)
+    ref, got = _pair(big)
+    assert ref["n_nodes"].sum() == 64 * 64
+    _same(ref, got)
+    # second call: a smaller round in sample mode (the scratch keeps the first call's
+    # contents; what must start from zero is cleared by the call)
+    small = inputs.make_instance("tiny", V=1000, R=3, B=5, k=3, Ncap=12, dtype="bf16",
+                                 mode="sample", temperature=0.8, seed=9)
+    print("noalloc call 2: R=3 B=5 k=3 N=12 V=1000 sample", flush=True)
+    ref, got = _pair(small)
+    assert ref["n_nodes"].min() > 0
+    _same(ref, got)
+
+
+def test_noalloc_rejects_oversized_round():
+    import torch
+    from draft_tree_construction_rank_amd import binding as B
+    from draft_tree_construction_rank_amd import runner as rt
+    inst = inputs.make_instance("tiny", V=64, R=600, B=16, k=8, Ncap=64, dtype="bf16")
+    p = rt.params_for(inst)
+    d = rt.to_device(inst)
+    out = B.alloc_tree(p, "cuda")
+    with pytest.raises(B.DtError) as e:
+        B.tree_build_noalloc(p, d.L, d.U, d.Wt, d.root_token, d.n_budget, d.tau, out)
+    assert e.value.code == B.DT_ENOSPC
+    torch.cuda.synchronize()

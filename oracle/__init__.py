@@ -215,13 +215,16 @@ def build_tree(inst, *, requests=None, method: int = 0, n_budget=None, tau=None,
     def one(rq):
         P = make_params(inst, R=1, mode=mode, temperature=temperature, round_=round_,
                         req_base=rq)
+        # every array handed to C is held in a local for the whole call (an address taken
+        # from a temporary would point at freed memory)
         L = _c32(inst.L[rq:rq + 1])
+        root = _c32(inst.root_token[rq:rq + 1], np.int32)
+        budget = _c32(nb[rq:rq + 1], np.int32)
+        thr = _c32(ta[rq:rq + 1])
         t = new_tree(1, inst.Ncap, inst.k)
         ts = _tree_struct(t)
         mg = new_margins(1)
-        rc = lib().or_build(C.byref(P), _p(L), _p(U), _p(Wt),
-                            _p(_c32(inst.root_token[rq:rq + 1], np.int32)),
-                            _p(_c32(nb[rq:rq + 1], np.int32)), _p(_c32(ta[rq:rq + 1])),
+        rc = lib().or_build(C.byref(P), _p(L), _p(U), _p(Wt), _p(root), _p(budget), _p(thr),
                             method, C.byref(ts), _p(mg))
         assert rc == 0
         return t, mg
@@ -326,8 +329,9 @@ def sample_rounds(inst, target_tab: np.ndarray, n_rounds: int, *, temperature=No
     first = np.zeros(n_rounds, np.int32)
     second = np.zeros(n_rounds, np.int32)
     nb = inst.Ncap if n_budget is None else n_budget
-    lib().or_sample_rounds(C.byref(P), _p(_c32(inst.L[:1])), _p(_c32(inst.U)),
-                           _p(_c32(inst.Wt)), int(inst.root_token[0]), int(nb), float(tau),
+    L, U, Wt = _c32(inst.L[:1]), _c32(inst.U), _c32(inst.Wt)  # alive for the whole call
+    lib().or_sample_rounds(C.byref(P), _p(L), _p(U), _p(Wt), int(inst.root_token[0]), int(nb),
+                           float(tau),
                            _p(tab), n_rounds, _p(first), _p(second))
     return first, second
 

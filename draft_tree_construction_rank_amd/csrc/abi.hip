@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -128,6 +129,18 @@ static void timing_mark(hipStream_t st) {
 
 static void timing_hook(hipStream_t st, int) { timing_mark(st); }
 
+// ---- bound of the construction kernel's internal waits: kSpinLimit polls, or the value of
+// the environment variable DT_WAIT_LIMIT (a test hook: a small bound makes a round give up
+// and report DT_REQ_SYNC_TIMEOUT while every kernel still exits normally)
+static uint32_t wait_limit() {
+    const char* e = std::getenv("DT_WAIT_LIMIT");
+    if (!e || !*e) return kSpinLimit;
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(e, &end, 10);
+    if (end == e || v < 1 || v > kSpinLimit) return kSpinLimit;
+    return (uint32_t)v;
+}
+
 // ---- tree_build: argument checks and the enqueue shared by both entry points
 static dt_status check_build_args(const dt_params* p, const void* block_logits, const void* U,
                                   const void* Wt, const int32_t* root_token,
@@ -184,6 +197,7 @@ static dt_status enqueue_build(const dt_params* p, const Layout& lay, const void
     a.seed_hi = (uint32_t)(p->seed >> 32);
     a.round = p->round;
     a.logits_bf16 = p->logits_dtype == DT_BF16;
+    a.spin_limit = wait_limit();
     for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
     if (launch_build(p, lay, a, st) != hipSuccess) return DT_EDEVICE;
     return DT_OK;

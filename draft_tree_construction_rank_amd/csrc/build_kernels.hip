@@ -95,20 +95,19 @@ __device__ __forceinline__ int block_sum(int v, int* sh) {
     return total;
 }
 
-// Upper bound on the iterations of one bounded wait (each sleeps ~128 cycles): about two
-// seconds, far above any level's work.
-constexpr uint32_t kSpinLimit = 1u << 25;
+// Bounded waits poll at most BuildArgs::spin_limit times (each poll sleeps ~128 cycles; the
+// default, kSpinLimit, is about two seconds, far above any level's work).
 
 // Thread 0 waits until *p >= target (or the error flag is set); the result is broadcast to
 // the workgroup.  Returns false on error or time-out.
 __device__ __forceinline__ bool wait_at_least(unsigned* sync, const unsigned* p, unsigned target,
-                                              int* bcast) {
+                                              int* bcast, uint32_t limit) {
     if (threadIdx.x == 0) {
         int ok = 1;
         uint32_t it = 0;
         while ((int)(cld32(p) - target) < 0) {
             __builtin_amdgcn_s_sleep(2);
-            if (++it > kSpinLimit) {
+            if (++it > limit) {
                 cst32(sync + kSyncErr, 1u);
                 ok = 0;
                 break;
@@ -129,14 +128,15 @@ __device__ __forceinline__ bool wait_at_least(unsigned* sync, const unsigned* p,
 
 // Thread 0 waits until the generation word's level reaches `level` (or the error flag is
 // set); the word is broadcast to the workgroup.  Returns false on error or time-out.
-__device__ __forceinline__ bool wait_gen(unsigned* sync, int level, int* bcast, uint64_t* gen) {
+__device__ __forceinline__ bool wait_gen(unsigned* sync, int level, int* bcast, uint64_t* gen,
+                                         uint32_t limit) {
     if (threadIdx.x == 0) {
         int ok = 1;
         uint32_t it = 0;
         uint64_t g;
         while ((int)((g = cld64(sync + kSyncGen)) & 0xFFu) < level) {
             __builtin_amdgcn_s_sleep(2);
-            if (++it > kSpinLimit) {
+            if (++it > limit) {
                 cst32(sync + kSyncErr, 1u);
                 ok = 0;
                 break;
@@ -156,6 +156,20 @@ __device__ __forceinline__ bool wait_gen(unsigned* sync, int level, int* bcast, 
     *gen = (uint64_t)(uint32_t)bcast[1] | ((uint64_t)(uint32_t)bcast[2] << 32);
     lds_sync();
     return ok;
+}
+
+// Work tickets of a level: thread 0 takes the next index of the level's counter and the
+// workgroup gets it through LDS.  Indices below T*S are expansion items, the next M are
+// merge rows, larger ones mean the level has no work left for this workgroup.  Tickets are
+// handed out in increasing order, so by the time any merge row is claimed every expansion
+// item has been claimed by a running workgroup: a workgroup only ever waits for work that
+// running workgroups hold, and a round completes with any number of resident workgroups.
+__device__ __forceinline__ int claim_ticket(unsigned* sync, int level, int* bcast) {
+    if (threadIdx.x == 0) bcast[0] = (int)cadd32(sync + kSyncClaim + level, 1u);
+    lds_sync();
+    const int c = bcast[0];
+    lds_sync();
+    return c;
 }
 
 // Vocabulary splits for T tiles on a grid of G workgroups: about one item per workgroup,
@@ -1379,11 +1393,11 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a) {
     if (tid == 0) *(uint64_t*)(a.sync + kSyncGen) = pack_gen(0, total, total);
 }
 
-// The level loop.  The grid is the kernel's resident capacity, launched plainly: workgroups
-// wait for each other's expansion items, so the loop relies on all of them being dispatched
-// eventually (they are, once any other work sharing the GPU drains; on an idle GPU all are
-// resident at once).  Every wait is bounded, so a grid that cannot be completed ends with
-// DT_REQ_SYNC_TIMEOUT instead of hanging.
+// The level loop.  The grid is the kernel's resident capacity, launched plainly.  Work is
+// handed out by per-level tickets (claim_ticket), so a workgroup only waits for work that
+// running workgroups hold: a round completes with any number of resident workgroups (a
+// workgroup dispatched late finds its level's tickets used up and goes on to the next level
+// or the emit).  Every wait is still bounded and reports DT_REQ_SYNC_TIMEOUT if it gives up.
 template <int KT, bool SAMPLE, bool HEAD_BF16, bool L_BF16>
 __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     __shared__ __attribute__((aligned(16))) BuildSmem<KT> sm;
@@ -1392,11 +1406,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
     bool failed = false;
     DT_STAMP(0, 0);
     if (tid < kMaxB + 2) sm.lrows[tid] = 0;  // levels never reached expand no rows
+    // the first ticket of a level is taken while the workgroup waits for the level to open
+    int ticket = claim_ticket(a.sync, 1, sm.bcast);
     for (int level = 1;; ++level) {
         // the previous level's selects are complete once the generation reaches level - 1;
         // the generation word also carries this level's row and request counts
         uint64_t gen;
-        if (!wait_gen(a.sync, level - 1, sm.bcast, &gen)) {
+        if (!wait_gen(a.sync, level - 1, sm.bcast, &gen, a.spin_limit)) {
             failed = true;
             break;
         }
@@ -1411,11 +1427,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
         const int GR = grp_mode ? kGroupRows : kTileRows;
         const int T = (M + GR - 1) / GR;
         const int S = splits_for(T, (int)gridDim.x, NB);
+        const int NI = T * S;
         unsigned* tdone = a.tdone + (size_t)level * a.Tmax;
-        // item i runs on workgroup i mod G.  Workgroups are dealt to the 8 XCDs round-robin,
-        // so when S and G are multiples of 8 split j of every row tile runs on one XCD, and a
-        // W block read for one tile is an L2 hit for the others.
-        for (int item = blockIdx.x; item < T * S; item += gridDim.x) {
+        // expansion items: ticket c is vocabulary split c % S of row tile (or group) c / S
+        for (; ticket < NI; ticket = claim_ticket(a.sync, level, sm.bcast)) {
+            const int item = ticket;
             if constexpr (HEAD_BF16 && L_BF16) {
                 if (grp_mode) expand_group<KT, SAMPLE>(a, level, M, S, item / S, item % S, sm);
                 else expand_item<KT, SAMPLE, HEAD_BF16, L_BF16>(a, level, M, S, item / S, item % S, sm);
@@ -1427,9 +1443,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
         }
         DT_STAMP(level, 2);
         bool first_task = true;
-        // merges: parent row m on workgroup m mod G, once all splits of its tile are in
-        for (int m = blockIdx.x; m < M; m += gridDim.x) {
-            if (!wait_at_least(a.sync, tdone + m / GR, (unsigned)S, sm.bcast)) {
+        // merges: ticket NI + m is parent row m, merged once all splits of its tile are in
+        for (; ticket < NI + M; ticket = claim_ticket(a.sync, level, sm.bcast)) {
+            const int m = ticket - NI;
+            if (!wait_at_least(a.sync, tdone + m / GR, (unsigned)S, sm.bcast, a.spin_limit)) {
                 failed = true;
                 break;
             }
@@ -1459,6 +1476,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_build(const BuildArgs a) {
         }
         DT_STAMP(level, 3);
         if (failed) break;
+        ticket = claim_ticket(a.sync, level + 1, sm.bcast);
     }
     DT_STAMP(kTraceLevels - 1, 0);
     if (failed) cst32(a.sync + kSyncErr, 1u);

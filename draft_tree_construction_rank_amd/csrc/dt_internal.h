@@ -23,6 +23,7 @@ constexpr int kBuildWaves = 8;      // wavefronts per workgroup of the construct
 constexpr int kGroupRows = 32 * kBuildWaves;  // parent rows per group-mode expansion item
 constexpr size_t kScratchBytes = DT_NOALLOC_SCRATCH_BYTES;  // device scratch of tree_build_noalloc
 constexpr int kMaxDevices = 64;
+constexpr uint32_t kSpinLimit = 1u << 25;  // default polls of one bounded wait (about 2 s)
 
 // A frontier entry: a node that is (or was) expanded at some level.  self = the low word of
 // its selection key (0xFFFFFFFF for the root).
@@ -107,7 +108,9 @@ constexpr int kSyncErr = 2;     // set when a bounded wait gives up
 constexpr int kSyncAlloc = 8;   // u64 [level]: rows allocated for that level
 constexpr int kSyncDone = 80;   // u64 [level]: (selects done << 48) | (requests with rows at
                                 // the next level << 32) | rows of the next level
-constexpr int kSyncWords = 160;
+constexpr int kSyncClaim = 160; // u32 [level]: work tickets handed out (expansion items, then
+                                // merge rows)
+constexpr int kSyncWords = 208;
 __host__ __device__ constexpr uint64_t pack_gen(int level, int nreq, int rows) {
     return ((uint64_t)(uint32_t)rows << 32) | ((uint64_t)(uint32_t)nreq << 8) | (uint64_t)level;
 }
@@ -145,6 +148,7 @@ struct BuildArgs {
     float invT;     // 1 / T' (sample ranking key)
     uint32_t seed_lo, seed_hi, round;
     int logits_bf16;
+    uint32_t spin_limit;  // iterations of a bounded wait before it gives up
     float cal[16];
 };
 

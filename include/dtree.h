@@ -26,6 +26,11 @@
  *  - Host-side argument errors return synchronously before anything is enqueued.
  *    Device-side data errors are reported per request in `status` and never abort.
  *  - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *  - tree_build's kernel hands its work out through per-level tickets, so a round completes
+ *    whatever number of its workgroups is resident at once (for example while another
+ *    kernel holds compute units).  Its internal waits are bounded (about two seconds); the
+ *    environment variable DT_WAIT_LIMIT, if set to a number of polls, lowers that bound
+ *    (a test hook that makes a round give up and report DT_REQ_SYNC_TIMEOUT).
  *
  * Markov head form: bias[p][c] = sum_j U[p][j] * W[j][c], a rank-r head shared by all block
  * positions (the pages fix what the head does, not its form).  W is passed TRANSPOSED,

@@ -227,3 +227,30 @@ def test_deterministic_repeat(rt):
     b = rt.tree_to_numpy(rnd.tree)
     for f in a:
         assert np.array_equal(a[f], b[f]), f
+
+
+def test_wait_give_up_reports_timeout(rt, monkeypatch):
+    """Forced from the host: DT_WAIT_LIMIT=1 makes the construction kernel's internal waits give
+    up after two polls (every kernel still exits normally).  Requests of a round that gave up
+    report DT_REQ_SYNC_TIMEOUT with an empty tree and the verifier emits nothing for them;
+    the next round, with the default bound, is complete again."""
+    import torch
+    inst = instance("tiny", strong=True, V=2048, r=32, B=4, k=4, Ncap=32, R=8, dtype="bf16")
+    monkeypatch.setenv("DT_WAIT_LIMIT", "1")
+    rnd, d, got = _gpu_round(rt, inst)
+    monkeypatch.delenv("DT_WAIT_LIMIT")
+    timed_out = (got["status"] & 4) != 0
+    assert timed_out.any(), got["status"]
+    assert (got["n_nodes"][timed_out] == 0).all()
+    assert (got["token"][timed_out] == -1).all()
+    tgt = np.zeros((inst.R, inst.Ncap + 1, inst.V), np.float32)
+    out = rnd.verify_greedy(rt.target_to_device(inst, tgt))
+    torch.cuda.synchronize()
+    assert (out["n_out"].cpu().numpy()[timed_out] == 0).all()
+    assert (out["accept_len"].cpu().numpy()[timed_out] == 0).all()
+    rnd.build(d)
+    torch.cuda.synchronize()
+    again = rt.tree_to_numpy(rnd.tree)
+    assert (again["status"] & 4 == 0).all() and (again["n_nodes"] == inst.Ncap).all()
+    for i in range(inst.R):
+        check_structure(inst, again, i)

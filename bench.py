@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft trees/sec & µs/round (B=16,k=4,N=64,V=151936); % HBM peak"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ("draft_tree_construction_rank_amd/csrc/build_kernels.hip",
                   "draft_tree_construction_rank_amd/csrc/dt_mma.h",
                   "draft_tree_construction_rank_amd/csrc/dt_device.h")
@@ -129,27 +130,87 @@ def run_workload(inst, tau, steps, warmup, torch, rt, B, timing=True):
                 target=tgt, level_rows=tree_np["level_rows"].tolist())
 
 
-def build_latency(inst, torch, rt, steps=30, warmup=5):
-    """Microseconds per tree_build call alone (one request, the B=16/k=4/N=64 headline)."""
+def _events(torch, n):
+    return [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n)]
+
+
+def _stats(us):
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 2), "p90": round(float(np.percentile(a, 90)), 2),
+            "mean": round(float(a.mean()), 2), "n": int(a.size)}
+
+
+class Flusher:
+    """Streams a 512 MiB buffer (read + write) to push earlier data out of the 256 MB
+    Infinity Cache (MALL) before a cold-timed round."""
+
+    def __init__(self, torch):
+        self.buf = torch.zeros((512 << 20) // 4, dtype=torch.int32, device="cuda")
+
+    def __call__(self):
+        self.buf.add_(1)
+
+
+def time_calls(torch, calls, n, flusher=None):
+    """Per-call event timing (µs) of each callable in `calls`, run in order n times on the
+    current stream; with a flusher the MALL is flushed before every repetition."""
+    evs = [_events(torch, n) for _ in calls]
+    for i in range(n):
+        if flusher is not None:
+            flusher()
+        for c, fn in enumerate(calls):
+            evs[c][i][0].record()
+            fn()
+            evs[c][i][1].record()
+    torch.cuda.synchronize()
+    return [[a.elapsed_time(b) * 1e3 for a, b in ev] for ev in evs]
+
+
+def build_profile(inst, torch, rt, flusher, steps=30, warmup=5, **pkw):
+    """tree_build alone on one workload: warm and cold µs per call (median/p90)."""
     d = rt.to_device(inst, "cuda")
-    rnd = rt.Round(inst)
+    rnd = rt.Round(inst, **pkw)
     for _ in range(warmup):
         rnd.build(d)
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        rnd.build(d)
-    e.record()
+    warm = time_calls(torch, [lambda: rnd.build(d)], steps)[0]
+    cold = time_calls(torch, [lambda: rnd.build(d)], max(10, steps // 3), flusher)[0]
+    return {"build_us_warm": _stats(warm), "build_us_cold": _stats(cold),
+            "trees_per_s": round(inst.R / (_stats(warm)["median"] * 1e-6), 1)}, rnd, d
+
+
+def greedy_round_profile(inst, tau, torch, rt, flusher, steps=30, warmup=5):
+    """tree_build + tree_verify_greedy per round: warm and cold medians, trees/s."""
+    d = rt.to_device(inst, "cuda", tau=tau)
+    rnd = rt.Round(inst)
+    rnd.build(d)
     torch.cuda.synchronize()
-    return s.elapsed_time(e) * 1e3 / steps
+    tgt = gpu_targets(inst, rnd.tree, inst.rho, 1234, torch)
+    for _ in range(warmup):
+        rnd.build(d)
+        rnd.verify_greedy(tgt)
+    torch.cuda.synchronize()
+    bw, vw = time_calls(torch, [lambda: rnd.build(d), lambda: rnd.verify_greedy(tgt)], steps)
+    bc, vc = time_calls(torch, [lambda: rnd.build(d), lambda: rnd.verify_greedy(tgt)],
+                        max(10, steps // 3), flusher)
+    rw = [a + b for a, b in zip(bw, vw)]
+    rc = [a + b for a, b in zip(bc, vc)]
+    tn = rt.tree_to_numpy(rnd.tree)
+    return {"round_us_warm": _stats(rw), "round_us_cold": _stats(rc),
+            "build_us_warm": _stats(bw), "verify_us_warm": _stats(vw),
+            "trees_per_s": round(inst.R / (_stats(rw)["median"] * 1e-6), 1),
+            "mean_nodes": round(float(tn["n_nodes"].mean()), 2),
+            "mean_expansions": round(float(tn["n_expand"].mean()), 2),
+            "mean_accept_len": round(float(rnd.vout["accept_len"].float().mean()), 3),
+            "level_rows": tn["level_rows"].tolist()}
 
 
-def sample_round_us(torch, rt, inputs, temperature, steps=20, warmup=3):
-    """Microseconds per lossless-sampling round on the sample workload (R=32, B=16, k=4,
-    N=64, V=151936): tree_build in sample mode (Gumbel-top-k siblings) followed by
-    tree_verify_sample (recursive rejection) against rho=0.7 targets; also the two parts."""
+def sample_round_us(torch, rt, inputs, temperature, flusher, steps=20, warmup=3):
+    """Lossless-sampling round on the sample workload (R=32, B=16, k=4, N=64, V=151936):
+    tree_build in sample mode (Gumbel-top-k siblings) followed by tree_verify_sample
+    (recursive rejection) against rho=0.7 targets; also the two parts."""
     inst = inputs.make_instance("sample", temperature=temperature)
     d = rt.to_device(inst, "cuda")
     rnd = rt.Round(inst)
@@ -160,44 +221,97 @@ def sample_round_us(torch, rt, inputs, temperature, steps=20, warmup=3):
         rnd.build(d)
         rnd.verify_sample(d, tgt)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    tb = tv = 0.0
-    for _ in range(steps):
-        ev[0].record()
-        rnd.build(d)
-        ev[1].record()
-        rnd.verify_sample(d, tgt)
-        ev[2].record()
-        torch.cuda.synchronize()
-        tb += ev[0].elapsed_time(ev[1])
-        tv += ev[1].elapsed_time(ev[2])
+    bw, vw = time_calls(torch, [lambda: rnd.build(d), lambda: rnd.verify_sample(d, tgt)], steps)
+    bc, vc = time_calls(torch, [lambda: rnd.build(d), lambda: rnd.verify_sample(d, tgt)],
+                        max(10, steps // 2), flusher)
     acc = float(rnd.vout["accept_len"].float().mean())
-    return {"round_us": round((tb + tv) * 1e3 / steps, 2), "build_us": round(tb * 1e3 / steps, 2),
-            "verify_us": round(tv * 1e3 / steps, 2), "mean_accept_len": round(acc, 3)}
+    return {"round_us_warm": _stats([a + b for a, b in zip(bw, vw)]),
+            "round_us_cold": _stats([a + b for a, b in zip(bc, vc)]),
+            "build_us_warm": _stats(bw), "verify_us_warm": _stats(vw),
+            "trees_per_s": round(inst.R / (_stats([a + b for a, b in zip(bw, vw)])["median"] * 1e-6), 1),
+            "mean_accept_len": round(acc, 3)}
 
 
-def cpu_baseline(inst, tau, res, budget_s=20.0):
+def kbuild_fractions(inst, res, B):
+    """HBM and MFMA fractions of k_build for a measured workload (alg bytes and flops per
+    launch over the event-timed average launch)."""
+    steps_launch = max(1, res["expand_launches"])
+    avg_us = res["expand_ms"] * 1e3 / steps_launch
+    alg = algorithmic_bytes(inst, res["levels_used"], res["n_expand"])
+    flops = sum(res["n_expand"]) * 2.0 * inst.r * inst.V
+    return {"k_build_avg_us": round(avg_us, 2), "alg_bytes_per_launch": int(alg),
+            "hbm_gbs": round(alg / (avg_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(alg / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_flops_per_launch": int(flops),
+            "mfma_tflops": round(flops / (avg_us * 1e-6) / 1e12, 2),
+            "mfma_frac": round(flops / (avg_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
+def host_model():
+    try:
+        return [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
+                if ln.startswith("model name")][0]
+    except Exception:
+        return platform.processor()
+
+
+class pinned_single_thread:
+    """Runs the oracle single-threaded on one core: the calling thread's affinity is set to
+    one CPU (the first one this process may use) and oracle calls run without a pool."""
+
+    def __enter__(self):
+        self.old_aff = os.sched_getaffinity(0)
+        self.core = min(self.old_aff)
+        os.sched_setaffinity(0, {self.core})
+        self.old_env = os.environ.get("DT_ORACLE_THREADS")
+        os.environ["DT_ORACLE_THREADS"] = "1"
+        return self
+
+    def __exit__(self, *a):
+        os.sched_setaffinity(0, self.old_aff)
+        if self.old_env is None:
+            os.environ.pop("DT_ORACLE_THREADS", None)
+        else:
+            os.environ["DT_ORACLE_THREADS"] = self.old_env
+
+
+def cpu_baseline(inst, tau, res, budget_s=15.0):
     """The oracle, as it stands, on a bounded sample: build + greedy verify of the first
-    requests of the same workload until ~budget_s of CPU time (single thread)."""
-    import numpy as np
+    requests of the same workload until ~budget_s of CPU time, single thread on one core."""
     import oracle
     oracle.build(force=False)
     tgt = res["target"]
-    done, t0 = 0, time.perf_counter()
-    while done < inst.R and time.perf_counter() - t0 < budget_s:
-        row = tgt[done:done + 1].float().cpu().numpy()
-        tr = oracle.build_tree(inst, requests=[done], tau=tau)
-        oracle.verify_greedy(inst, tr, row)
-        done += 1
-    dt = time.perf_counter() - t0
-    try:
-        model = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo")
-                 if ln.startswith("model name")][0]
-    except Exception:
-        model = platform.processor()
-    return {"value": done / dt, "unit": "trees/s", "cores": 1, "kind": "oracle",
-            "sample": "first %d of %d requests (build + greedy verify, single thread, %.1f s); "
-                      "host %s, %d cores" % (done, inst.R, dt, model, os.cpu_count() or 0)}
+    with pinned_single_thread() as pin:
+        done, t0 = 0, time.perf_counter()
+        while done < inst.R and time.perf_counter() - t0 < budget_s:
+            row = tgt[done:done + 1].float().cpu().numpy()
+            tr = oracle.build_tree(inst, requests=[done], tau=tau)
+            oracle.verify_greedy(inst, tr, row)
+            done += 1
+        dt = time.perf_counter() - t0
+    return {"value": round(done / dt, 3), "unit": "trees/s", "cores": 1, "kind": "oracle",
+            "sample": "first %d of %d requests of the same workload (build + greedy verify), "
+                      "%.1f s, one thread pinned to CPU %d; host %s, nproc %d" % (
+                          done, inst.R, dt, pin.core, host_model(), len(os.sched_getaffinity(0)))}
+
+
+def oracle_per_config(inputs, rounds=3):
+    """The oracle's µs per round (build, one thread, one core; median of `rounds`) on the
+    single-request workloads."""
+    import numpy as np
+    import oracle
+    out = {}
+    with pinned_single_thread():
+        for name in ("tiny", "b7", "b16"):
+            inst = inputs.make_instance(name)
+            ts = []
+            for _ in range(rounds):
+                t0 = time.perf_counter()
+                oracle.build_tree(inst)
+                ts.append((time.perf_counter() - t0) * 1e6)
+            med = float(np.median(ts))
+            out[name] = {"build_us_median": round(med, 1), "trees_per_s": round(1e6 / med, 3)}
+    return out
 
 
 def main():
@@ -269,14 +383,49 @@ def main():
                            "mean_accept_len": float(res["verify"]["accept_len"].mean()),
                            "level_rows": res["level_rows"]}}
     if not args.no_extras:
+        flusher = Flusher(torch)
         extras = {}
-        h = inputs.make_instance("b16")
-        extras["tree_build_us_R1_B16_k4_N64"] = round(build_latency(h, torch, rt), 2)
+        # the headline workload per round: warm and cold (MALL flushed), median and p90
+        extras["headline_per_round"] = greedy_round_profile(inst, args.tau, torch, rt, flusher)
+        # full trees: tau = 0 keeps 64 nodes per request (65 expansions each), the regime
+        # where the expansion's MFMA work binds
+        full = run_workload(inst, 0.0, 20, 3, torch, rt, B)
+        fx = kbuild_fractions(inst, full, B)
+        fx.update(greedy_round_profile(inst, 0.0, torch, rt, flusher))
+        extras["batched_tau0_full_trees"] = fx
         for t in (0.2, 0.5):
             if t != args.tau:
-                r2 = run_workload(inst, t, 20, 3, torch, rt, B, timing=False)
-                extras["batched_tau%g_trees_per_s" % t] = round(inst.R / (r2["ms_per_step"] * 1e-3), 1)
-        extras["sample_T1.0_R32"] = sample_round_us(torch, rt, inputs, 1.0)
+                r2 = run_workload(inst, t, 20, 3, torch, rt, B)
+                e = kbuild_fractions(inst, r2, B)
+                e["trees_per_s"] = round(inst.R / (r2["ms_per_step"] * 1e-3), 1)
+                e["us_per_round"] = round(r2["ms_per_step"] * 1e3, 2)
+                extras["batched_tau%g" % t] = e
+        # single-request workloads: tree_build latency, warm and cold
+        per = {}
+        for name in ("tiny", "b7"):
+            per[name] = build_profile(inputs.make_instance(name), torch, rt, flusher)[0]
+        h = inputs.make_instance("b16")
+        sweep = {}
+        for k in (1, 2, 4, 8):
+            for n in (16, 32, 64):
+                hk = inputs.make_instance("b16", k=k, Ncap=n) if (k, n) != (4, 64) else h
+                sweep["k%d_N%d" % (k, n)] = build_profile(hk, torch, rt, flusher)[0]
+        per["b16_sweep"] = sweep
+        extras["per_config"] = per
+        extras["tree_build_us_R1_B16_k4_N64"] = sweep["k4_N64"]["build_us_warm"]["median"]
+        extras["sample"] = {"T%g" % T: sample_round_us(torch, rt, inputs, T, flusher)
+                            for T in (0.6, 1.0, 1.5)}
+        extras["targets"] = {
+            "tree_build_us_R1_B16_k4_N64": {"measured_median": extras["tree_build_us_R1_B16_k4_N64"],
+                                            "target": 100.0,
+                                            "met": extras["tree_build_us_R1_B16_k4_N64"] < 100.0},
+            "batched_hbm_frac_target": 0.6,
+            "batched_hbm_frac": {("tau%g" % t): (roof["frac"] if t == args.tau else
+                                                 extras.get("batched_tau%g" % t, {}).get("hbm_frac"))
+                                 for t in (0.05, 0.2, 0.5)},
+            "batched_full_trees": {"hbm_frac": fx["hbm_frac"], "mfma_frac": fx["mfma_frac"]}}
+        if not args.no_cpu_baseline:
+            extras["oracle_per_config"] = oracle_per_config(inputs)
         line["extras"] = extras
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inst, args.tau, res)

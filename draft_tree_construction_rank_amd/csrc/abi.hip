@@ -14,7 +14,7 @@ namespace dt {
 
 static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Layout make_layout(const dt_params* p) {
+Layout make_layout(const dt_params* p, bool allow_resident) {
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -29,7 +29,10 @@ Layout make_layout(const dt_params* p) {
     const size_t tmax = (R * N + kTileRows - 1) / kTileRows;
     // records: (parent row, vocabulary split) pairs; a level of T row groups of g rows uses
     // at most g * max(G, T) of them (g = kTileRows in tile mode, kGroupRows in group mode)
-    const size_t cap_rows = (size_t)kGroupRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
+    size_t cap_rows = (size_t)kGroupRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
+    // the W-resident kernel writes one record per parent row and workgroup
+    L.resident = allow_resident && resident_params_ok(p);
+    if (L.resident && R * N * (size_t)kMaxGrid > cap_rows) cap_rows = R * N * (size_t)kMaxGrid;
     L.sync = take(kSyncWords * sizeof(unsigned));
     L.tdone = take((B + 2) * (size_t)max_tiles((int)R, (int)N) * sizeof(unsigned));
     L.rdone = take((B + 2) * R * sizeof(unsigned));
@@ -42,9 +45,6 @@ Layout make_layout(const dt_params* p) {
     L.nbeff = take(R * sizeof(int));
     L.rstat = take(R * sizeof(int));
     L.partials = take(cap_rows * rec_floats(L.KT) * sizeof(float));
-#ifdef DT_TRACE
-    L.trace = take((size_t)kMaxGrid * kTraceLevels * 16 * sizeof(uint64_t));
-#endif
     L.build_total = off;  // everything below is used by the verifiers only
     L.vsplits = 0;
     L.vrow = L.vprow = L.vstate = L.vpart = 0;
@@ -72,6 +72,11 @@ Layout make_layout(const dt_params* p) {
         L.gsplits = (int)s;
         L.gpart = take(R * s * 8);
     }
+#ifdef DT_TRACE
+    // phase timestamps (instrumented builds only): last, and counted in the build's extent
+    L.trace = take((size_t)kMaxGrid * kTraceLevels * 16 * sizeof(uint64_t));
+    L.build_total = off;
+#endif
     L.total = off;
     return L;
 }
@@ -258,7 +263,10 @@ dt_status tree_build(const dt_params* p, const void* block_logits, const void* U
     const dt_status v = check_build_args(p, block_logits, U, Wt, root_token, n_budget, tau, out);
     if (v != DT_OK) return v;
     if (!workspace || ((uintptr_t)workspace & 255)) return DT_EINVAL;
-    const Layout lay = make_layout(p);
+    // the W-resident kernel's layout when the workspace holds it (dt_build_workspace_bytes
+    // returns that size), else the streaming kernel's
+    Layout lay = make_layout(p, true);
+    if (ws_bytes < lay.total) lay = make_layout(p, false);
     if (ws_bytes < lay.total) return DT_ENOSPC;
     return enqueue_build(p, lay, block_logits, U, Wt, root_token, n_budget, tau, out,
                          (char*)workspace, (hipStream_t)stream, g_timing.on);
@@ -269,7 +277,8 @@ dt_status tree_build_noalloc(const dt_params* p, const void* block_logits, const
                              const float* tau, const dt_tree* out, void* stream) {
     const dt_status v = check_build_args(p, block_logits, U, Wt, root_token, n_budget, tau, out);
     if (v != DT_OK) return v;
-    const Layout lay = make_layout(p);
+    Layout lay = make_layout(p, true);
+    if (lay.build_total > kScratchBytes) lay = make_layout(p, false);
     if (lay.build_total > kScratchBytes) return DT_ENOSPC;
     char* ws = scratch_ptr();
     if (!ws) return DT_EDEVICE;

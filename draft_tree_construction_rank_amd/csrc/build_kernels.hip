@@ -590,11 +590,8 @@ static hipError_t launch_build_t(const BuildArgs& a, hipStream_t st) {
     const int G = resident_grid(f);
     if (G < 1) return hipErrorLaunchFailure;
     {
-        // enough workgroups to clear the per-level counters in a few stores per thread
-        const size_t words = (size_t)(a.B + 2) * (a.Tmax + a.R);
-        int g = (int)((words + 256 * 16 - 1) / (256 * 16));
-        g = g < 1 ? 1 : (g > 256 ? 256 : g);
-        hipLaunchKernelGGL(k_build_init, dim3(g), dim3(256), 0, st, a);
+        const hipError_t e = launch_build_init(a, st);
+        if (e != hipSuccess) return e;
     }
     if (a.timing_hook) a.timing_hook(st, 0);
     // a plain launch: the loop needs no co-residency guarantee (see k_build), and a
@@ -619,8 +616,22 @@ static hipError_t launch_build_kt(const dt_params* p, const BuildArgs& a, hipStr
                                 : launch_build_ks<KT, false>(p, a, st);
 }
 
+hipError_t launch_build_init(const BuildArgs& a, hipStream_t st) {
+    // enough workgroups to clear the per-level counters in a few stores per thread
+    const size_t words = (size_t)(a.B + 2) * (a.Tmax + a.R);
+    int g = (int)((words + 256 * 16 - 1) / (256 * 16));
+    g = g < 1 ? 1 : (g > 256 ? 256 : g);
+    hipLaunchKernelGGL(k_build_init, dim3(g), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_build(const dt_params* p, const Layout& lay, const BuildArgs& a,
                         hipStream_t st) {
+    if (lay.resident) {
+        bool used = false;
+        const hipError_t e = launch_build_resident(p, lay, a, st, &used);
+        if (used || e != hipSuccess) return e;
+    }
     switch (lay.KT) {
         case 1: return launch_build_kt<1>(p, a, st);
         case 2: return launch_build_kt<2>(p, a, st);

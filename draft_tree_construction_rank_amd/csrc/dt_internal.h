@@ -24,6 +24,8 @@ constexpr int kGroupRows = 32 * kBuildWaves;  // parent rows per group-mode expa
 constexpr size_t kScratchBytes = DT_NOALLOC_SCRATCH_BYTES;  // device scratch of tree_build_noalloc
 constexpr int kMaxDevices = 64;
 constexpr uint32_t kSpinLimit = 1u << 25;  // default polls of one bounded wait (about 2 s)
+constexpr int kResMaxBlocks = 20;  // W-resident kernel: largest vocabulary slice (32-column blocks)
+constexpr int kCountRows = 32;     // rows per tdone counter (the smallest expansion tile)
 
 // A frontier entry: a node that is (or was) expanded at some level.  self = the low word of
 // its selection key (0xFFFFFFFF for the root).
@@ -84,9 +86,12 @@ struct Layout {
     int KT;           // top-k list length used by the kernels (1, 2, 4 or 8)
     int vsplits;      // vocabulary splits per request in sample verify
     int gsplits;      // vocabulary splits per request of the root-row argmax in greedy verify
+    bool resident;    // partials sized for the W-resident kernel
 };
 
-Layout make_layout(const dt_params* p);
+// allow_resident: size the partial records for the W-resident kernel too (one record per
+// row and workgroup), which needs more workspace than the streaming kernel.
+Layout make_layout(const dt_params* p, bool allow_resident = true);
 
 inline int kt_for(int k) { return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8; }
 
@@ -155,8 +160,25 @@ struct BuildArgs {
 // Host-side launchers (enqueue only).
 hipError_t launch_build(const dt_params* p, const Layout& lay, const BuildArgs& a,
                         hipStream_t st);
-// Tiles of kTileRows parent rows needed for R * Ncap rows.
-inline int max_tiles(int R, int Ncap) { return (R * Ncap + kTileRows - 1) / kTileRows; }
+// tdone counters per level: one per kCountRows parent rows (both kernels index them by a
+// row tile of at least that many rows).
+inline int max_tiles(int R, int Ncap) { return (R * Ncap + kCountRows - 1) / kCountRows; }
+// W-resident construction (build_resident.hip): bf16 head and logits, r = 256, V a
+// multiple of 8, and rounds of at most kResMaxRows parent rows per level (R * Ncap): every
+// workgroup of that kernel expands every row over its slice, which loses to the streaming
+// kernel once levels get wide (measured: 64 requests of 64 nodes ran 1.3x to 2x slower).
+// The slice-size check needs the device and happens at launch.
+constexpr int kResMaxRows = 128;
+inline bool resident_params_ok(const dt_params* p) {
+    return p->head_dtype == DT_BF16 && p->logits_dtype == DT_BF16 && p->r == 256 &&
+           (p->V & 7) == 0 && p->R * p->Ncap <= kResMaxRows;
+}
+// Set-up kernel of a round (control words, counters, roots); shared by both kernels.
+hipError_t launch_build_init(const BuildArgs& a, hipStream_t st);
+// Enqueues the W-resident kernel if it applies on the current device (*used); otherwise
+// enqueues nothing.
+hipError_t launch_build_resident(const dt_params* p, const Layout& lay, const BuildArgs& a,
+                                 hipStream_t st, bool* used);
 hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
                                 const dt_tree* tree, const void* target,
                                 const dt_verify_out* out, hipStream_t st);

@@ -32,8 +32,15 @@ def _pair(inst, **pkw):
 
 
 def _same(ref, got):
+    """Discrete outputs and survival bit for bit; logq within 1e-5 * max(1, |ref|) (when the
+    round's W-resident workspace does not fit the fixed scratch, the call runs the streaming
+    construction kernel, whose log-sum-exp adds in another order)."""
     for f in FIELDS:
-        assert np.array_equal(ref[f], got[f]), f
+        if f == "logq":
+            a, b = ref[f].astype(np.float64), got[f].astype(np.float64)
+            assert (np.abs(a - b) <= 1e-5 * np.maximum(1.0, np.abs(a))).all(), f
+        else:
+            assert np.array_equal(ref[f], got[f]), f
 
 
 def test_noalloc_equals_tree_build_two_calls():

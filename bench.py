@@ -232,6 +232,82 @@ def sample_round_us(torch, rt, inputs, temperature, flusher, steps=20, warmup=3)
             "mean_accept_len": round(acc, 3)}
 
 
+def _hashed_normal(torch, keys, V, sd):
+    """N(0, sd) rows keyed by int64 `keys` (one row per key): SplitMix64-style mixing of
+    (key, column) to a uniform, then the inverse normal CDF.  Bench input synthesis only."""
+    M = (1 << 64) - 1
+    c1, c2, g = 0xBF58476D1CE4E5B9, 0x94D049BB133111EB, 0x9E3779B97F4A7C15
+
+    def s64(x):  # as signed int64
+        return x - (1 << 64) if x >= (1 << 63) else x
+
+    def srl(z, k):  # logical right shift of int64
+        return (z >> k) & ((1 << (64 - k)) - 1)
+
+    def mix(z):
+        z = z + s64(g)
+        z = (z ^ srl(z, 30)) * s64(c1)
+        z = (z ^ srl(z, 27)) * s64(c2)
+        return z ^ srl(z, 31)
+
+    cols = torch.arange(V, device=keys.device, dtype=torch.int64)
+    z = mix(mix(keys.view(-1, 1)) ^ cols.view(1, -1))
+    u = (srl(z, 40).to(torch.float64) + 0.5) / float(1 << 24)
+    return (torch.erfinv(2.0 * u - 1.0) * (math.sqrt(2.0) * sd)).to(torch.float32)
+
+
+def markov_target(torch, inst, d, tree, rho):
+    """Target rows [R][N+1][V] of a Markov target model: row(v) = rho * (L[d_v] + U[t_v].W)
+    + sqrt(1 - rho^2) * E(request, d_v, t_v), a function of the node's depth and token only,
+    so every tree variant is verified against the same model."""
+    R, N1, V = inst.R, tree["token"].shape[1] + 1, inst.V
+    dev = d.L.device
+    tok = torch.cat([d.root_token.view(R, 1).to(torch.int64), tree["token"].to(torch.int64)], 1)
+    dep = torch.cat([torch.zeros((R, 1), dtype=torch.int64, device=dev),
+                     tree["depth"].to(torch.int64)], 1)
+    tok = torch.where(tok >= 0, tok, tok[:, :1].expand_as(tok))  # empty slots: the root
+    out = torch.empty((R, N1, V), dtype=torch.bfloat16, device=dev)
+    b = math.sqrt(max(0.0, 1.0 - rho * rho))
+    Wt = d.Wt.float()
+    for r in range(R):
+        bias = d.U[tok[r]].float() @ Wt.t()                                  # [N1][V]
+        Lrow = d.L[r].float()[dep[r].clamp(max=inst.B - 1)]                  # [N1][V]
+        keys = (r * 1000003 + dep[r]) * 4000037 + tok[r]
+        out[r] = (rho * (Lrow + bias) + b * _hashed_normal(torch, keys, V, 2.0)).to(torch.bfloat16)
+    return out
+
+
+def mechanism_isolation(torch, rt, inputs, rho=0.8):
+    """Chain (k = 1), Shared-Markov (chain head), parent-conditioned and marginal (no head)
+    trees of the batched workload with a strong head (R = 64, B = 16, N = 64, k = 4,
+    tau = 0), greedily verified against one Markov target: mean accepted draft nodes."""
+    import numpy as np
+    from draft_tree_construction_rank_amd import binding as Bd
+    inst = inputs.make_instance("batched", strong_head=True, tau=0.0)
+    d = rt.to_device(inst, "cuda", tau=0.0)
+    out = {}
+    variants = [("chain_k1", dict(k=1, Ncap=inst.B, cond=Bd.DT_COND_PARENT)),
+                ("shared_markov", dict(cond=Bd.DT_COND_CHAIN)),
+                ("pctree", dict(cond=Bd.DT_COND_PARENT)),
+                ("marginal", dict(cond=Bd.DT_COND_NONE))]
+    for name, kw in variants:
+        rnd = rt.Round(inst, **kw)
+        nb = torch.full((inst.R,), rnd.p.Ncap, dtype=torch.int32, device="cuda")
+        dd = rt.DeviceInputs(L=d.L, U=d.U, Wt=d.Wt, root_token=d.root_token, n_budget=nb, tau=d.tau)
+        rnd.build(dd)
+        torch.cuda.synchronize()
+        tgt = markov_target(torch, inst, d, rnd.tree, rho)
+        rnd.verify_greedy(tgt)
+        torch.cuda.synchronize()
+        acc = rnd.vout["accept_len"].float().cpu().numpy()
+        us = time_calls(torch, [lambda: rnd.build(dd)], 10)[0]
+        out[name] = {"mean_accept_len": round(float(acc.mean()), 3),
+                     "sem": round(float(acc.std(ddof=1) / np.sqrt(len(acc))), 3),
+                     "tree_build_us_median": _stats(us)["median"]}
+        del tgt
+    return out
+
+
 def kbuild_fractions(inst, res, B):
     """HBM and MFMA fractions of k_build for a measured workload (alg bytes and flops per
     launch over the event-timed average launch)."""
@@ -415,6 +491,7 @@ def main():
         extras["tree_build_us_R1_B16_k4_N64"] = sweep["k4_N64"]["build_us_warm"]["median"]
         extras["sample"] = {"T%g" % T: sample_round_us(torch, rt, inputs, T, flusher)
                             for T in (0.6, 1.0, 1.5)}
+        extras["mechanism_isolation_markov_target"] = mechanism_isolation(torch, rt, inputs)
         extras["targets"] = {
             "tree_build_us_R1_B16_k4_N64": {"measured_median": extras["tree_build_us_R1_B16_k4_N64"],
                                             "target": 100.0,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libdtree.so")
 DT_OK, DT_EINVAL, DT_ENOSPC, DT_EDEVICE = 0, 1, 2, 3
 DT_F32, DT_BF16 = 0, 1
 DT_GREEDY, DT_SAMPLE = 0, 1
+DT_COND_PARENT, DT_COND_CHAIN, DT_COND_NONE = 0, 1, 2
 DT_REQ_BAD_ROOT, DT_REQ_BUDGET_CLAMPED = 1, 2
 
 EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_build_noalloc", "tree_verify_greedy",
@@ -36,7 +37,7 @@ class dt_params(C.Structure):
                 ("r", C.c_int32), ("Ncap", C.c_int32), ("logits_dtype", C.c_int32),
                 ("head_dtype", C.c_int32), ("mode", C.c_int32), ("temperature", C.c_float),
                 ("cal", C.c_float * 16), ("seed", C.c_uint64), ("round", C.c_uint32),
-                ("reserved", C.c_uint32)]
+                ("cond", C.c_uint32)]
 
 
 class dt_tree(C.Structure):
@@ -92,7 +93,7 @@ def status_string(code: int) -> str:
 
 def make_params(*, R: int, B: int, k: int, V: int, r: int, Ncap: int, logits_dtype: int,
                 head_dtype: int, mode: int, temperature: float, cal: Sequence[float],
-                seed: int = 0, round_: int = 0) -> dt_params:
+                seed: int = 0, round_: int = 0, cond: int = 0) -> dt_params:
     p = dt_params()
     p.R, p.B, p.k, p.V, p.r, p.Ncap = R, B, k, V, r, Ncap
     p.logits_dtype, p.head_dtype, p.mode = logits_dtype, head_dtype, mode
@@ -101,7 +102,7 @@ def make_params(*, R: int, B: int, k: int, V: int, r: int, Ncap: int, logits_dty
         p.cal[i] = float(cal[i])
     p.seed = int(seed)
     p.round = int(round_)
-    p.reserved = 0
+    p.cond = int(cond)
     return p
 
 

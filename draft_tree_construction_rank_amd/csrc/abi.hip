@@ -99,7 +99,9 @@ static dt_status validate(const dt_params* p) {
         if (!(c >= 0.0f && c <= 1.0f)) return DT_EINVAL;
         if (i > 0 && c < p->cal[i - 1]) return DT_EINVAL;
     }
-    if (p->reserved != 0) return DT_EINVAL;
+    if (p->cond != DT_COND_PARENT && p->cond != DT_COND_CHAIN && p->cond != DT_COND_NONE)
+        return DT_EINVAL;
+    if (p->cond != DT_COND_PARENT && p->mode != DT_GREEDY) return DT_EINVAL;
     return DT_OK;
 }
 
@@ -203,6 +205,7 @@ static dt_status enqueue_build(const dt_params* p, const Layout& lay, const void
     a.round = p->round;
     a.logits_bf16 = p->logits_dtype == DT_BF16;
     a.spin_limit = wait_limit();
+    a.cond = (int)p->cond;
     for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
     if (launch_build(p, lay, a, st) != hipSuccess) return DT_EDEVICE;
     return DT_OK;

@@ -85,11 +85,13 @@ __device__ __forceinline__ void expand_item(const BuildArgs& a, int level, int M
         uint64_t hh = 0;
         if (tid < nrows) {
             const RowRec* rr = level_rows(a, level) + m0 + tid + opaque_zero();
-            const uint64_t w0 = cld64(rr), w1 = cld64((const char*)rr + 8);
+            const uint64_t w0 = cld64(rr), w3 = cld64((const char*)rr + 24);
             hh = cld64((const char*)rr + 16);
             const int req = (int)(uint32_t)w0;
-            tok = (int)(uint32_t)w1;
-            tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
+            // the head token selects the U row; -1 (no bias) gives a zero row below, and
+            // U is never indexed out of range
+            tok = (int)(uint32_t)(w3 >> 32);
+            tok = tok < 0 ? -1 : ((uint32_t)tok < (uint32_t)a.V ? tok : 0);
             lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
         }
         sm.tok[tid] = tok;
@@ -300,16 +302,19 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
     int tok = 0;
     size_t lb = 0;
     uint64_t hh = 0;
+    bool bias = false;
     if (live) {
         const RowRec* rr = level_rows(a, level) + row;
-        const uint64_t w0 = cld64(rr), w1 = cld64((const char*)rr + 8);
+        const uint64_t w0 = cld64(rr), w3 = cld64((const char*)rr + 24);
         hh = cld64((const char*)rr + 16);
         const int req = (int)(uint32_t)w0;
-        tok = (int)(uint32_t)w1;
-        tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
+        // the head token selects the U row (-1: no bias); U is never indexed out of range
+        tok = (int)(uint32_t)(w3 >> 32);
+        bias = tok >= 0;
+        tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;
         lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
     }
-    // B fragments: U[tok][16 s + 8 h .. +8], zero past r
+    // B fragments: U[tok][16 s + 8 h .. +8], zero past r and for rows without a bias
     bf16x8 uf[16];
     {
         const uint16_t* urow = (const uint16_t*)a.U + (size_t)tok * a.r;
@@ -317,7 +322,7 @@ __device__ __forceinline__ void expand_group(const BuildArgs& a, int level, int 
         for (int s = 0; s < 16; ++s) {
             const int kk = 16 * s + 8 * h;
             const uint4 v = *(const uint4*)(urow + (kk < a.r ? kk : 0));
-            uf[s] = __builtin_bit_cast(bf16x8, kk < a.r ? v : make_uint4(0, 0, 0, 0));
+            uf[s] = __builtin_bit_cast(bf16x8, (kk < a.r && bias) ? v : make_uint4(0, 0, 0, 0));
         }
     }
     if (h == 0) sm.glbase[rl] = lb;
@@ -452,7 +457,8 @@ __global__ __launch_bounds__(256) void k_build_init(const BuildArgs a) {
             rr.s = 1.0f;
             rr.hash = root_hash(a.round, r, root);
             rr.F = 1;
-            rr.pad = 0;
+            // the root's own token is also the chain's first token; no bias without a head
+            rr.htok = a.cond == DT_COND_NONE ? -1 : root;
             rows[off++] = rr;
         }
     }

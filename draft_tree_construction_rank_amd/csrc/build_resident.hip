@@ -164,11 +164,12 @@ __device__ __forceinline__ void expand_res_tile(const BuildArgs& a, int level, i
         uint64_t hh = 0;
         if (tid < nrows) {
             const RowRec* rr = level_rows(a, level) + m0 + tid + opaque_zero();
-            const uint64_t w0 = cld64(rr), w1 = cld64((const char*)rr + 8);
+            const uint64_t w0 = cld64(rr), w3 = cld64((const char*)rr + 24);
             hh = cld64((const char*)rr + 16);
             const int req = (int)(uint32_t)w0;
-            tok = (int)(uint32_t)w1;
-            tok = (uint32_t)tok < (uint32_t)a.V ? tok : 0;  // never index U out of range
+            // the head token selects the U row (-1: no bias); U is never indexed out of range
+            tok = (int)(uint32_t)(w3 >> 32);
+            tok = tok < 0 ? -1 : ((uint32_t)tok < (uint32_t)a.V ? tok : 0);
             lb = ((size_t)req * a.B + lvl) * (size_t)a.V;
         }
         sm.tok[tid] = tok;
@@ -181,9 +182,11 @@ __device__ __forceinline__ void expand_res_tile(const BuildArgs& a, int level, i
     // B operand: U[token of row p][16 s + 8 h .. + 8], s = 0..15
     u32x4_t uf[16];
     {
-        const u32x4_t* urow = (const u32x4_t*)((const uint16_t*)a.U + (size_t)sm.tok[p] * 256 + 8 * h);
+        const int tk = sm.tok[p];
+        const u32x4_t* urow = (const u32x4_t*)((const uint16_t*)a.U + (size_t)(tk >= 0 ? tk : 0) * 256 + 8 * h);
+        const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int s = 0; s < 16; ++s) uf[s] = urow[2 * s];
+        for (int s = 0; s < 16; ++s) uf[s] = tk >= 0 ? urow[2 * s] : zero;
     }
     const size_t lb = sm.lbase[p];
     const uint64_t hh = sm.hash[p];

@@ -766,6 +766,13 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
     const int base = bcast[0];
     if (fnext > 0) {
         RowRec* nrows = level_rows(a, level + 1) + base;
+        // head token of a next-level row: the node's own token (parent-conditioned), the
+        // chain token of this depth (every row of this level shares one distribution, so
+        // the rank-0 child of the first row is the greedy chain's next token), or none
+        const int chain_tok = ss.ctok[0];
+        auto htok_of = [&](int t) {
+            return a.cond == DT_COND_CHAIN ? chain_tok : (a.cond == DT_COND_NONE ? -1 : t);
+        };
         for (int i = tid; i < nkept; i += blockDim.x) {
             const uint32_t low = (uint32_t)ss.sorted[i];
             if (low_depth(low) != level) continue;
@@ -792,7 +799,7 @@ __device__ __forceinline__ void select_request(const BuildArgs& a, int level, in
             cst64(rr, (uint64_t)(uint32_t)req | ((uint64_t)(uint32_t)rank << 32));
             cst64((char*)rr + 8, (uint64_t)(uint32_t)tok | ((uint64_t)__float_as_uint(sv) << 32));
             cst64((char*)rr + 16, hh);
-            cst64((char*)rr + 24, (uint64_t)(uint32_t)fnext);
+            cst64((char*)rr + 24, (uint64_t)(uint32_t)fnext | ((uint64_t)(uint32_t)htok_of(tok) << 32));
         }
     }
     publish_wg();

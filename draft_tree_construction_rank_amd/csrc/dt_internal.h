@@ -56,7 +56,7 @@ struct alignas(16) RowRec {
     float s;        // the node's survival
     uint64_t hash;  // the node's random stream
     int32_t F;      // parent rows of this request at this level
-    int32_t pad;
+    int32_t htok;   // head token: whose U row biases the expansion (-1: no bias)
 };
 
 // Offsets (bytes) of every workspace region; sizes depend only on the parameters.
@@ -154,6 +154,7 @@ struct BuildArgs {
     uint32_t seed_lo, seed_hi, round;
     int logits_bf16;
     uint32_t spin_limit;  // iterations of a bounded wait before it gives up
+    int cond;             // DT_COND_*: head token of a row (own token, chain token, none)
     float cal[16];
 };
 

@@ -25,8 +25,9 @@ __device__ __forceinline__ int opaque_zero() {
     return z;
 }
 
-// A tile: rows < nrows take U[token_of(row)], other rows and columns >= r are zero.
-// NT threads (the workgroup size).  Ends with the caller's __syncthreads().
+// A tile: rows < nrows take U[token_of(row)] (a zero row where token_of(row) < 0), other
+// rows and columns >= r are zero.  NT threads (the workgroup size).  Ends with the
+// caller's __syncthreads().
 template <bool HEAD_BF16, int NT = 256, typename TokFn>
 __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, TokFn token_of,
                                             uint16_t* sA, float* sAf) {
@@ -41,8 +42,9 @@ __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, Tok
         for (int q = 0; q < per; ++q) {
             const int i = tid + q * NT;
             const int row = i / segs, seg = i % segs;
-            const bool ok = i < kTileRows * segs && row < nrows && seg * 8 < r;
-            const int tok = (i < kTileRows * segs && row < nrows) ? token_of(row) : 0;
+            const int t = (i < kTileRows * segs && row < nrows) ? token_of(row) : 0;
+            const bool ok = i < kTileRows * segs && row < nrows && seg * 8 < r && t >= 0;
+            const int tok = t >= 0 ? t : 0;
             const uint4 x = *(const uint4*)((const uint16_t*)U + (size_t)tok * r +
                                             (seg * 8 < r ? seg * 8 : 0));
             v[q] = ok ? x : make_uint4(0, 0, 0, 0);
@@ -56,7 +58,10 @@ __device__ __forceinline__ void load_a_tile(const void* U, int r, int nrows, Tok
         for (int i = tid; i < kTileRows * kAfStride; i += NT) {
             const int row = i / kAfStride, kk = i % kAfStride;
             float v = 0.0f;
-            if (row < nrows && kk < r) v = ((const float*)U)[(size_t)token_of(row) * r + kk];
+            if (row < nrows && kk < r) {
+                const int t = token_of(row);
+                if (t >= 0) v = ((const float*)U)[(size_t)t * r + kk];
+            }
             sAf[i] = v;
         }
     }

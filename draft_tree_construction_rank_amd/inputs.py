@@ -99,6 +99,7 @@ class Instance:
     target_peak: str  # peak law of the target's fresh draws E(v)
     strength: np.ndarray  # [R] float64 peak strength per request (boost of rank 1)
     subseed: np.ndarray  # [R] int64: per-request sub-seed used for the block logits
+    cond: int = 0  # whose head row biases an expansion: 0 parent, 1 greedy chain, 2 none
 
     @property
     def L(self) -> np.ndarray:

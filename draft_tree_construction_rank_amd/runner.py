@@ -23,7 +23,8 @@ def _torch_dtype(dtype: str):
 
 def params_for(inst, *, R: Optional[int] = None, k: Optional[int] = None,
                Ncap: Optional[int] = None, mode: Optional[str] = None,
-               temperature: Optional[float] = None, round_: Optional[int] = None) -> B.dt_params:
+               temperature: Optional[float] = None, round_: Optional[int] = None,
+               cond: Optional[int] = None) -> B.dt_params:
     m = inst.mode if mode is None else mode
     return B.make_params(R=inst.R if R is None else R, B=inst.B, k=inst.k if k is None else k,
                          V=inst.V, r=inst.r, Ncap=inst.Ncap if Ncap is None else Ncap,
@@ -31,7 +32,8 @@ def params_for(inst, *, R: Optional[int] = None, k: Optional[int] = None,
                          mode=B.DT_SAMPLE if m == "sample" else B.DT_GREEDY,
                          temperature=inst.temperature if temperature is None else temperature,
                          cal=inst.cal, seed=inst.seed,
-                         round_=inst.round if round_ is None else round_)
+                         round_=inst.round if round_ is None else round_,
+                         cond=getattr(inst, "cond", 0) if cond is None else cond)
 
 
 @dataclasses.dataclass

@@ -55,6 +55,16 @@ typedef enum {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };   /* storage dtypes */
 enum { DT_GREEDY = 0, DT_SAMPLE = 1 };
+/* Which token's Markov-head row biases a node's expansion (dt_params.cond).
+ *  DT_COND_PARENT  the node's own token: the parent-conditioned tree (PCTree summary,
+ *                  method paragraph).
+ *  DT_COND_CHAIN   the drafter's greedy chain token at the node's depth: every sibling at
+ *                  one depth reuses the chain's distribution for that depth (the
+ *                  "Shared-Markov tree" control of the PCTree summary).  Greedy mode only.
+ *  DT_COND_NONE    no bias: each depth's block row alone, the per-position marginal that
+ *                  ranks candidates without their parent (TreeSpark article, the first
+ *                  flaw of existing draft trees).  Greedy mode only. */
+enum { DT_COND_PARENT = 0, DT_COND_CHAIN = 1, DT_COND_NONE = 2 };
 
 /* Per-request status bits written to dt_tree.status. */
 enum {
@@ -83,7 +93,7 @@ typedef struct dt_params {
                              values in [0, 1] and non-decreasing */
     uint64_t seed;        /* key of the counter-based generator (sample mode) */
     uint32_t round;       /* round counter, folded into every node's random stream */
-    uint32_t reserved;    /* must be 0 */
+    uint32_t cond;        /* DT_COND_*; 0 (DT_COND_PARENT) is the parent-conditioned tree */
 } dt_params;
 
 /* Emitted trees.  Node order is canonical: depth ascending, then the path of sibling ranks
@@ -130,7 +140,8 @@ dt_status dt_build_workspace_bytes(const dt_params* p, size_t* bytes);
  *  tau          [R] float: stopping threshold; nodes with survival < tau are never kept
  *                          (tau <= 0 disables stopping)
  *  out          host struct of device pointers (dt_tree), fully overwritten
- * Expansion of node v (token t, depth d): z[c] = L[d][c] + U[t] . Wt[c]; q = softmax(z / T')
+ * Expansion of node v (token t, depth d): z[c] = L[d][c] + U[t] . Wt[c] (t replaced by the
+ * chain token of depth d, or the bias dropped, under p->cond); q = softmax(z / T')
  * with T' = 1 (greedy) or temperature (sample); the k children are the largest z (greedy;
  * ties to the lower token id) or the largest z/T + Gumbel noise (sample); a child's survival
  * is fl32(s_parent * cal[min(15, floor(16 q))]), the root's is 1; logq = log q.  The tree is

@@ -22,6 +22,7 @@ _SRC = os.path.join(_HERE, "dtree_oracle.c")
 _LIB = os.path.join(_HERE, "libdtree_oracle.so")
 
 GREEDY, SAMPLE = 0, 1
+COND_PARENT, COND_CHAIN, COND_NONE = 0, 1, 2
 STREAM_GUMBEL, STREAM_ACCEPT, STREAM_RESID = 1, 2, 3
 STATUS_BAD_ROOT, STATUS_BUDGET_CLAMPED = 1, 2
 
@@ -40,7 +41,7 @@ class Params(C.Structure):
     _fields_ = [("R", C.c_int32), ("B", C.c_int32), ("k", C.c_int32), ("V", C.c_int32),
                 ("r", C.c_int32), ("Ncap", C.c_int32), ("mode", C.c_int32),
                 ("temperature", C.c_double), ("cal", C.c_float * 16), ("seed", C.c_uint64),
-                ("round", C.c_uint32), ("req_base", C.c_int32)]
+                ("round", C.c_uint32), ("req_base", C.c_int32), ("cond", C.c_int32)]
 
 
 class _Tree(C.Structure):
@@ -103,6 +104,7 @@ def make_params(inst, *, R=None, mode=None, temperature=None, round_=None,
                 req_base=0) -> Params:
     P = Params()
     P.req_base = int(req_base)
+    P.cond = int(getattr(inst, "cond", 0))
     P.R = inst.R if R is None else R
     P.B, P.k, P.V, P.r, P.Ncap = inst.B, inst.k, inst.V, inst.r, inst.Ncap
     m = inst.mode if mode is None else mode

@@ -103,12 +103,13 @@ double or_expand(const or_params* P, const float* L_req, const float* U, const f
     const int V = P->V, r = P->r, k = P->k;
     const double T = (P->mode == OR_SAMPLE) ? P->temperature : 1.0;
     const float* Lrow = L_req + (size_t)depth * (size_t)V;
-    const float* u = U + (size_t)token * (size_t)r;
+    const float* u = token >= 0 ? U + (size_t)token * (size_t)r : NULL;
 
     for (int c = 0; c < V; ++c) {
         const float* w = Wt + (size_t)c * (size_t)r;
         double bias = 0.0;
-        for (int j = 0; j < r; ++j) bias += (double)u[j] * (double)w[j];
+        if (u)
+            for (int j = 0; j < r; ++j) bias += (double)u[j] * (double)w[j];
         double z = (double)Lrow[c] + bias;
         y[c] = z / T;
     }
@@ -158,6 +159,8 @@ typedef struct {
 typedef struct {
     node_t* v;
     int n, cap;
+    int use_head;      /* 0: a node's own token is its head token */
+    int32_t head[33];  /* else: head token of every node at depth d (-1: no bias) */
 } store_t;
 
 static int store_add(store_t* st, node_t nd)
@@ -244,7 +247,8 @@ static void expand_in_store(const or_params* P, const float* L_req, const float*
     int32_t ctok[8];
     double cy[8], lse;
     node_t par = st->v[idx];
-    double gap = or_expand(P, L_req, U, Wt, par.depth, par.token, par.hash, ybuf, &lse, ctok, cy);
+    const int32_t head = st->use_head ? st->head[par.depth] : par.token;
+    double gap = or_expand(P, L_req, U, Wt, par.depth, head, par.hash, ybuf, &lse, ctok, cy);
     if (mg) upd_min(&mg->key_gap, gap);
     int first = -1;
     for (int j = 0; j < k; ++j) {
@@ -395,6 +399,32 @@ static int build_levelsync(const or_params* P, const float* L_req, const float* 
     return nsel;
 }
 
+/* Head tokens of the Shared-Markov control (PCTree summary, mechanism paragraph): first walk
+ * the drafter's greedy chain -- c_0 = the root, c_{d+1} = the argmax (ties: lower id) of the
+ * head-biased row L[d] + U[c_d] . W -- then every node at depth d is expanded with the chain's
+ * distribution of that depth, i.e. with head token c_d.  Without a head, every node's
+ * head is -1. */
+static void head_tokens(const or_params* P, const float* L_req, const float* U, const float* Wt,
+                        int32_t root, double* ybuf, store_t* st)
+{
+    st->use_head = P->cond != OR_COND_PARENT;
+    if (P->cond == OR_COND_NONE) {
+        for (int d = 0; d <= P->B; ++d) st->head[d] = -1;
+        return;
+    }
+    if (P->cond != OR_COND_CHAIN) return;
+    or_params Q = *P;
+    Q.k = 1;
+    Q.mode = OR_GREEDY;
+    st->head[0] = root;
+    for (int d = 0; d + 1 < P->B; ++d) {
+        int32_t t;
+        double y, lse;
+        or_expand(&Q, L_req, U, Wt, d, st->head[d], 0, ybuf, &lse, &t, &y);
+        st->head[d + 1] = t;
+    }
+}
+
 int or_build(const or_params* P, const float* L, const float* U, const float* Wt,
              const int32_t* root_token, const int32_t* n_budget, const float* tau,
              int32_t method, or_tree* out, or_margin* margins)
@@ -426,6 +456,7 @@ int or_build(const or_params* P, const float* L, const float* U, const float* Wt
             root.logq = 0.0f;
             root.hash = or_root_hash(P->round, P->req_base + req, root_token[req]);
             store_add(&st, root);
+            head_tokens(P, L_req, U, Wt, root_token[req], ybuf, &st);
             if (method == 0)
                 nsel = build_heap(P, L_req, U, Wt, &st, nb, tau[req], sel, ybuf, mg, &nexp);
             else

@@ -31,6 +31,10 @@ extern "C" {
 enum { OR_GREEDY = 0, OR_SAMPLE = 1 };
 enum { OR_STREAM_GUMBEL = 1, OR_STREAM_ACCEPT = 2, OR_STREAM_RESID = 3 };
 enum { OR_STATUS_BAD_ROOT = 1, OR_STATUS_BUDGET_CLAMPED = 2 };
+/* Which token's head row biases a node's expansion: its own (parent-conditioned tree), the
+ * greedy chain's token at its depth (Shared-Markov control), or none (per-position
+ * marginals).  The last two are greedy-mode variants. */
+enum { OR_COND_PARENT = 0, OR_COND_CHAIN = 1, OR_COND_NONE = 2 };
 
 typedef struct {
     int32_t R, B, k, V, r, Ncap;
@@ -41,6 +45,7 @@ typedef struct {
     uint32_t round;
     int32_t req_base;     /* request id of row 0 of every [R] array: request i's random
                              streams are keyed by req_base + i */
+    int32_t cond;         /* OR_COND_* */
 } or_params;
 
 /* Emitted trees, canonical (depth, path-lex) order; caller-owned host arrays. */
@@ -81,7 +86,8 @@ uint64_t or_child_hash(uint64_t parent_hash, int32_t token);
 double or_uniform(uint64_t seed, uint64_t hash, uint32_t stream, uint32_t index);
 
 /* One expansion.  Writes z[V] (float64), lse, and the k ranked children (token, y value).
- * Returns the smallest adjacent gap among the top-(k+1) ranking keys. */
+ * `token` selects the head row U[token]; token < 0 means no bias.  Returns the smallest
+ * adjacent gap among the top-(k+1) ranking keys. */
 double or_expand(const or_params* P, const float* L_req, const float* U, const float* Wt,
                  int32_t depth, int32_t token, uint64_t hash, double* z, double* lse,
                  int32_t* child_tok, double* child_y);

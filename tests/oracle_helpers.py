@@ -23,10 +23,21 @@ def small_instance(seed: int, *, V=24, r=4, B=3, k=2, Ncap=6, mode="greedy", tem
 
 
 def node_dist(inst, req, depth, token, T):
-    """float64 tempered logits y of a node's children distribution (numpy, independent)."""
-    z = inst.L[req, depth].astype(np.float64) + \
-        inst.Wt.astype(np.float64) @ inst.U[token].astype(np.float64)
+    """float64 tempered logits y of a node's children distribution (numpy, independent);
+    token None means no head bias."""
+    z = inst.L[req, depth].astype(np.float64)
+    if token is not None:
+        z = z + inst.Wt.astype(np.float64) @ inst.U[token].astype(np.float64)
     return z / T
+
+
+def chain_tokens(inst, req):
+    """The drafter's greedy chain under the head: c_0 = root, c_{d+1} = argmax of
+    L[d] + U[c_d] . W (ties: lower id, which numpy's argmax gives)."""
+    c = [int(inst.root_token[req])]
+    for d in range(inst.B - 1):
+        c.append(int(np.argmax(node_dist(inst, req, d, c[d], 1.0))))
+    return c
 
 
 def ranked_children(inst, req, depth, token, h, mode, T):
@@ -45,12 +56,18 @@ def cal_bin(q):
     return min(15, int(np.floor(16.0 * q)))
 
 
-def brute_force(inst, req, N, tau, mode="greedy", T=1.0, round_=0):
+def brute_force(inst, req, N, tau, mode="greedy", T=1.0, round_=0, cond="parent"):
     """Enumerate the whole k-ary candidate tree to depth B; keep s >= tau; sort by
     (s desc, depth asc, rank path asc); keep the first N.  Returns the kept nodes in
-    canonical (depth, rank path) order as dicts."""
+    canonical (depth, rank path) order as dicts.  cond: whose head row biases a node at
+    depth d -- "parent" its own token, "chain" the greedy chain's token c_d, "none" no bias."""
     Teff = T if mode == "sample" else 1.0
     root = int(inst.root_token[req])
+    chain = chain_tokens(inst, req) if cond == "chain" else None
+
+    def head(depth, token):
+        return token if cond == "parent" else (chain[depth] if cond == "chain" else None)
+
     h0 = oracle.mix64(oracle.mix64((round_ << 32) | req) ^ root)
     allnodes = []
     frontier = [dict(token=root, depth=0, s=np.float32(1.0), ranks=(), toks=(), h=h0)]
@@ -59,7 +76,8 @@ def brute_force(inst, req, N, tau, mode="greedy", T=1.0, round_=0):
         for nd in frontier:
             if nd["depth"] >= inst.B:
                 continue
-            for j, (c, lq) in enumerate(ranked_children(inst, req, nd["depth"], nd["token"],
+            for j, (c, lq) in enumerate(ranked_children(inst, req, nd["depth"],
+                                                        head(nd["depth"], nd["token"]),
                                                         nd["h"], mode, Teff)):
                 a = inst.cal[cal_bin(np.exp(lq))]
                 ch = dict(token=c, depth=nd["depth"] + 1, s=np.float32(nd["s"] * a),

@@ -230,6 +230,11 @@ def _full_cases():
     for T in (0.6, 1.0, 1.5):
         c["sample|T=%g|strong=0" % T] = dict(name="sample", temperature=T)
     c["sample|T=1|strong=1"] = dict(name="sample", strong=True, temperature=1.0)
+    # head variants (Shared-Markov chain head, no head), strong head so that they matter
+    for cond in (1, 2):
+        c["b16|strong=1|cond=%d" % cond] = dict(name="b16", strong=True, cond=cond)
+        c["batched|tau=0.05|strong=1|cond=%d" % cond] = dict(name="batched", strong=True,
+                                                             tau=0.05, cond=cond)
     return c
 
 

@@ -160,6 +160,31 @@ def test_batched_strong_head(rt, tau):
     _check_expansions(inst, got, list(range(inst.R)) if tau > 0 else list(range(8)))
 
 
+# ------------------------------------------------------------------ head variants ----------
+@pytest.mark.parametrize("key", ["b16|strong=1|cond=1", "b16|strong=1|cond=2",
+                                 "batched|tau=0.05|strong=1|cond=1",
+                                 "batched|tau=0.05|strong=1|cond=2"])
+def test_head_variants_full_vocab(rt, key):
+    """Shared-Markov (chain head) and marginal (no head) trees at V = 151936, through the
+    W-resident kernel (one request) and the streaming kernel (64 requests)."""
+    _greedy_case(rt, None, key=key)
+
+
+VARIANT_SMALL = [
+    dict(seed=1, V=1000, r=8, B=4, k=2, Ncap=8, R=3, dtype="f32"),
+    dict(seed=7, V=2048, r=256, B=3, k=4, Ncap=64, R=2, dtype="bf16"),
+    dict(seed=10, V=2048, r=32, B=3, k=4, Ncap=32, R=200, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("cond", [1, 2])
+@pytest.mark.parametrize("cfg", VARIANT_SMALL, ids=lambda c: "seed%d" % c["seed"])
+def test_head_variants_small(rt, cfg, cond):
+    """Tile mode (float32 and bf16 heads) and group mode (levels of more than 64 rows)."""
+    inst = instance("tiny", strong=True, cal="monotone", rho=0.5, cond=cond, **cfg)
+    _greedy_case(rt, inst, margin=STRESS_MARGIN)
+
+
 # ------------------------------------------------------------------ exact ties -------------
 TIES = [
     # tile mode, full vocabulary, one request

@@ -47,7 +47,8 @@ Layout make_layout(const dt_params* p, bool allow_resident) {
     L.partials = take(cap_rows * rec_floats(L.KT) * sizeof(float));
     L.build_total = off;  // everything below is used by the verifiers only
     L.vsplits = 0;
-    L.vrow = L.vprow = L.vstate = L.vpart = 0;
+    L.vrow = L.vstate = L.vpart = L.vcnt = L.vred = 0;
+    L.vcsplits = 0;
     if (p->mode == DT_SAMPLE) {
         // sample verify: ceil(R/64) request tiles x vsplits vocabulary splits, grid <= 1024
         const int tiles = (int)((R + kTileRows - 1) / kTileRows);
@@ -56,10 +57,16 @@ Layout make_layout(const dt_params* p, bool allow_resident) {
         if (s > L.NC) s = L.NC;
         if (s < 1) s = 1;
         L.vsplits = s;
+        // rejection chain: about 512 workgroups over all requests, at most kVsMaxSplits each
+        int c = (int)(512 / R);
+        c = c < 1 ? 1 : (c > kVsMaxSplits ? kVsMaxSplits : c);
+        if ((size_t)c > V) c = (int)V;
+        L.vcsplits = c;
         L.vrow = take(R * V * sizeof(float));
-        L.vprow = take(R * V * sizeof(float));
-        L.vstate = take(R * sizeof(VState));
+        L.vstate = take(2 * R * sizeof(VState));
         L.vpart = take(R * (size_t)L.vsplits * 4 * sizeof(float));
+        L.vcnt = take(R * sizeof(unsigned));
+        L.vred = take(R * (size_t)kVsPhases * kVsMaxSplits * sizeof(uint64_t));
     }
     {
         // greedy verify: the root rows are split over about 1024 workgroups, each of at least

@@ -73,10 +73,12 @@ struct Layout {
     size_t nbeff;     // int [R]: budget after clamping
     size_t rstat;     // int [R]: per-request status bits
     size_t partials;  // float [64*max(G, tiles)][2+3*KT]: per (row, vocabulary split) partials
-    size_t vrow;      // float [R][V]: sample verify, draft row (log2 units, then q) of the node
-    size_t vprow;     // float [R][V]: sample verify, target probabilities p of the node
+    size_t vrow;      // float [R][V]: sample verify, draft row of the node (log2 units)
     size_t vstate;    // VState [R]
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
+    size_t vcnt;      // unsigned [R]: sample verify, per-request barrier counters
+    size_t vred;      // u64 [R][kVsPhases][kVsMaxSplits]: per-slice partials of a step's
+                      // reductions (residual masses, draws)
     size_t gpart;     // (float, int) [R][gsplits]: greedy verify, split argmax of the root rows
     size_t trace;     // u64 [kMaxGrid][kTraceLevels][16]: phase timestamps (DT_TRACE builds only)
     size_t build_total;  // extent of the regions tree_build uses (a prefix of the layout)
@@ -84,7 +86,8 @@ struct Layout {
     int G;            // largest grid of the construction kernel (sizes the partial records)
     int NC;           // vocabulary chunks of 128 columns
     int KT;           // top-k list length used by the kernels (1, 2, 4 or 8)
-    int vsplits;      // vocabulary splits per request in sample verify
+    int vsplits;      // vocabulary splits per request in sample verify (draft rows)
+    int vcsplits;     // workgroups per request of the rejection chain
     int gsplits;      // vocabulary splits per request of the root-row argmax in greedy verify
     bool resident;    // partials sized for the W-resident kernel
 };
@@ -99,11 +102,14 @@ inline int kt_for(int k) { return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8; }
 // a multiple of 4 for 16-byte accesses.
 __host__ __device__ constexpr int rec_floats(int KT) { return ((2 + 3 * KT) + 3) & ~3; }
 
-// Walk state of one request in sample verify.
+// Walk state of one request in sample verify.  nbar: per-request barriers passed so far in
+// the round (the chain's workgroups of a request count the same barriers).
 struct alignas(8) VState {
-    int active, v, row, depth, token, nacc, nemit, pad;
+    int active, v, row, depth, token, nacc, nemit, nbar;
     uint64_t hash;
 };
+constexpr int kVsMaxSplits = 16;     // chain workgroups per request at most
+constexpr int kVsPhases = kMaxK + 1;  // reductions of one step: k residual masses, one draw
 
 // Control words at the start of the workspace.  Per-level words are indexed by the level
 // (1..B+1) so that a late workgroup never reads the next level's value.

@@ -225,8 +225,12 @@ hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
 //   k_vs_rows  - for every request still walking at a node of depth < B: the node's draft
 //                row y_q = (L[d] + U[t] . Wt) * log2(e)/T on MFMA (same tile as expansion),
 //                stored to vrow, plus per-split (max, sum) of y_q and of the target row;
-//   k_vs_chain - one workgroup per request: the normalisers, then recursive rejection over
-//                the k drawn siblings in draw order, then the final draw and the move.
+//   k_vs_split - the rejection chain, each request on S workgroups that split the
+//                vocabulary: every workgroup of a request takes the same decisions (they
+//                depend only on values every workgroup computes identically), and each
+//                vocabulary-wide reduction (a residual mass, a draw) is one partial per
+//                slice, published and summed in slice order after a per-request barrier.
+//                p and q are evaluated where they are needed, never stored.
 // Residuals in closed form: after j rejections the target law is max(p - a_j q, 0) / S_j
 // with a_0 = 0, S_0 = 1, a_{j+1} = a_j + S_j / c_j, c_j = 1 - (q mass of the rejected
 // siblings), S_{j+1} = sum max(p - a_{j+1} q, 0), and the draft law is q / c_j on the
@@ -237,10 +241,11 @@ hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
 // =======================================================================================
 __global__ __launch_bounds__(256) void k_vs_init(int R, int B, uint32_t round,
                                                  const int32_t* root_token, dt_tree tree,
-                                                 VState* state, dt_verify_out out) {
+                                                 VState* state, unsigned* vcnt, dt_verify_out out) {
     const int req = blockIdx.x * blockDim.x + threadIdx.x;
     if (req >= R) return;
     VState s;
+    // a bad root or a build whose internal wait gave up: nothing is emitted
     s.active = (tree.status[req] & (DT_REQ_BAD_ROOT | DT_REQ_SYNC_TIMEOUT)) ? 0 : 1;
     s.v = -1;
     s.row = 0;
@@ -248,9 +253,10 @@ __global__ __launch_bounds__(256) void k_vs_init(int R, int B, uint32_t round,
     s.token = root_token[req];
     s.nacc = 0;
     s.nemit = 0;
-    s.pad = 0;
+    s.nbar = 0;
     s.hash = root_hash(round, req, s.token);
     state[req] = s;
+    vcnt[req] = 0u;
     for (int i = 0; i < B; ++i) out.path[(size_t)req * B + i] = -1;
     for (int i = 0; i <= B; ++i) out.out_tokens[(size_t)req * (B + 1) + i] = -1;
     out.accept_len[req] = 0;
@@ -376,64 +382,119 @@ __device__ float block_sum_f(float v, float* sh) {
     __syncthreads();
     float t = 0.0f;
     for (int i = 0; i < nw; ++i) t += sh[i];
+    __syncthreads();
     return t;
 }
 
 struct ChainArgs {
     const void* target;
-    VState* state;
-    float* vrow;
-    float* vprow;
+    const VState* state;  // this step's walk states
+    VState* next;         // next step's walk states
+    const float* vrow;
     const float* vpart;
+    unsigned* vcnt;
+    uint64_t* vred;
     dt_tree tree;
     dt_verify_out out;
-    int R, B, V, k, Ncap, S;
+    int R, B, V, k, Ncap, S, SC;
     float y2scale, invT;
-    uint32_t seed_lo, seed_hi;
+    uint32_t seed_lo, seed_hi, spin_limit;
     int bf16;
 };
 
-__global__ __launch_bounds__(1024) void k_vs_chain(const ChainArgs a) {
-    __shared__ float shf[16];
-    __shared__ ArgMax sha[16];
-    __shared__ Lse2 shl[2][16];
+// Per-request exchange of one partial per slice: publishes this workgroup's value in the
+// phase's slot, counts the barrier and waits (bounded) until every workgroup of the
+// request has; then every thread reads the SC partials.  nbar: barriers of the request
+// passed before this one.
+__device__ __forceinline__ bool vs_exchange(const ChainArgs& a, int req, int sp, int phase,
+                                            uint64_t val, int nbar, uint64_t* parts, int* bc) {
+    uint64_t* red = a.vred + ((size_t)req * kVsPhases + phase) * kVsMaxSplits;
+    const int tid = threadIdx.x;
+    if (tid == 0) cst64(red + sp, val);
+    publish();
+    __syncthreads();
+    if (tid == 0) {
+        int ok = 1;
+        const unsigned target = (unsigned)(a.SC * (nbar + 1));
+        cadd32(a.vcnt + req, 1u);
+        uint32_t it = 0;
+        while ((int)(cld32(a.vcnt + req) - target) < 0) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it > a.spin_limit) {
+                ok = 0;
+                break;
+            }
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        bc[0] = ok;
+    }
+    __syncthreads();
+    const bool ok = bc[0] != 0;
+    if (ok)
+        for (int i = 0; i < a.SC; ++i) parts[i] = cld64(red + i);
+    __syncthreads();
+    return ok;
+}
+
+__global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
+    __shared__ float shf[8];
+    __shared__ ArgMax sha[8];
+    __shared__ Lse2 shl[2][8];
     __shared__ int s_tok[kMaxNcap], s_par[kMaxNcap];
-    const int req = blockIdx.x, tid = threadIdx.x;
+    __shared__ int bc[2];
+    const int req = blockIdx.x / a.SC, sp = blockIdx.x % a.SC, tid = threadIdx.x;
     VState st = a.state[req];
-    if (!st.active) return;
+    if (!st.active) {
+        if (sp == 0 && tid == 0) a.next[req] = st;
+        return;
+    }
     const int n = a.tree.n_nodes[req];
     if (tid < a.Ncap) {
         s_tok[tid] = a.tree.token[(size_t)req * a.Ncap + tid];
         s_par[tid] = a.tree.parent[(size_t)req * a.Ncap + tid];
     }
+    const int lo = (int)((long long)sp * a.V / a.SC), hi = (int)((long long)(sp + 1) * a.V / a.SC);
     const size_t tbase = ((size_t)req * (a.Ncap + 1) + st.row) * (size_t)a.V;
-    float* q = a.vrow + (size_t)req * a.V;
-    float* p = a.vprow + (size_t)req * a.V;
+    const float* yq = a.vrow + (size_t)req * a.V;
+    int nbar = st.nbar;
     int emitted = -1;
-    bool descend = false;
-
-    if (st.depth == a.B) {
-        // a draw from p: Gumbel-max over target / T
+    bool descend = false, failed = false;
+    uint64_t parts[kVsMaxSplits];
+    // draw of this slice as a ranked entry (key desc, then lower index); 0 = no candidate
+    auto slice_draw = [&](bool residual, float lse_q, float lse_p, float alpha) -> uint64_t {
         ArgMax best{-INFINITY, 0x7fffffff};
-        for (int g = tid; 4 * g < a.V; g += blockDim.x) {
+        for (int g = (lo >> 2) + tid; 4 * g < hi; g += blockDim.x) {
             const uint4 w = rand4((uint32_t)g, STREAM_RESID, st.hash, a.seed_lo, a.seed_hi);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int x = 4 * g + e;
-                if (x < a.V)
-                    best = amax(best, ArgMax{load_logit(a.target, tbase + x, a.bf16) * a.invT +
-                                             gumbel(ws[e]), x});
+                if (x < lo || x >= hi) continue;
+                const float t = load_logit(a.target, tbase + x, a.bf16);
+                if (!residual) {
+                    best = amax(best, ArgMax{t * a.invT + gumbel(ws[e]), x});
+                } else {
+                    const float d = exp2f(t * a.y2scale - lse_p) - alpha * exp2f(yq[x] - lse_q);
+                    if (d > 0.0f) best = amax(best, ArgMax{logf(d) + gumbel(ws[e]), x});
+                }
             }
         }
-        best = wave_amax(best);
-        __syncthreads();
-        if ((tid & 63) == 0) sha[tid >> 6] = best;
-        __syncthreads();
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) best = amax(best, sha[i]);
-        emitted = best.i;
+        best = block_amax(best, sha);
+        return best.v == -INFINITY ? 0ull : pack_entry(best.v, best.i);
+    };
+    auto pick = [&](const uint64_t* ps) -> int {
+        uint64_t b = 0;
+        for (int i = 0; i < a.SC; ++i) b = ps[i] > b ? ps[i] : b;
+        return b ? entry_tok(b) : -1;
+    };
+    if (st.depth == a.B) {
+        // a draw from p: Gumbel-max over target / T
+        const uint64_t mine = slice_draw(false, 0.0f, 0.0f, 0.0f);
+        if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc)) emitted = pick(parts);
+        else failed = true;
+        ++nbar;
     } else {
-        // normalisers of q and p (log2 units)
+        // normalisers of q and p (log2 units), from the draft-row partials
         Lse2 lq, lp;
         lq.init();
         lp.init();
@@ -459,11 +520,6 @@ __global__ __launch_bounds__(1024) void k_vs_chain(const ChainArgs a) {
             lp.merge(shl[1][i].m, shl[1][i].s);
         }
         const float lse_q = lq.m + log2f(lq.s), lse_p = lp.m + log2f(lp.s);
-        for (int x = tid; x < a.V; x += blockDim.x) {
-            q[x] = exp2f(q[x] - lse_q);
-            p[x] = exp2f(load_logit(a.target, tbase + x, a.bf16) * a.y2scale - lse_p);
-        }
-        __syncthreads();
         const int32_t* cand = a.tree.cand + ((size_t)req * (a.Ncap + 1) + st.row) * a.k;
         float alpha = 0.0f, S = 1.0f, c = 1.0f;
         for (int j = 0; j < a.k; ++j) {
@@ -471,7 +527,8 @@ __global__ __launch_bounds__(1024) void k_vs_chain(const ChainArgs a) {
             // an empty slot (a ranked list shorter than k, only possible with non-finite
             // draft logits) is no drawn sibling
             if (x < 0 || x >= a.V) continue;
-            const float qx = q[x], px = p[x];
+            const float qx = exp2f(yq[x] - lse_q);
+            const float px = exp2f(load_logit(a.target, tbase + x, a.bf16) * a.y2scale - lse_p);
             const uint4 w = rand4((uint32_t)(j >> 2), STREAM_ACCEPT, st.hash, a.seed_lo, a.seed_hi);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
             const float u = u01(ws[j & 3]);
@@ -483,76 +540,79 @@ __global__ __launch_bounds__(1024) void k_vs_chain(const ChainArgs a) {
             alpha += S / c;
             c -= qx;
             float part = 0.0f;
-            for (int y = tid; y < a.V; y += blockDim.x) part += fmaxf(p[y] - alpha * q[y], 0.0f);
-            S = block_sum_f(part, shf);
+            for (int y = lo + tid; y < hi; y += blockDim.x)
+                part += fmaxf(exp2f(load_logit(a.target, tbase + y, a.bf16) * a.y2scale - lse_p) -
+                                  alpha * exp2f(yq[y] - lse_q),
+                              0.0f);
+            part = block_sum_f(part, shf);
+            if (!vs_exchange(a, req, sp, j, (uint64_t)__float_as_uint(part), nbar, parts, bc)) {
+                failed = true;
+                break;
+            }
+            ++nbar;
+            S = 0.0f;
+            for (int i = 0; i < a.SC; ++i) S += __uint_as_float((uint32_t)parts[i]);
             if (!(S > 0.0f)) {
                 emitted = x;
                 descend = true;
                 break;
             }
         }
-        if (emitted < 0) {
+        if (emitted < 0 && !failed) {
             // every sibling rejected: a draw from the residual max(p - alpha q, 0)
-            ArgMax best{-INFINITY, 0x7fffffff};
-            for (int g = tid; 4 * g < a.V; g += blockDim.x) {
-                const uint4 w = rand4((uint32_t)g, STREAM_RESID, st.hash, a.seed_lo, a.seed_hi);
-                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int x = 4 * g + e;
-                    if (x < a.V) {
-                        const float d = p[x] - alpha * q[x];
-                        if (d > 0.0f) best = amax(best, ArgMax{logf(d) + gumbel(ws[e]), x});
-                    }
-                }
-            }
-            best = wave_amax(best);
-            __syncthreads();
-            if ((tid & 63) == 0) sha[tid >> 6] = best;
-            __syncthreads();
-            for (int i = 0; i < (int)(blockDim.x >> 6); ++i) best = amax(best, sha[i]);
-            emitted = best.i;
+            const uint64_t mine = slice_draw(true, lse_q, lse_p, alpha);
+            if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc)) emitted = pick(parts);
+            else failed = true;
+            ++nbar;
         }
     }
     __syncthreads();
+    if (sp != 0 || tid != 0) return;
+    if (failed) {
+        // an internal wait gave up: the walk ends, n_out = -1 reports it
+        st.active = 0;
+        a.out.accept_len[req] = st.nacc;
+        a.out.n_out[req] = -1;
+        a.next[req] = st;
+        return;
+    }
     int w = -1;
     if (descend) {
         for (int i = 0; i < n; ++i)
             if (s_par[i] == st.v && s_tok[i] == emitted) w = i;
     }
-    if (tid == 0) {
-        a.out.out_tokens[(size_t)req * (a.B + 1) + st.nemit] = emitted;
-        st.nemit += 1;
-        if (w >= 0) {
-            a.out.path[(size_t)req * a.B + st.nacc] = w;
-            st.nacc += 1;
-            st.v = w;
-            st.row = w + 1;
-            st.depth += 1;
-            st.token = emitted;
-            st.hash = child_hash(st.hash, emitted);
-        } else {
-            st.active = 0;
-            a.out.accept_len[req] = st.nacc;
-            a.out.n_out[req] = st.nemit;
-        }
-        a.state[req] = st;
+    a.out.out_tokens[(size_t)req * (a.B + 1) + st.nemit] = emitted;
+    st.nemit += 1;
+    st.nbar = nbar;
+    if (w >= 0) {
+        a.out.path[(size_t)req * a.B + st.nacc] = w;
+        st.nacc += 1;
+        st.v = w;
+        st.row = w + 1;
+        st.depth += 1;
+        st.token = emitted;
+        st.hash = child_hash(st.hash, emitted);
+    } else {
+        st.active = 0;
+        a.out.accept_len[req] = st.nacc;
+        a.out.n_out[req] = st.nemit;
     }
+    a.next[req] = st;
 }
 
 hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
                                 const dt_tree* tree, const void* L, const void* U,
                                 const void* Wt, const int32_t* root_token, const void* target,
                                 const dt_verify_out* out, hipStream_t st) {
-    VState* state = (VState*)(ws + lay.vstate);
+    VState* state = (VState*)(ws + lay.vstate);  // two buffers of R: this step's, the next's
+    unsigned* vcnt = (unsigned*)(ws + lay.vcnt);
     hipLaunchKernelGGL(k_vs_init, dim3((p->R + 255) / 256), dim3(256), 0, st, p->R, p->B,
-                       p->round, root_token, *tree, state, *out);
+                       p->round, root_token, *tree, state, vcnt, *out);
     VsArgs va{};
     va.L = L;
     va.U = U;
     va.Wt = Wt;
     va.target = target;
-    va.state = state;
     va.vrow = (float*)(ws + lay.vrow);
     va.vpart = (float*)(ws + lay.vpart);
     va.R = p->R;
@@ -566,10 +626,10 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
     va.bf16 = p->logits_dtype == DT_BF16;
     ChainArgs ca{};
     ca.target = target;
-    ca.state = state;
     ca.vrow = va.vrow;
-    ca.vprow = (float*)(ws + lay.vprow);
     ca.vpart = va.vpart;
+    ca.vcnt = vcnt;
+    ca.vred = (uint64_t*)(ws + lay.vred);
     ca.tree = *tree;
     ca.out = *out;
     ca.R = p->R;
@@ -578,19 +638,24 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
     ca.k = p->k;
     ca.Ncap = p->Ncap;
     ca.S = lay.vsplits;
+    ca.SC = lay.vcsplits;
     ca.y2scale = va.y2scale;
     ca.invT = (float)(1.0 / (double)p->temperature);
     ca.seed_lo = (uint32_t)p->seed;
     ca.seed_hi = (uint32_t)(p->seed >> 32);
+    ca.spin_limit = kSpinLimit;
     ca.bf16 = va.bf16;
     const int tiles = (p->R + kTileRows - 1) / kTileRows;
     const dim3 grid(tiles * lay.vsplits);
     for (int step = 0; step <= p->B; ++step) {
+        va.state = state + (size_t)(step & 1) * p->R;
+        ca.state = va.state;
+        ca.next = state + (size_t)((step + 1) & 1) * p->R;
         if (p->head_dtype == DT_BF16)
             hipLaunchKernelGGL(k_vs_rows<true>, grid, dim3(256), 0, st, va);
         else
             hipLaunchKernelGGL(k_vs_rows<false>, grid, dim3(256), 0, st, va);
-        hipLaunchKernelGGL(k_vs_chain, dim3(p->R), dim3(1024), 0, st, ca);
+        hipLaunchKernelGGL(k_vs_split, dim3(p->R * lay.vcsplits), dim3(256), 0, st, ca);
     }
     return hipGetLastError();
 }

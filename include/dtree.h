@@ -188,7 +188,9 @@ dt_status tree_verify_greedy(const dt_params* p, const dt_tree* tree, const void
  * p_{j+1} = max(p_j - q_j, 0) / Z and q_{j+1} = q_j without x_j, renormalised.  An accepted
  * sibling that is a tree node is descended into; one that is not ends the round; if all are
  * rejected the round ends with a draw from the final residual; at depth B it ends with a
- * draw from p. */
+ * draw from p.  Each request's vocabulary-wide reductions are split over several
+ * workgroups that wait for each other (bounded, about two seconds); a request whose wait
+ * gave up reports n_out = -1. */
 dt_status tree_verify_sample(const dt_params* p, const dt_tree* tree, const void* block_logits,
                              const void* U, const void* Wt, const int32_t* root_token,
                              const void* target_logits, const dt_verify_out* out,

@@ -308,6 +308,51 @@ def mechanism_isolation(torch, rt, inputs, rho=0.8):
     return out
 
 
+def load_sweep(torch, rt, inputs, loads=(0.0, 0.5, 0.8, 0.95), length=64):
+    """Multi-round decoding of the batched workload's shape (R = 64, B = 16, k = 4, N = 64,
+    V = 151936, strong head) on the synthetic Markov world.  The calibration table is first
+    fitted to the world (acceptance rate of drafted edges per q bin, from rounds at no
+    load); then per load level the policy's threshold and budget, rounds per sample (rounds
+    to emit `length` tokens), accepted tokens per round, nodes per tree and the build +
+    verify time per round; a chain (k = 1) at no load for reference."""
+    from draft_tree_construction_rank_amd import driver, synth
+    inst = inputs.make_instance("batched", strong_head=True, tau=0.0)
+    U = torch.from_numpy(inst.U).cuda().to(torch.bfloat16)
+    Wt = torch.from_numpy(inst.Wt).cuda().to(torch.bfloat16)
+    world = synth.TorchMarkovWorld(torch, seed=7, R=inst.R, B=inst.B, V=inst.V, U=U, Wt=Wt,
+                                   rho=0.8)
+
+    def bl(pos0):
+        return world.block_logits(torch.from_numpy(pos0).cuda())
+
+    def tr(roots, pos0, tree):
+        return world.target_rows(torch.from_numpy(roots).cuda(), torch.from_numpy(pos0).cuda(), tree)
+
+    out = {}
+    # calibration: edges drafted at visited nodes in rounds at no load, binned by q
+    p0 = rt.params_for(inst)
+    cal_run = driver.run(p0, U=U, Wt=Wt, roots=inst.root_token, length=24,
+                         load_of_round=lambda t: 0.0, tau_max=0.5, capacity=inst.R * p0.Ncap,
+                         block_logits=bl, target_rows=tr, collect_edges=True)
+    cal = driver.fit_calibration(cal_run.edge_q, cal_run.edge_acc, prior=inst.cal)
+    out["calibration"] = {"edges": int(cal_run.edge_q.size),
+                          "table": [round(float(x), 4) for x in cal]}
+    runs = [("load%g" % ld, ld, {}) for ld in loads] + [("chain_k1_load0", 0.0, dict(k=1, Ncap=inst.B))]
+    for name, ld, kw in runs:
+        p = rt.params_for(inst, **kw)
+        for i in range(16):
+            p.cal[i] = float(cal[i])
+        res = driver.run(p, U=U, Wt=Wt, roots=inst.root_token, length=length,
+                         load_of_round=lambda t, ld=ld: ld, tau_max=0.5,
+                         capacity=inst.R * p.Ncap, block_logits=bl, target_rows=tr)
+        sm = res.summary()
+        sm.update({"tau": float(res.tau[0]), "n_budget": int(res.n_budget[0]),
+                   "tokens_per_s_build_verify": round(
+                       float(res.n_out.sum()) / ((res.build_us.sum() + res.verify_us.sum()) * 1e-6), 1)})
+        out[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in sm.items()}
+    return out
+
+
 def kbuild_fractions(inst, res, B):
     """HBM and MFMA fractions of k_build for a measured workload (alg bytes and flops per
     launch over the event-timed average launch)."""
@@ -492,6 +537,7 @@ def main():
         extras["sample"] = {"T%g" % T: sample_round_us(torch, rt, inputs, T, flusher)
                             for T in (0.6, 1.0, 1.5)}
         extras["mechanism_isolation_markov_target"] = mechanism_isolation(torch, rt, inputs)
+        extras["multi_round_load_sweep"] = load_sweep(torch, rt, inputs)
         extras["targets"] = {
             "tree_build_us_R1_B16_k4_N64": {"measured_median": extras["tree_build_us_R1_B16_k4_N64"],
                                             "target": 100.0,

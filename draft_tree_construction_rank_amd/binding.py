@@ -22,7 +22,8 @@ DT_COND_PARENT, DT_COND_CHAIN, DT_COND_NONE = 0, 1, 2
 DT_REQ_BAD_ROOT, DT_REQ_BUDGET_CLAMPED = 1, 2
 
 EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_build_noalloc", "tree_verify_greedy",
-            "tree_verify_sample", "dt_status_string", "dt_timing_enable", "dt_timing_read")
+            "tree_verify_sample", "dt_load_policy", "dt_status_string", "dt_timing_enable",
+            "dt_timing_read")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # DT_NOALLOC_SCRATCH_BYTES of include/dtree.h
 
 
@@ -45,6 +46,10 @@ class dt_tree(C.Structure):
                 ("anc_mask", C.c_void_p), ("surv", C.c_void_p), ("logq", C.c_void_p),
                 ("n_nodes", C.c_void_p), ("cand", C.c_void_p), ("status", C.c_void_p),
                 ("n_expand", C.c_void_p), ("level_rows", C.c_void_p)]
+
+
+class dt_policy(C.Structure):
+    _fields_ = [("tau_max", C.c_float), ("capacity", C.c_int32), ("Ncap", C.c_int32)]
 
 
 class dt_verify_out(C.Structure):
@@ -77,6 +82,8 @@ def lib() -> C.CDLL:
         L.tree_verify_sample.argtypes = [P, C.POINTER(dt_tree), vp, vp, vp, vp, vp,
                                          C.POINTER(dt_verify_out), vp, C.c_size_t, vp]
         L.tree_verify_sample.restype = C.c_int
+        L.dt_load_policy.argtypes = [C.POINTER(dt_policy), C.c_float, C.c_int32, vp, vp]
+        L.dt_load_policy.restype = C.c_int
         L.dt_status_string.argtypes = [C.c_int]
         L.dt_status_string.restype = C.c_char_p
         L.dt_timing_enable.argtypes = [C.c_int32]
@@ -208,6 +215,18 @@ def tree_verify_sample(p: dt_params, tree: dict, block_logits: torch.Tensor, U: 
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     if rc != DT_OK:
         raise DtError("tree_verify_sample", rc)
+
+
+def load_policy(load: float, R: int, *, tau_max: float, capacity: int, Ncap: int):
+    """(tau[R] float32, n_budget[R] int32) host arrays from dt_load_policy."""
+    import numpy as np
+    pol = dt_policy(float(tau_max), int(capacity), int(Ncap))
+    tau = np.zeros(R, np.float32)
+    nb = np.zeros(R, np.int32)
+    rc = lib().dt_load_policy(C.byref(pol), float(load), int(R), tau.ctypes.data, nb.ctypes.data)
+    if rc != DT_OK:
+        raise DtError("dt_load_policy", rc)
+    return tau, nb
 
 
 def timing_enable(on: bool) -> None:

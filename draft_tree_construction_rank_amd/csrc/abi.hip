@@ -333,6 +333,23 @@ dt_status tree_verify_sample(const dt_params* p, const dt_tree* tree, const void
     return DT_OK;
 }
 
+dt_status dt_load_policy(const dt_policy* pol, float load, int32_t R, float* tau,
+                         int32_t* n_budget) {
+    if (!pol || !tau || !n_budget || R < 1) return DT_EINVAL;
+    if (!std::isfinite(load) || load < 0.0f || load > 1.0f) return DT_EINVAL;
+    if (!std::isfinite(pol->tau_max) || pol->tau_max < 0.0f || pol->tau_max > 1.0f) return DT_EINVAL;
+    if (pol->Ncap < 1 || pol->Ncap > kMaxNcap || pol->capacity < 0) return DT_EINVAL;
+    const double avail = (1.0 - (double)load) * (double)pol->capacity;
+    long long n = (long long)std::floor(avail / (double)R);
+    n = n < 1 ? 1 : (n > pol->Ncap ? pol->Ncap : n);
+    const float t = pol->tau_max * load;
+    for (int32_t i = 0; i < R; ++i) {
+        tau[i] = t;
+        n_budget[i] = (int32_t)n;
+    }
+    return DT_OK;
+}
+
 dt_status dt_timing_enable(int32_t on) {
     std::lock_guard<std::mutex> lk(g_timing.mu);
     g_timing.on = on != 0;

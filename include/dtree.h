@@ -196,6 +196,25 @@ dt_status tree_verify_sample(const dt_params* p, const dt_tree* tree, const void
                              const void* target_logits, const dt_verify_out* out,
                              void* workspace, size_t ws_bytes, void* stream);
 
+/* Load-adaptive per-round tree sizing (TreeSpark article, core idea: path survival drives
+ * best-first expansion, per-round stopping and a load-adaptive serving policy; as load rises
+ * the tree shrinks back toward a chain).  The pages give no formula; this is the reading
+ * taken.  Under calibration a node's survival estimates the probability that its path is
+ * accepted, so the stopping threshold acts as the price of one more verified token:
+ *   tau[i]      = tau_max * load
+ *   n_budget[i] = clamp(floor((1 - load) * capacity / R), 1, Ncap)
+ * with load in [0, 1] the share of the target forward's token capacity (capacity tokens per
+ * round for this batch) taken by other work.  Host function: tau and n_budget are HOST
+ * arrays of R entries (copy them to the device for tree_build).  DT_EINVAL for R < 1,
+ * Ncap outside 1..64, capacity < 0, or load / tau_max not finite or outside [0, 1]. */
+typedef struct dt_policy {
+    float tau_max;    /* threshold at full load, in [0, 1] */
+    int32_t capacity; /* target-forward tokens per round available to this batch at no load */
+    int32_t Ncap;     /* largest node budget per request (the tree arrays' width) */
+} dt_policy;
+dt_status dt_load_policy(const dt_policy* pol, float load, int32_t R, float* tau,
+                         int32_t* n_budget);
+
 /* Human-readable name of a status code (static string). */
 const char* dt_status_string(dt_status s);
 

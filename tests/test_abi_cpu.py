@@ -123,3 +123,28 @@ def test_noalloc_rejects_rounds_beyond_its_scratch(lib):
                                   C.byref(t), None) == B.DT_EINVAL
     assert lib.tree_build_noalloc(C.byref(_params()), None, fake, fake, fake, fake, fake,
                                   C.byref(t), None) == B.DT_EINVAL
+
+
+def test_load_policy_closed_form(lib):
+    """dt_load_policy: tau = tau_max * load, budget = clamp(floor((1 - load) * C / R), 1, Ncap),
+    for every request; monotone in load (trees shrink as load rises)."""
+    import numpy as np
+    prev = None
+    for load in np.linspace(0.0, 1.0, 21).astype(np.float32):
+        tau, nb = B.load_policy(float(load), 8, tau_max=0.5, capacity=1024, Ncap=64)
+        want = int(np.clip(np.floor((1.0 - np.float64(load)) * 1024 / 8), 1, 64))
+        assert (nb == want).all() and np.allclose(tau, np.float32(0.5) * load, rtol=0, atol=0)
+        if prev is not None:
+            assert (nb <= prev[1]).all() and (tau >= prev[0]).all()
+        prev = (tau, nb)
+    tau, nb = B.load_policy(0.0, 64, tau_max=0.5, capacity=4096, Ncap=64)
+    assert (nb == 64).all() and (tau == 0).all()
+    tau, nb = B.load_policy(1.0, 64, tau_max=0.5, capacity=4096, Ncap=64)
+    assert (nb == 1).all() and (tau == 0.5).all()
+    for bad in (dict(load=-0.1), dict(load=1.5), dict(load=float("nan")), dict(tau_max=2.0),
+                dict(capacity=-1), dict(Ncap=65), dict(R=0)):
+        kw = dict(load=0.5, R=4, tau_max=0.5, capacity=100, Ncap=64)
+        kw.update(bad)
+        with pytest.raises(B.DtError):
+            B.load_policy(kw["load"], kw["R"], tau_max=kw["tau_max"], capacity=kw["capacity"],
+                          Ncap=kw["Ncap"])

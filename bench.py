@@ -435,6 +435,99 @@ def oracle_per_config(inputs, rounds=3):
     return out
 
 
+# ---------------------------------------------------------------- tree attention ----------
+ATTN_WORKLOADS = {
+    # name: (R, Hq, Hkv, Ncap, ctx_lo, ctx_hi)
+    "batched_R64_N64": (64, 32, 8, 64, 512, 2048),
+    "R1_N64_ctx2048": (1, 32, 8, 64, 2048, 2048),
+    "R1_N32_ctx1024": (1, 32, 8, 32, 1024, 1024),
+    "batched_R64_N64_14b": (64, 40, 8, 64, 512, 2048),
+}
+
+
+def _attn_inputs(torch, R, Hq, Hkv, Ncap, ctx_lo, ctx_hi, seed=7):
+    """Device inputs drawn directly on the GPU (N(0,1) bf16), random full trees of Ncap
+    nodes (parent uniform over the root and earlier nodes), ancestor masks and depths built
+    here on the host."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(ctx_lo, ctx_hi + 1, size=R).astype(np.int32)
+    Cmax = ctx_hi + Ncap + 1
+    par = np.full((R, Ncap), -1, np.int64)
+    depth = np.zeros((R, Ncap), np.int64)
+    masks = np.zeros((R, Ncap), np.uint64)
+    for r in range(R):
+        m = [0] * Ncap
+        for i in range(Ncap):
+            p = int(rng.integers(-1, i)) if i else -1
+            par[r, i] = p
+            depth[r, i] = 1 + (depth[r, p] if p >= 0 else 0)
+            m[i] = (m[p] if p >= 0 else 0) | (1 << i)
+        masks[r] = np.array(m, dtype=np.uint64)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    D = 128
+    Q = torch.randn((R, Hq, Ncap + 1, D), generator=g, device="cuda").to(torch.bfloat16)
+    K = torch.randn((R, Hkv, Cmax, D), generator=g, device="cuda").to(torch.bfloat16)
+    V = torch.randn((R, Hkv, Cmax, D), generator=g, device="cuda").to(torch.bfloat16)
+    return dict(Q=Q, K=K, V=V, O=torch.empty_like(Q), Cmax=Cmax, ctx=ctx, depth=depth,
+                ctx_d=torch.from_numpy(ctx).cuda(),
+                n_d=torch.full((R,), Ncap, dtype=torch.int32, device="cuda"),
+                anc_d=torch.from_numpy(masks.view(np.int64)).cuda())
+
+
+def attention_profile(torch, B, flusher, steps=30):
+    """tree_attention alone: warm and cold µs per call, algorithmic HBM bytes (K and V of
+    every used slot once, Q and O) and MFMA flops (4 * D per visible (query, key) pair) per
+    call, and the fractions of the HBM and bf16 MFMA peaks."""
+    out = {}
+    for name, (R, Hq, Hkv, Ncap, lo, hi) in ATTN_WORKLOADS.items():
+        d = _attn_inputs(torch, R, Hq, Hkv, Ncap, lo, hi)
+        p = B.make_attn_params(R=R, Hq=Hq, Hkv=Hkv, D=128, Ncap=Ncap, Cmax=d["Cmax"],
+                               scale=1.0 / math.sqrt(128))
+        ws = B.alloc_attn_workspace(p, "cuda")
+        call = lambda: B.tree_attention(p, d["Q"], d["K"], d["V"], d["ctx_d"], d["n_d"],
+                                        d["anc_d"], d["O"], ws)
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        warm = _stats(time_calls(torch, [call], steps)[0])
+        cold = _stats(time_calls(torch, [call], max(10, steps // 3), flusher)[0])
+        keys = d["ctx"].astype("int64") + Ncap + 1
+        byts = float(Hkv * keys.sum() * 128 * 2 * 2 + 2 * R * Hq * (Ncap + 1) * 128 * 2)
+        # visible keys: the root query sees ctx + 1 slots, node i sees ctx + 1 + depth_i
+        vis = float((d["ctx"].astype("int64") + 1).sum() * (Ncap + 1) + d["depth"].sum())
+        flops = 4.0 * 128 * Hq * vis
+        t = warm["median"] * 1e-6
+        out[name] = {"R": R, "Hq": Hq, "Hkv": Hkv, "N": Ncap, "ctx": [lo, hi],
+                     "us_warm": warm, "us_cold": cold,
+                     "workspace_bytes": B.dt_attn_workspace_bytes(p),
+                     "alg_bytes": int(byts), "alg_flops": int(flops),
+                     "hbm_gbs": round(byts / t / 1e9, 1),
+                     "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_tflops": round(flops / t / 1e12, 1),
+                     "mfma_frac": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del d, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def attention_oracle_rate():
+    """The float64 oracle on the host for one request of the batched workload (all 32 query
+    heads, 65 tree positions, context 1280): requests per second on one core."""
+    import numpy as np
+    import oracle.attention as oa
+    from draft_tree_construction_rank_amd import attn_inputs
+    inst = attn_inputs.make_attn_instance(seed=5, R=1, Hq=32, Hkv=8, D=128, Ncap=64,
+                                          ctx_lo=1280, ctx_hi=1280, threads=1)
+    Q, K, V = inst.f32("Q"), inst.f32("K"), inst.f32("V")
+    t0 = time.perf_counter()
+    oa.tree_attention(Q, K, V, inst.ctx_len, inst.n_nodes, inst.parent, inst.scale)
+    dt = time.perf_counter() - t0
+    return {"requests_per_s": round(1.0 / dt, 3), "cores": 1,
+            "sample": "one request, 32 query heads x 65 tree positions, context 1280"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -538,6 +631,9 @@ def main():
                             for T in (0.6, 1.0, 1.5)}
         extras["mechanism_isolation_markov_target"] = mechanism_isolation(torch, rt, inputs)
         extras["multi_round_load_sweep"] = load_sweep(torch, rt, inputs)
+        extras["tree_attention"] = attention_profile(torch, B, flusher)
+        if not args.no_cpu_baseline:
+            extras["tree_attention"]["oracle"] = attention_oracle_rate()
         extras["targets"] = {
             "tree_build_us_R1_B16_k4_N64": {"measured_median": extras["tree_build_us_R1_B16_k4_N64"],
                                             "target": 100.0,

@@ -23,7 +23,7 @@ DT_REQ_BAD_ROOT, DT_REQ_BUDGET_CLAMPED = 1, 2
 
 EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_build_noalloc", "tree_verify_greedy",
             "tree_verify_sample", "dt_load_policy", "dt_status_string", "dt_timing_enable",
-            "dt_timing_read")
+            "dt_timing_read", "dt_attn_workspace_bytes", "tree_attention")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # DT_NOALLOC_SCRATCH_BYTES of include/dtree.h
 
 
@@ -50,6 +50,11 @@ class dt_tree(C.Structure):
 
 class dt_policy(C.Structure):
     _fields_ = [("tau_max", C.c_float), ("capacity", C.c_int32), ("Ncap", C.c_int32)]
+
+
+class dt_attn_params(C.Structure):
+    _fields_ = [("R", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("D", C.c_int32),
+                ("Ncap", C.c_int32), ("Cmax", C.c_int32), ("scale", C.c_float)]
 
 
 class dt_verify_out(C.Structure):
@@ -84,6 +89,11 @@ def lib() -> C.CDLL:
         L.tree_verify_sample.restype = C.c_int
         L.dt_load_policy.argtypes = [C.POINTER(dt_policy), C.c_float, C.c_int32, vp, vp]
         L.dt_load_policy.restype = C.c_int
+        A = C.POINTER(dt_attn_params)
+        L.dt_attn_workspace_bytes.argtypes = [A, C.POINTER(C.c_size_t)]
+        L.dt_attn_workspace_bytes.restype = C.c_int
+        L.tree_attention.argtypes = [A, vp, vp, vp, vp, C.POINTER(dt_tree), vp, vp, C.c_size_t, vp]
+        L.tree_attention.restype = C.c_int
         L.dt_status_string.argtypes = [C.c_int]
         L.dt_status_string.restype = C.c_char_p
         L.dt_timing_enable.argtypes = [C.c_int32]
@@ -215,6 +225,53 @@ def tree_verify_sample(p: dt_params, tree: dict, block_logits: torch.Tensor, U: 
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     if rc != DT_OK:
         raise DtError("tree_verify_sample", rc)
+
+
+def make_attn_params(*, R: int, Hq: int, Hkv: int, D: int, Ncap: int, Cmax: int,
+                     scale: float) -> dt_attn_params:
+    return dt_attn_params(int(R), int(Hq), int(Hkv), int(D), int(Ncap), int(Cmax), float(scale))
+
+
+def dt_attn_workspace_bytes(p: dt_attn_params) -> int:
+    n = C.c_size_t(0)
+    rc = lib().dt_attn_workspace_bytes(C.byref(p), C.byref(n))
+    if rc != DT_OK:
+        raise DtError("dt_attn_workspace_bytes", rc)
+    return int(n.value)
+
+
+def alloc_attn_workspace(p: dt_attn_params, device) -> Optional[torch.Tensor]:
+    n = dt_attn_workspace_bytes(p)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def tree_attention(p: dt_attn_params, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                   ctx_len: torch.Tensor, n_nodes: torch.Tensor, anc_mask: torch.Tensor,
+                   O: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Q [R][Hq][Ncap+1][D], K/V [R][Hkv][Cmax][D], O like Q (bf16); ctx_len, n_nodes [R]
+    int32; anc_mask [R][Ncap] (int64 or uint64 storage).  Shapes and dtypes are checked
+    here, before anything reaches the device."""
+    R, Hq, Hkv, D, Ncap, Cmax = p.R, p.Hq, p.Hkv, p.D, p.Ncap, p.Cmax
+    want = {"Q": (Q, (R, Hq, Ncap + 1, D), torch.bfloat16),
+            "K": (K, (R, Hkv, Cmax, D), torch.bfloat16),
+            "V": (V, (R, Hkv, Cmax, D), torch.bfloat16),
+            "O": (O, (R, Hq, Ncap + 1, D), torch.bfloat16),
+            "ctx_len": (ctx_len, (R,), torch.int32),
+            "n_nodes": (n_nodes, (R,), torch.int32)}
+    for name, (t, shape, dt) in want.items():
+        if tuple(t.shape) != shape or t.dtype != dt or t.device.type != "cuda":
+            raise ValueError("tree_attention: %s must be a %s cuda tensor of shape %s, got %s %s"
+                             % (name, dt, shape, t.dtype, tuple(t.shape)))
+    if tuple(anc_mask.shape) != (R, Ncap) or anc_mask.element_size() != 8:
+        raise ValueError("tree_attention: anc_mask must be [R][Ncap] with 8-byte elements")
+    ts = dt_tree()
+    ts.n_nodes = _ptr(n_nodes)
+    ts.anc_mask = _ptr(anc_mask)
+    rc = lib().tree_attention(C.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(ctx_len), C.byref(ts),
+                              _ptr(O), _ptr(workspace),
+                              0 if workspace is None else workspace.numel(), _stream(stream))
+    if rc != DT_OK:
+        raise DtError("tree_attention", rc)
 
 
 def load_policy(load: float, R: int, *, tau_max: float, capacity: int, Ncap: int):

@@ -243,6 +243,18 @@ static char* scratch_ptr() {
     return g_scratch.ptr[dev];
 }
 
+// ---- tree attention
+static dt_status validate_attn(const dt_attn_params* p) {
+    if (!p) return DT_EINVAL;
+    if (p->R < 1 || p->R > 65536 || p->Hkv < 1 || p->Hkv > 256 || p->Hq < p->Hkv ||
+        p->Hq % p->Hkv != 0 || p->Hq / p->Hkv > 16)
+        return DT_EINVAL;
+    if (p->D != 128 || p->Ncap < 1 || p->Ncap > kMaxNcap || p->Cmax < 2 || p->Cmax > (1 << 24))
+        return DT_EINVAL;
+    if (!std::isfinite(p->scale) || !(p->scale > 0.0f)) return DT_EINVAL;
+    return DT_OK;
+}
+
 }  // namespace dt
 
 using namespace dt;
@@ -329,6 +341,34 @@ dt_status tree_verify_sample(const dt_params* p, const dt_tree* tree, const void
     if (ws_bytes < lay.total) return DT_ENOSPC;
     if (launch_verify_sample(p, lay, (char*)workspace, tree, block_logits, U, Wt, root_token,
                              target_logits, out, (hipStream_t)stream) != hipSuccess)
+        return DT_EDEVICE;
+    return DT_OK;
+}
+
+dt_status dt_attn_workspace_bytes(const dt_attn_params* p, size_t* bytes) {
+    const dt_status v = validate_attn(p);
+    if (v != DT_OK) return v;
+    if (!bytes) return DT_EINVAL;
+    *bytes = attn_plan(p).total;
+    return DT_OK;
+}
+
+dt_status tree_attention(const dt_attn_params* p, const void* Q, const void* K, const void* V,
+                         const int32_t* ctx_len, const dt_tree* tree, void* O,
+                         void* workspace, size_t ws_bytes, void* stream) {
+    const dt_status v = validate_attn(p);
+    if (v != DT_OK) return v;
+    if (!Q || !K || !V || !ctx_len || !tree || !tree->n_nodes || !tree->anc_mask || !O)
+        return DT_EINVAL;
+    if (((uintptr_t)Q & 15) || ((uintptr_t)K & 15) || ((uintptr_t)V & 15) || ((uintptr_t)O & 15))
+        return DT_EINVAL;
+    const AttnPlan pl = attn_plan(p);
+    if (pl.total > 0) {
+        if (!workspace || ((uintptr_t)workspace & 255)) return DT_EINVAL;
+        if (ws_bytes < pl.total) return DT_ENOSPC;
+    }
+    if (launch_tree_attention(p, pl, Q, K, V, ctx_len, tree->n_nodes, tree->anc_mask, O,
+                              (char*)workspace, (hipStream_t)stream) != hipSuccess)
         return DT_EDEVICE;
     return DT_OK;
 }

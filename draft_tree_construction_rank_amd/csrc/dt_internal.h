@@ -194,4 +194,17 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
                                 const void* Wt, const int32_t* root_token, const void* target,
                                 const dt_verify_out* out, hipStream_t st);
 
+// Tree attention (attn_kernels.hip): G grouped query heads per key/value head, QG query
+// groups of NW wavefronts (one 32-query tile each), S key splits; with S > 1 the workspace
+// holds po_bytes of partial outputs, then the (max, sum) pairs.
+struct AttnPlan {
+    int G, QG, NW, S;
+    size_t po_bytes, total;
+};
+AttnPlan attn_plan(const dt_attn_params* p);
+hipError_t launch_tree_attention(const dt_attn_params* p, const AttnPlan& pl, const void* Q,
+                                 const void* K, const void* V, const int32_t* ctx_len,
+                                 const int32_t* n_nodes, const uint64_t* anc, void* O,
+                                 char* ws, hipStream_t st);
+
 }  // namespace dt

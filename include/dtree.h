@@ -216,6 +216,47 @@ dt_status dt_load_policy(const dt_policy* pol, float load, int32_t R, float* tau
                          int32_t* n_budget);
 
 /* Human-readable name of a status code (static string). */
+/* ---- Tree attention: the verify forward's attention over a round's trees -------------
+ * One attention layer of the target model that scores every tree position in one pass
+ * (PCTree summary, introduction: the target checks all nodes of the tree in one forward;
+ * TreeSpark article, introduction: one verification pass over several continuations).
+ * Tree position j of request r is the root (j = 0, the round's last emitted token) or node
+ * j - 1 of the emitted tree.  Its key and value sit in the cache at slot ctx_len[r] + j,
+ * after the request's context.  The query of position j sees every context slot, the
+ * root's slot, and, for a node, the slots of the nodes set in its ancestor mask (itself and
+ * its ancestors): each node is scored as if its own path were the whole continuation.
+ * Scores scale * q.k, softmax over the visible slots, output = the weighted sum of values.
+ * Query head hq uses key/value head hq / (Hq / Hkv). */
+typedef struct dt_attn_params {
+    int32_t R;     /* requests, 1..65536 */
+    int32_t Hq;    /* query heads, a multiple of Hkv, Hq / Hkv <= 16 */
+    int32_t Hkv;   /* key/value heads, 1..256 */
+    int32_t D;     /* head dimension: 128 */
+    int32_t Ncap;  /* tree capacity, 1..64: Q and O hold Ncap + 1 positions per head */
+    int32_t Cmax;  /* cache slots per (request, key/value head), 2..2^24 */
+    float scale;   /* score scale, finite and > 0 (usually 1/sqrt(D)) */
+} dt_attn_params;
+
+/* Workspace for tree_attention (0 when the call needs none).  DT_EINVAL on bad parameters. */
+dt_status dt_attn_workspace_bytes(const dt_attn_params* p, size_t* bytes);
+
+/* Q        [R][Hq][Ncap+1][D] bf16, row j = tree position j.
+ * K, V     [R][Hkv][Cmax][D]  bf16 caches; slots ctx_len[r] .. ctx_len[r] + n_nodes[r]
+ *          hold the tree's keys and values.
+ * ctx_len  [R] int32 context entries before the root.
+ * tree     the emitted trees: only n_nodes and anc_mask are read (tree_build's output, or
+ *          any trees whose masks have bit i set only for i < n_nodes).
+ * O        [R][Hq][Ncap+1][D] bf16 output.  Rows past n_nodes, and every row of a request
+ *          whose n_nodes is outside [0, Ncap] or whose tree does not fit the cache
+ *          (ctx_len < 0 or ctx_len + n_nodes + 1 > Cmax), are written as zeros.
+ * workspace  device memory of dt_attn_workspace_bytes() bytes, 256-byte aligned (may be
+ *          NULL when that size is 0).
+ * Q, K, V and O must be 16-byte aligned.  Arithmetic: bf16 MFMA products with fp32
+ * accumulation, fp32 online softmax, probabilities rounded to bf16 for the value product. */
+dt_status tree_attention(const dt_attn_params* p, const void* Q, const void* K, const void* V,
+                         const int32_t* ctx_len, const dt_tree* tree, void* O,
+                         void* workspace, size_t ws_bytes, void* stream);
+
 const char* dt_status_string(dt_status s);
 
 /* Measurement support (host only, not thread-safe): when enabled, the library brackets each

@@ -148,3 +148,43 @@ def test_load_policy_closed_form(lib):
         with pytest.raises(B.DtError):
             B.load_policy(kw["load"], kw["R"], tau_max=kw["tau_max"], capacity=kw["capacity"],
                           Ncap=kw["Ncap"])
+
+
+def _attn(**kw):
+    d = dict(R=4, Hq=32, Hkv=8, D=128, Ncap=64, Cmax=2113, scale=0.08838834764831845)
+    d.update(kw)
+    return B.make_attn_params(**d)
+
+
+@pytest.mark.parametrize("kw", [dict(R=0), dict(Hkv=0), dict(Hq=12, Hkv=8), dict(Hq=34, Hkv=2),
+                                dict(D=64), dict(Ncap=0), dict(Ncap=65), dict(Cmax=1),
+                                dict(Cmax=(1 << 24) + 1), dict(scale=0.0),
+                                dict(scale=float("nan")), dict(scale=-1.0)])
+def test_attention_bad_params_rejected(lib, kw):
+    n = C.c_size_t(0)
+    assert lib.dt_attn_workspace_bytes(C.byref(_attn(**kw)), C.byref(n)) == B.DT_EINVAL
+
+
+def test_attention_workspace(lib):
+    # wide batches run as one key split (no workspace); one request splits its keys
+    assert B.dt_attn_workspace_bytes(_attn(R=64)) == 0
+    one = B.dt_attn_workspace_bytes(_attn(R=1))
+    assert one > 0 and one % 256 == 0
+    # short caches are never split
+    assert B.dt_attn_workspace_bytes(_attn(R=1, Cmax=100)) == 0
+
+
+def test_attention_null_and_misaligned_rejected(lib):
+    p = _attn(R=1)
+    need = B.dt_attn_workspace_bytes(p)
+    t = B.dt_tree()
+    t.n_nodes, t.anc_mask = 0x2000, 0x2000
+    fake = 0x10000
+    call = lambda *a: lib.tree_attention(C.byref(p), *a)
+    assert call(None, fake, fake, fake, C.byref(t), fake, fake, need, None) == B.DT_EINVAL
+    assert call(fake + 2, fake, fake, fake, C.byref(t), fake, fake, need, None) == B.DT_EINVAL
+    assert call(fake, fake, fake, fake, C.byref(t), fake, None, need, None) == B.DT_EINVAL
+    assert call(fake, fake, fake, fake, C.byref(t), fake, fake, need - 1, None) == B.DT_ENOSPC
+    assert call(fake, fake, fake, fake, C.byref(t), fake, fake + 16, need, None) == B.DT_EINVAL
+    t.anc_mask = None
+    assert call(fake, fake, fake, fake, C.byref(t), fake, fake, need, None) == B.DT_EINVAL

@@ -34,9 +34,14 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 abf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float af32x16;
 
 constexpr int kAttD = 128;             // head dimension
-// bf16 per V^T row in LDS: 136 B (64 keys) or 72 B (32 keys), conflict-free b64 reads
-template <int BLK> constexpr int att_vs() { return BLK + 4; }
-constexpr int kAttWaves = 9;           // at most 9 query wavefronts per workgroup
+#ifndef DT_ATTN_MAX_WAVES
+#define DT_ATTN_MAX_WAVES 9
+#endif
+constexpr int kAttWaves = DT_ATTN_MAX_WAVES;  // query wavefronts per workgroup, at most
+#ifndef DT_ATTN_BLK_SMALL
+#define DT_ATTN_BLK_SMALL 32
+#endif
+constexpr int kAttBlkSmall = DT_ATTN_BLK_SMALL;  // keys per block below 8 wavefronts
 constexpr int kAttMinWaves = 4;        // wavefronts that share the LDS fills at least
 constexpr float kLazy = 8.0f;          // rescale only when the max grows by more than 2^8
 
@@ -55,9 +60,28 @@ struct AttnArgs {
     float c2;        // scale * log2(e)
 };
 
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef float af32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 abf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even; v_cvt_pk_bf16_f32), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((af32x2){a, b}, abf16x2));
+}
+
+// 2^x on the transcendental unit (v_exp_f32): results below the normal range flush to
+// zero, which only drops probabilities under 2^-126 of the running maximum.
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef short as16x4 __attribute__((ext_vector_type(4)));
+
+// Two transposing LDS reads (four bf16 each) joined into one MFMA operand.
+__device__ __forceinline__ abf16x8 tr_pair(const uint16_t* p0, const uint16_t* p1) {
+    typedef __attribute__((address_space(3))) as16x4 lds_v4;
+    const as16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)p0);
+    const as16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)p1);
+    typedef short as16x8 __attribute__((ext_vector_type(8)));
+    const as16x8 z = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+    return __builtin_bit_cast(abf16x8, z);
 }
 
 // Workgroup barrier that waits only for this wavefront's LDS accesses: loads still in flight
@@ -77,39 +101,75 @@ __device__ __forceinline__ bool attn_request_ok(int ctx, int n, int Ncap, int Cm
     return n >= 0 && n <= Ncap && ctx >= 0 && ctx <= Cmax - n - 1;
 }
 
-// Workgroup index -> (unit = request * Hkv + head, split, query group).  Workgroups are
-// dispatched round-robin over the 8 XCDs; the query groups of one (unit, split) are placed 8
-// apart so that they land on the same XCD and share its L2 for the K/V blocks.
-__device__ __forceinline__ void attn_decode(const AttnArgs& a, int& unit, int& s, int& qg) {
+// Workgroup index -> (ordered unit u, split, query group).  Workgroups are dispatched
+// round-robin over the 8 XCDs; the query groups of one (unit, split) are placed 8 apart so
+// that they land on the same XCD and share its L2 for the K/V blocks.
+__device__ __forceinline__ void attn_decode(const AttnArgs& a, int& u, int& s, int& qg) {
     const int b = blockIdx.x;
     const int lo = b & 7, mid = (b >> 3) % a.QG, hi = (b >> 3) / a.QG;
     const int w = hi * 8 + lo;  // (unit, split) index
-    unit = w / a.S;
+    u = w / a.S;
     s = w % a.S;
     qg = mid;
 }
 
-// Three wavefronts per SIMD (168 VGPRs each): nine query wavefronts fit one compute unit.
-// Keys go through LDS in blocks of BLK: 64 with 512 threads or more, else 32.  K blocks are
-// copied global -> LDS directly (global_load_lds, 16 bytes a lane, 1 KB a wavefront: four
-// 256-byte rows), double-buffered; the 16-byte segment s of row k sits at position
-// s ^ (k % 16) of its row, so that the 16 rows read by a quarter-wavefront fall in 16
-// distinct bank groups.  V blocks go through registers (one (key pair, 8 d) unit a thread),
-// transposed on the store to LDS.
+// Ordered units run the requests longest first (keys ctx_len + n_nodes + 1; invalid requests
+// count zero; ties by request index), so that the dispatcher, which hands out workgroups in
+// index order as compute units free up, pairs long requests with short ones instead of
+// leaving a few compute units with two long ones.  Every workgroup derives the order itself:
+// the key counts go to LDS and thread i ranks request i by counting the requests before it
+// (R <= kLptMax; larger batches keep the request order).
+constexpr int kLptMax = 1024;
+
+__device__ __forceinline__ int attn_keys(const AttnArgs& a, int i) {
+    const int ctx = a.ctx_len[i], n = a.n_nodes[i];
+    return attn_request_ok(ctx, n, a.Ncap, a.Cmax) ? ctx + n + 1 : 0;
+}
+
+template <int NT>
+__device__ __forceinline__ int lpt_request(const AttnArgs& a, int k, int* sL, int* sP) {
+    if (a.R > kLptMax) return k;
+    for (int i = threadIdx.x; i < a.R; i += NT) sL[i] = attn_keys(a, i);
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.R; i += NT) {
+        const int Li = sL[i];
+        int rank = 0;
+        for (int j = 0; j < a.R; ++j) {
+            const int Lj = sL[j];
+            rank += (Lj > Li) | ((Lj == Li) & (j < i));
+        }
+        sP[rank] = i;
+    }
+    __syncthreads();
+    return sP[k];
+}
+
+// Keys go through LDS in blocks of BLK (64 with 512 threads or more, else 32).  K and V
+// blocks are copied global -> LDS directly (global_load_lds: 16 bytes a lane, 1 KB a
+// wavefront, i.e. four 256-byte rows) into double buffers, so a block's copies are in
+// flight while the previous block is computed and one barrier per block suffices.  Rows
+// are swizzled in 16-byte segments against bank conflicts: segment s of K row k sits at
+// position s ^ (k % 16) (a quarter-wavefront reads 16 rows at one segment), segment s of V
+// row k at s ^ 4(k % 4) (a half-wavefront's transposing reads cover four rows and four
+// segments).  V is read with ds_read_b64_tr_b16: in each 16-lane group, lane 4a + b receives
+// element b of the 8-byte rows addressed by lanes a, 4 + a, 8 + a and 12 + a; with lane
+// 4e + a addressing V row (key) e of its half-wavefront's four keys at head-dimension columns
+// 4a.. of its 16-column half, lane 4a + b receives four keys of column 4a + b, which is the
+// MFMA A-operand fragment of V^T for that row.
 template <int NW, int BLK>
 __global__ __launch_bounds__(NW * 64, 3) void k_tree_attn(AttnArgs a) {
     constexpr int NT = NW * 64;
-    constexpr int kAttVS = att_vs<BLK>();
-    constexpr int VU = (BLK / 2 * 16 + NT - 1) / NT;   // (key pair, 8 d) V units per thread
-    static_assert(VU <= 1, "prefetch registers");
     __shared__ __align__(1024) uint16_t sK0[BLK * kAttD];
     __shared__ __align__(1024) uint16_t sK1[BLK * kAttD];
-    __shared__ __align__(16) uint16_t sV[kAttD * kAttVS];
+    __shared__ __align__(1024) uint16_t sV0[BLK * kAttD];
+    __shared__ __align__(1024) uint16_t sV1[BLK * kAttD];
+    __shared__ int sL[kLptMax], sP[kLptMax];
 
-    int unit, s, qg;
-    attn_decode(a, unit, s, qg);
-    if (unit >= a.units) return;
-    const int r = unit / a.Hkv, h = unit % a.Hkv;
+    int u, s, qg;
+    attn_decode(a, u, s, qg);
+    if (u >= a.units) return;
+    const int r = lpt_request<NT>(a, u / a.Hkv, sL, sP), h = u % a.Hkv;
+    const int unit = r * a.Hkv + h;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane & 31, hh = lane >> 5;
     const int ctx = a.ctx_len[r], n = a.n_nodes[r];
@@ -156,37 +216,25 @@ __global__ __launch_bounds__(NW * 64, 3) void k_tree_attn(AttnArgs a) {
 
     const uint16_t* Kb = a.K + (size_t)unit * a.Cmax * kAttD;
     const uint16_t* Vb = a.V + (size_t)unit * a.Cmax * kAttD;
-    uint4 pv[2];
-    auto issue_k = [&](int b, uint16_t* dst) {
+    // one block's K and V rows, copied by the wavefronts in 1 KB chunks (keys past the
+    // request's last slot repeat it; their scores are masked)
+    auto issue = [&](int b, uint16_t* kdst, uint16_t* vdst) {
         const int key0 = b * BLK;
         for (int ch = wave; ch < BLK / 4; ch += NW) {
             const int row = 4 * ch + (lane >> 4);
-            const int seg = (lane & 15) ^ (row & 15);
-            const int key = min(key0 + row, L - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(Kb + (size_t)key * kAttD + seg * 8),
-                                             (void*)(dst + ch * 512), 16, 0, 0);
+            const size_t src = (size_t)min(key0 + row, L - 1) * kAttD;
+            const int ks = (lane & 15) ^ (row & 15), vs = (lane & 15) ^ (4 * (row & 3));
+            __builtin_amdgcn_global_load_lds((const void*)(Kb + src + ks * 8),
+                                             (void*)(kdst + ch * 512), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(Vb + src + vs * 8),
+                                             (void*)(vdst + ch * 512), 16, 0, 0);
         }
     };
-    auto issue_v = [&](int b) {
-        const int key0 = b * BLK;
-        const int pr = (tid >> 4) & (BLK / 2 - 1), db = tid & 15;
-        const int k0 = min(key0 + 2 * pr, L - 1), k1 = min(key0 + 2 * pr + 1, L - 1);
-        pv[0] = *(const uint4*)(Vb + (size_t)k0 * kAttD + db * 8);
-        pv[1] = *(const uint4*)(Vb + (size_t)k1 * kAttD + db * 8);
-    };
-    auto store_v = [&]() {
-        if (VU * NT == BLK * 8 || tid < BLK * 8) {
-            const int pr = tid >> 4, db = tid & 15;
-            const uint32_t x0[4] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w};
-            const uint32_t x1[4] = {pv[1].x, pv[1].y, pv[1].z, pv[1].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (e & 1) ? (x0[e >> 1] >> 16) : (x0[e >> 1] & 0xFFFFu);
-                const uint32_t hi = (e & 1) ? (x1[e >> 1] & 0xFFFF0000u) : (x1[e >> 1] << 16);
-                *(uint32_t*)(sV + (db * 8 + e) * kAttVS + 2 * pr) = lo | hi;
-            }
-        }
-    };
+    // per-lane part of the transposing V reads: row 4hh + e (e = (lane % 16) / 4) of each
+    // 16-key step, columns 16 * ((lane / 16) % 2) + 4 * (lane % 4) of each 32-column tile
+    const int tr_e = (lane & 15) >> 2, tr_a = lane & 3, tr_g = (lane >> 4) & 1;
+    const int tr_row = 4 * hh + tr_e;
+    const int tr_lo = 2 * tr_g + (tr_a >> 1), tr_in = 4 * (tr_a & 1);
 
     af32x16 o[4];
 #pragma unroll
@@ -195,17 +243,14 @@ __global__ __launch_bounds__(NW * 64, 3) void k_tree_attn(AttnArgs a) {
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.0f;
     float m = -INFINITY, lsum = 0.0f;
 
-    // one key block: wait for its copies, store its V^T, start the next block's copies
-    // (into the other K buffer), then every query wavefront works on it
-    auto step = [&](int b, const uint16_t* __restrict__ kbuf, uint16_t* __restrict__ knext) {
+    // one key block: wait for this thread's copies of it, barrier (every copy landed, every
+    // wavefront done with the previous block and so with the buffers the next block's copies
+    // go to), start the next block's copies, then every query wavefront works on it
+    auto step = [&](int b, const uint16_t* __restrict__ kbuf, const uint16_t* __restrict__ vbuf,
+                    uint16_t* __restrict__ knext, uint16_t* __restrict__ vnext) {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         att_barrier();
-        store_v();
-        if (b + 1 < b1) {
-            issue_k(b + 1, knext);
-            issue_v(b + 1);
-        }
-        att_barrier();
+        if (b + 1 < b1) issue(b + 1, knext, vnext);
         if (!active) return;
 #pragma unroll
         for (int kt = 0; kt < BLK / 32; ++kt) {
@@ -221,25 +266,29 @@ __global__ __launch_bounds__(NW * 64, 3) void k_tree_attn(AttnArgs a) {
                 sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                     __builtin_bit_cast(abf16x8, *(const uint4*)(kp + (((2 * ks + hh) ^ (c & 15)) * 8))),
                     qf[ks], sacc, 0, 0, 0);
-            // scores in the log2 domain; element i is key key0 + 8(i/4) + 4hh + i%4
+            // element i is key key0 + 8(i/4) + 4hh + i%4; masked keys become -inf
             const bool tail = key0 + 32 > ctx + 1;
-            float mx = -INFINITY;
+            if (tail) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float v = sacc[i] * a.c2;
-                if (tail) {
+                for (int i = 0; i < 16; ++i) {
+                    // rel < 0: context or root; 0 <= rel < n: node rel, visible when its
+                    // bit is set in this query's mask (the shift amount is masked to stay
+                    // defined; its bit only counts when 0 <= rel < n <= 64)
                     const int rel = key0 + 8 * (i >> 2) + 4 * hh + (i & 3) - ctx - 1;
-                    const bool vis = rel < 0 || (rel < n && ((qmask >> rel) & 1ull));
-                    v = vis ? v : -INFINITY;
+                    const bool bit = (qmask >> ((unsigned)rel & 63u)) & 1ull;
+                    const bool vis = (rel < 0) | ((rel < n) & bit);
+                    sacc[i] = vis ? sacc[i] : -INFINITY;
                 }
-                sacc[i] = v;
-                mx = fmaxf(mx, v);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float mx = sacc[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+            // the maximum in the log2 domain (the scale is positive)
+            mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.c2;
             const bool raise = mx > m + kLazy;
             if (__any(raise)) {
                 const float mn = raise ? mx : m;
-                const float alpha = raise ? exp2f(m - mn) : 1.0f;
+                const float alpha = raise ? ex2(m - mn) : 1.0f;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -251,32 +300,31 @@ __global__ __launch_bounds__(NW * 64, 3) void k_tree_attn(AttnArgs a) {
             uint32_t pw[8];
 #pragma unroll
             for (int i = 0; i < 16; i += 2) {
-                const float p0 = exp2f(sacc[i] - mu), p1 = exp2f(sacc[i + 1] - mu);
+                const float p0 = ex2(fmaf(sacc[i], a.c2, -mu));
+                const float p1 = ex2(fmaf(sacc[i + 1], a.c2, -mu));
                 lsum += p0 + p1;
-                pw[i >> 1] = bf16_rne(p0) | (bf16_rne(p1) << 16);
+                pw[i >> 1] = pack_bf16x2(p0, p1);
             }
             const abf16x8 pb0 = __builtin_bit_cast(abf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
             const abf16x8 pb1 = __builtin_bit_cast(abf16x8, make_uint4(pw[4], pw[5], pw[6], pw[7]));
+            // V^T fragments: keys kt*32 + 16kk + {4hh + 0..3, 8 + 4hh + 0..3} (the same order
+            // as this lane's probabilities), head-dimension row 32dt + c
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const uint16_t* vp = sV + (dt * 32 + c) * kAttVS + kt * 32 + 4 * hh;
-                const uint2 l0 = *(const uint2*)(vp), h0 = *(const uint2*)(vp + 8);
-                const uint2 l1 = *(const uint2*)(vp + 16), h1 = *(const uint2*)(vp + 24);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(abf16x8, make_uint4(l0.x, l0.y, h0.x, h0.y)), pb0, o[dt], 0, 0, 0);
-                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    __builtin_bit_cast(abf16x8, make_uint4(l1.x, l1.y, h1.x, h1.y)), pb1, o[dt], 0, 0, 0);
+                const int col = (((4 * dt) ^ (4 * tr_e)) + tr_lo) * 8 + tr_in;
+                const uint16_t* vp = vbuf + (kt * 32 + tr_row) * kAttD + col;
+                const abf16x8 v0 = tr_pair(vp, vp + 8 * kAttD);
+                const abf16x8 v1 = tr_pair(vp + 16 * kAttD, vp + 24 * kAttD);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, pb0, o[dt], 0, 0, 0);
+                o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, pb1, o[dt], 0, 0, 0);
             }
         }
     };
-    if (b0 < b1) {
-        issue_k(b0, sK0);
-        issue_v(b0);
-    }
-    // unrolled by two so that each step names its K buffers statically
+    if (b0 < b1) issue(b0, sK0, sV0);
+    // unrolled by two so that each step names its buffers statically
     for (int b = b0; b < b1; b += 2) {
-        step(b, sK0, sK1);
-        if (b + 1 < b1) step(b + 1, sK1, sK0);
+        step(b, sK0, sV0, sK1, sV1);
+        if (b + 1 < b1) step(b + 1, sK1, sV1, sK0, sV0);
     }
     if (!active) return;
     const float lt = lsum + __shfl_xor(lsum, 32);
@@ -291,8 +339,8 @@ __global__ __launch_bounds__(NW * 64, 3) void k_tree_attn(AttnArgs a) {
             for (int q4 = 0; q4 < 4; ++q4) {
                 const float e0 = o[dt][4 * q4], e1 = o[dt][4 * q4 + 1];
                 const float e2 = o[dt][4 * q4 + 2], e3 = o[dt][4 * q4 + 3];
-                const uint2 w = make_uint2(bf16_rne(e0 * inv) | (bf16_rne(e1 * inv) << 16),
-                                           bf16_rne(e2 * inv) | (bf16_rne(e3 * inv) << 16));
+                const uint2 w = make_uint2(pack_bf16x2(e0 * inv, e1 * inv),
+                                           pack_bf16x2(e2 * inv, e3 * inv));
                 *(uint2*)(op + 32 * dt + 8 * q4) = w;
             }
     } else {
@@ -328,14 +376,14 @@ __global__ __launch_bounds__(64) void k_tree_attn_combine(AttnArgs a) {
     for (int s = 0; s < a.S; ++s) {
         const float2 ml = a.pml[base + s * sstride];
         if (ml.x == -INFINITY) continue;
-        const float w = exp2f(ml.x - M);
+        const float w = ex2(ml.x - M);
         const float2 v = *(const float2*)(a.po + (base + s * sstride) * kAttD + 2 * threadIdx.x);
         l += w * ml.y;
         o0 += w * v.x;
         o1 += w * v.y;
     }
     const float inv = 1.0f / l;
-    *(uint32_t*)op = bf16_rne(o0 * inv) | (bf16_rne(o1 * inv) << 16);
+    *(uint32_t*)op = pack_bf16x2(o0 * inv, o1 * inv);
 }
 
 AttnPlan attn_plan(const dt_attn_params* p) {
@@ -386,10 +434,10 @@ hipError_t launch_tree_attention(const dt_attn_params* p, const AttnPlan& pl, co
     const long w = (long)a.units * a.S;
     const int grid = (int)(((w + 7) / 8) * 8 * a.QG);
     switch (pl.NW) {
-        case 4: k_tree_attn<4, 32><<<grid, 256, 0, st>>>(a); break;
-        case 5: k_tree_attn<5, 32><<<grid, 320, 0, st>>>(a); break;
-        case 6: k_tree_attn<6, 32><<<grid, 384, 0, st>>>(a); break;
-        case 7: k_tree_attn<7, 32><<<grid, 448, 0, st>>>(a); break;
+        case 4: k_tree_attn<4, kAttBlkSmall><<<grid, 256, 0, st>>>(a); break;
+        case 5: k_tree_attn<5, kAttBlkSmall><<<grid, 320, 0, st>>>(a); break;
+        case 6: k_tree_attn<6, kAttBlkSmall><<<grid, 384, 0, st>>>(a); break;
+        case 7: k_tree_attn<7, kAttBlkSmall><<<grid, 448, 0, st>>>(a); break;
         case 8: k_tree_attn<8, 64><<<grid, 512, 0, st>>>(a); break;
         default: k_tree_attn<9, 64><<<grid, 576, 0, st>>>(a); break;
     }

@@ -261,8 +261,8 @@ using namespace dt;
 
 extern "C" {
 
-const char* dt_status_string(dt_status s) {
-    switch (s) {
+const char* dt_status_string(int32_t code) {
+    switch (code) {
         case DT_OK: return "DT_OK";
         case DT_EINVAL: return "DT_EINVAL: invalid argument";
         case DT_ENOSPC: return "DT_ENOSPC: workspace too small";

@@ -257,7 +257,8 @@ dt_status tree_attention(const dt_attn_params* p, const void* Q, const void* K, 
                          const int32_t* ctx_len, const dt_tree* tree, void* O,
                          void* workspace, size_t ws_bytes, void* stream);
 
-const char* dt_status_string(dt_status s);
+/* Text for a status code; any integer is accepted (unknown codes give a fixed text). */
+const char* dt_status_string(int32_t code);
 
 /* Measurement support (host only, not thread-safe): when enabled, the library brackets each
  * launch of the fused Markov-bias/top-k kernel with HIP events on the caller's stream.

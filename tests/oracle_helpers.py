@@ -169,3 +169,25 @@ def exact_emitted_law(p, q, k):
             rej *= 1.0 - acc[j]
         law += w * rej * resid
     return law
+
+
+def chisq_binned(counts, probs, min_expected=5.0):
+    """Pearson chi-square of observed counts against probabilities, cells merged in order of
+    expected count until each merged cell expects at least `min_expected`; (stat, dof)."""
+    n = counts.sum()
+    exp = n * probs
+    order = np.argsort(exp)
+    obs_b, exp_b, acc_o, acc_e = [], [], 0.0, 0.0
+    for i in order:
+        acc_o += counts[i]
+        acc_e += exp[i]
+        if acc_e >= min_expected:
+            obs_b.append(acc_o)
+            exp_b.append(acc_e)
+            acc_o = acc_e = 0.0
+    if acc_e > 0 and exp_b:
+        obs_b[-1] += acc_o
+        exp_b[-1] += acc_e
+    obs_b, exp_b = np.array(obs_b), np.array(exp_b)
+    stat = ((obs_b - exp_b) ** 2 / exp_b).sum()
+    return stat, len(obs_b) - 1

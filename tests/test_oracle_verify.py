@@ -16,7 +16,7 @@ from scipy import stats
 from scipy.special import logsumexp, softmax
 
 import oracle
-from oracle_helpers import (exact_emitted_law, node_dist, plackett_luce, small_instance,
+from oracle_helpers import (chisq_binned, exact_emitted_law, node_dist, plackett_luce, small_instance,
                             tree_paths)
 
 
@@ -116,26 +116,6 @@ def test_exact_law_negative_controls_fail(fault):
 
 
 # ------------------------------------------------------------------ statistics -----------
-def _chisq(counts, probs, min_expected=5.0):
-    n = counts.sum()
-    exp = n * probs
-    order = np.argsort(exp)
-    obs_b, exp_b, acc_o, acc_e = [], [], 0.0, 0.0
-    for i in order:
-        acc_o += counts[i]
-        acc_e += exp[i]
-        if acc_e >= min_expected:
-            obs_b.append(acc_o)
-            exp_b.append(acc_e)
-            acc_o = acc_e = 0.0
-    if acc_e > 0 and exp_b:
-        obs_b[-1] += acc_o
-        exp_b[-1] += acc_e
-    obs_b, exp_b = np.array(obs_b), np.array(exp_b)
-    stat = ((obs_b - exp_b) ** 2 / exp_b).sum()
-    return stat, len(obs_b) - 1
-
-
 def _lossless_instance(T, seed=11, k=3):
     inst = small_instance(seed, V=16, r=4, B=2, k=k, Ncap=5, mode="sample", temperature=T,
                           cal="linear")
@@ -148,14 +128,14 @@ def _lossless_pvalue(inst, tab, T, n):
     first, second = oracle.sample_rounds(inst, tab, n, temperature=T)
     root = int(inst.root_token[0])
     p0 = softmax(tab[0, root].astype(np.float64) / T)
-    s1, d1 = _chisq(np.bincount(first, minlength=inst.V).astype(float), p0)
+    s1, d1 = chisq_binned(np.bincount(first, minlength=inst.V).astype(float), p0)
     stat, dof = s1, d1
     for x in range(inst.V):
         sel = second[(first == x) & (second >= 0)]
         if len(sel) < 200:
             continue
         px = softmax(tab[1, x].astype(np.float64) / T)
-        s, d = _chisq(np.bincount(sel, minlength=inst.V).astype(float), px)
+        s, d = chisq_binned(np.bincount(sel, minlength=inst.V).astype(float), px)
         stat += s
         dof += d
     return stats.chi2.sf(stat, dof), (second >= 0).mean()
@@ -203,7 +183,7 @@ def _depth_b_pvalue(inst, tab, T, n):
         if len(sel) < 200:
             continue
         px = softmax(tab[1, x].astype(np.float64) / T)
-        s, d = _chisq(np.bincount(sel, minlength=inst.V).astype(float), px)
+        s, d = chisq_binned(np.bincount(sel, minlength=inst.V).astype(float), px)
         stat += s
         dof += d
     return stats.chi2.sf(stat, dof), (second >= 0).mean(), dof
@@ -286,5 +266,5 @@ def test_gumbel_topk_matches_plackett_luce():
         counts[idx[tuple(int(x) for x in e["child_tok"])]] += 1
     probs = np.array([plackett_luce(q, p) for p in pairs])
     assert abs(probs.sum() - 1) < 1e-12
-    stat, dof = _chisq(counts, probs)
+    stat, dof = chisq_binned(counts, probs)
     assert stats.chi2.sf(stat, dof) > 1e-4

@@ -30,6 +30,8 @@ METRIC = "draft trees/sec & µs/round (B=16,k=4,N=64,V=151936); % HBM peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 KERNEL_SOURCES = ("draft_tree_construction_rank_amd/csrc/build_kernels.hip",
+                  "draft_tree_construction_rank_amd/csrc/dt_build_common.h",
+                  "draft_tree_construction_rank_amd/csrc/dt_internal.h",
                   "draft_tree_construction_rank_amd/csrc/dt_mma.h",
                   "draft_tree_construction_rank_amd/csrc/dt_device.h")
 COUNTERS = os.path.join(ROOT, "profiles", "k_build_counters.json")

@@ -22,6 +22,7 @@ _SRC = os.path.join(_HERE, "dtree_oracle.c")
 _LIB = os.path.join(_HERE, "libdtree_oracle.so")
 
 GREEDY, SAMPLE = 0, 1
+BUILD_HEAP, BUILD_LEVELSYNC, BUILD_FLASH = 0, 1, 2
 COND_PARENT, COND_CHAIN, COND_NONE = 0, 1, 2
 STREAM_GUMBEL, STREAM_ACCEPT, STREAM_RESID = 1, 2, 3
 STATUS_BAD_ROOT, STATUS_BUDGET_CLAMPED = 1, 2
@@ -84,6 +85,8 @@ def lib() -> C.CDLL:
                                 vp, vp, vp, vp]
         L.or_build.argtypes = [C.POINTER(Params), vp, vp, vp, vp, vp, vp, C.c_int32,
                                C.POINTER(_Tree), vp]
+        L.or_build_flash.argtypes = [C.POINTER(Params), vp, vp, vp, vp, vp, vp,
+                                     C.POINTER(_Tree), vp]
         L.or_verify_greedy.argtypes = [C.POINTER(Params), C.POINTER(_Tree), vp,
                                        C.POINTER(_Verify), vp]
         L.or_verify_sample.argtypes = [C.POINTER(Params), C.POINTER(_Tree), vp, vp, vp, vp, vp,
@@ -203,9 +206,10 @@ def build_tree(inst, *, requests=None, method: int = 0, n_budget=None, tau=None,
                margins: Optional[np.ndarray] = None, mode=None, temperature=None,
                round_=None) -> dict:
     """Build trees for the listed requests (default all).  ``method`` 0 = best-first
-    priority queue, 1 = level-synchronous.  Returns the tree dict (arrays over the listed
-    requests, in that order).  Each request is built by its own single-request call, keyed
-    by its true request id; the calls run on a thread pool."""
+    priority queue, 1 = level-synchronous, 2 = the two-stage M-ary tree (M = inst.k,
+    greedy; or_build_flash).  Returns the tree dict (arrays over the listed requests, in
+    that order).  Each request is built by its own single-request call, keyed by its true
+    request id; the calls run on a thread pool."""
     reqs = list(range(inst.R)) if requests is None else list(requests)
     R = len(reqs)
     nb = np.asarray(inst.n_budget if n_budget is None else np.broadcast_to(n_budget, inst.R),
@@ -226,8 +230,12 @@ def build_tree(inst, *, requests=None, method: int = 0, n_budget=None, tau=None,
         t = new_tree(1, inst.Ncap, inst.k)
         ts = _tree_struct(t)
         mg = new_margins(1)
-        rc = lib().or_build(C.byref(P), _p(L), _p(U), _p(Wt), _p(root), _p(budget), _p(thr),
-                            method, C.byref(ts), _p(mg))
+        if method == 2:
+            rc = lib().or_build_flash(C.byref(P), _p(L), _p(U), _p(Wt), _p(root), _p(budget),
+                                      _p(thr), C.byref(ts), _p(mg))
+        else:
+            rc = lib().or_build(C.byref(P), _p(L), _p(U), _p(Wt), _p(root), _p(budget),
+                                _p(thr), method, C.byref(ts), _p(mg))
         assert rc == 0
         return t, mg
 

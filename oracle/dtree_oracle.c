@@ -473,6 +473,195 @@ int or_build(const or_params* P, const float* L, const float* U, const float* Wt
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* Two-stage M-ary tree (TreeFlash explainer, technical summary, methodology: two-stage    */
+/* inference construction), carried onto this library's Markov head.                     */
+/* ------------------------------------------------------------------------------------ */
+/* Stage 1: for every block row j, S_j = the M tokens with the largest unconditioned block
+ * logits L[j] (ties: lower id); S_j is the only token set the tree uses at depth j + 1.
+ * Stage 2: the parent-conditioned law of every state (row j, token t) -- t = the root for
+ * j = 0, t in S_{j-1} for j >= 1 -- is evaluated over the whole vocabulary, z = L[j] +
+ * U[t] . W, lse = log sum exp z, and for each c in S_j: q(c) = exp(z_c - lse); the M
+ * siblings are ranked by (z desc, token asc).  Final selection: best-first top-N with
+ * per-round stopping (the same order, calibration and survival as the parent-conditioned
+ * tree) over the lattice in which a node of depth j with token t has the children S_j with
+ * the q of state (j, t).  M = P->k; greedy mode. */
+typedef struct {
+    int M, B;
+    int32_t* set;  /* [B][M] S_j, logit order */
+    int32_t* tok;  /* [B][M][M] state (j, slot) -> children in sibling order */
+    double* z;     /* [B][M][M] their conditional logits */
+    double* lse;   /* [B][M] */
+} flash_t;
+
+static int flash_slot(const flash_t* F, int j, int32_t t)
+{
+    if (j == 0) return 0;
+    for (int s = 0; s < F->M; ++s)
+        if (F->set[(size_t)(j - 1) * F->M + s] == t) return s;
+    return -1;
+}
+
+static void flash_stages(const or_params* P, const float* L_req, const float* U,
+                         const float* Wt, int32_t root, flash_t* F, double* ybuf,
+                         or_margin* mg)
+{
+    const int M = F->M, V = P->V;
+    /* stage 1: M passes of "largest logit, lower id on ties" per row */
+    unsigned char* taken = (unsigned char*)malloc((size_t)V);
+    for (int j = 0; j < F->B; ++j) {
+        const float* row = L_req + (size_t)j * (size_t)V;
+        memset(taken, 0, (size_t)V);
+        for (int s = 0; s < M; ++s) {
+            int best = -1;
+            for (int c = 0; c < V; ++c)
+                if (!taken[c] && (best < 0 || (double)row[c] > (double)row[best])) best = c;
+            taken[best] = 1;
+            F->set[(size_t)j * M + s] = best;
+        }
+    }
+    free(taken);
+    /* stage 2: every state's conditional law over V, gathered at S_j */
+    or_params Q = *P;
+    Q.k = 1;
+    Q.mode = OR_GREEDY;
+    for (int j = 0; j < F->B; ++j) {
+        const int nstate = j == 0 ? 1 : M;
+        for (int s = 0; s < nstate; ++s) {
+            const int32_t t = j == 0 ? root : F->set[(size_t)(j - 1) * M + s];
+            int32_t ct;
+            double cy, lse;
+            or_expand(&Q, L_req, U, Wt, j, t, 0, ybuf, &lse, &ct, &cy);
+            const size_t st = (size_t)j * M + s;
+            F->lse[st] = lse;
+            int32_t* tk = F->tok + st * M;
+            double* zz = F->z + st * M;
+            for (int i = 0; i < M; ++i) {
+                tk[i] = F->set[(size_t)j * M + i];
+                zz[i] = ybuf[tk[i]];
+            }
+            for (int i = 1; i < M; ++i) { /* insertion sort: z desc, token asc */
+                int32_t xt = tk[i];
+                double xz = zz[i];
+                int a = i - 1;
+                while (a >= 0 && (zz[a] < xz || (zz[a] == xz && tk[a] > xt))) {
+                    tk[a + 1] = tk[a];
+                    zz[a + 1] = zz[a];
+                    --a;
+                }
+                tk[a + 1] = xt;
+                zz[a + 1] = xz;
+            }
+            if (mg)
+                for (int i = 1; i < M; ++i) upd_min(&mg->key_gap, zz[i - 1] - zz[i]);
+        }
+    }
+}
+
+static void expand_flash(const or_params* P, const flash_t* F, store_t* st, int idx,
+                         or_margin* mg)
+{
+    const int M = F->M;
+    node_t par = st->v[idx];
+    const int j = par.depth;
+    const size_t sti = (size_t)j * M + flash_slot(F, j, par.token);
+    int first = -1;
+    for (int i = 0; i < M; ++i) {
+        const double lq = F->z[sti * M + i] - F->lse[sti];
+        const double q = exp(lq);
+        if (mg) upd_min(&mg->q_edge, q_edge_distance(q));
+        node_t ch;
+        ch.token = F->tok[sti * M + i];
+        ch.depth = j + 1;
+        ch.parent = idx;
+        ch.rank = i;
+        ch.child0 = -1;
+        ch.s = par.s * P->cal[cal_bin(q)]; /* float x float, rounded to float */
+        ch.logq = (float)lq;
+        ch.hash = or_child_hash(par.hash, ch.token);
+        int id = store_add(st, ch);
+        if (i == 0) first = id;
+    }
+    st->v[idx].child0 = first;
+}
+
+int or_build_flash(const or_params* P, const float* L, const float* U, const float* Wt,
+                   const int32_t* root_token, const int32_t* n_budget, const float* tau,
+                   or_tree* out, or_margin* margins)
+{
+    if (P->k < 1 || P->k > 8 || P->k > P->V || P->B < 1 || P->B > 32 || P->Ncap < 1 ||
+        P->Ncap > 64 || P->mode != OR_GREEDY)
+        return -1;
+    const int M = P->k, B = P->B;
+    double* ybuf = (double*)malloc(sizeof(double) * (size_t)P->V);
+    int* sel = (int*)malloc(sizeof(int) * 128);
+    flash_t F;
+    F.M = M;
+    F.B = B;
+    F.set = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * M);
+    F.tok = (int32_t*)malloc(sizeof(int32_t) * (size_t)B * M * M);
+    F.z = (double*)malloc(sizeof(double) * (size_t)B * M * M);
+    F.lse = (double*)malloc(sizeof(double) * (size_t)B * M);
+    for (int req = 0; req < P->R; ++req) {
+        const float* L_req = L + (size_t)req * (size_t)B * (size_t)P->V;
+        or_margin* mg = margins ? &margins[req] : NULL;
+        int status = 0, nsel = 0, nexp = 0;
+        int nb = n_budget[req];
+        if (nb < 0 || nb > P->Ncap) {
+            status |= OR_STATUS_BUDGET_CLAMPED;
+            nb = nb < 0 ? 0 : P->Ncap;
+        }
+        store_t st = {0};
+        if (root_token[req] < 0 || root_token[req] >= P->V) {
+            status |= OR_STATUS_BAD_ROOT;
+        } else {
+            flash_stages(P, L_req, U, Wt, root_token[req], &F, ybuf, mg);
+            node_t root;
+            root.token = root_token[req];
+            root.depth = 0;
+            root.parent = -1;
+            root.rank = 0;
+            root.child0 = -1;
+            root.s = 1.0f;
+            root.logq = 0.0f;
+            root.hash = or_root_hash(P->round, P->req_base + req, root_token[req]);
+            store_add(&st, root);
+            /* best-first with a priority queue, as build_heap, over the lattice */
+            int npend = 0;
+            int* pend = (int*)malloc(sizeof(int) * (size_t)(M * (nb + 1) + 1));
+            expand_flash(P, &F, &st, 0, mg);
+            nexp = 1;
+            for (int i = 0; i < M; ++i) pend[npend++] = st.v[0].child0 + i;
+            while (nsel < nb && npend > 0) {
+                int bi = 0;
+                for (int i = 1; i < npend; ++i)
+                    if (key_better(&st, pend[i], pend[bi])) bi = i;
+                int best = pend[bi];
+                pend[bi] = pend[--npend];
+                if (st.v[best].s < tau[req]) break;
+                sel[nsel++] = best;
+                if (st.v[best].depth < B) {
+                    expand_flash(P, &F, &st, best, mg);
+                    ++nexp;
+                    for (int i = 0; i < M; ++i) pend[npend++] = st.v[best].child0 + i;
+                }
+            }
+            free(pend);
+        }
+        emit_tree(P, &st, sel, nsel, req, out);
+        out->status[req] = status;
+        out->n_expand[req] = nexp;
+        free(st.v);
+    }
+    free(F.set);
+    free(F.tok);
+    free(F.z);
+    free(F.lse);
+    free(ybuf);
+    free(sel);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* Verification.                                                                           */
 /* ------------------------------------------------------------------------------------ */
 static int find_child(const or_tree* T, const or_params* P, int req, int parent, int32_t tok)

@@ -98,6 +98,13 @@ int or_build(const or_params* P, const float* L, const float* U, const float* Wt
              const int32_t* root_token, const int32_t* n_budget, const float* tau,
              int32_t method, or_tree* out, or_margin* margins /* [R] or NULL */);
 
+/* Two-stage M-ary tree (M = P->k; greedy mode): per block row the M largest unconditioned
+ * logits form the depth's token set; every (row, token) state's parent-conditioned law is
+ * evaluated; best-first top-N over the resulting lattice.  Same outputs as or_build. */
+int or_build_flash(const or_params* P, const float* L, const float* U, const float* Wt,
+                   const int32_t* root_token, const int32_t* n_budget, const float* tau,
+                   or_tree* out, or_margin* margins /* [R] or NULL */);
+
 /* Greedy accept-walk; target is [R][Ncap+1][V]. */
 int or_verify_greedy(const or_params* P, const or_tree* tree, const float* target,
                      or_verify* out, or_margin* margins);

@@ -540,6 +540,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--attention-only", nargs="*", metavar="WORKLOAD", default=None,
+                    help="time only tree_attention on the named workloads (all if none given) "
+                         "and print their JSON; for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requests shard "
@@ -561,6 +564,13 @@ def main():
         y.copy_(x)
         torch.cuda.synchronize()
         del x, y
+
+    if args.attention_only is not None:
+        global ATTN_WORKLOADS
+        names = args.attention_only or list(ATTN_WORKLOADS)
+        ATTN_WORKLOADS = {k: v for k, v in ATTN_WORKLOADS.items() if k in names}
+        print(json.dumps(attention_profile(torch, B, Flusher(torch))), flush=True)
+        return
 
     inst = inputs.make_instance("batched", tau=args.tau)
     res = run_workload(inst, args.tau, args.steps, args.warmup, torch, rt, B)

@@ -23,7 +23,8 @@ DT_REQ_BAD_ROOT, DT_REQ_BUDGET_CLAMPED = 1, 2
 
 EXPORTED = ("dt_build_workspace_bytes", "tree_build", "tree_build_noalloc", "tree_verify_greedy",
             "tree_verify_sample", "dt_load_policy", "dt_status_string", "dt_timing_enable",
-            "dt_timing_read", "dt_attn_workspace_bytes", "tree_attention")
+            "dt_timing_read", "dt_attn_workspace_bytes", "tree_attention",
+            "dt_flash_workspace_bytes", "tree_build_flash")
 NOALLOC_SCRATCH_BYTES = 32 << 20  # DT_NOALLOC_SCRATCH_BYTES of include/dtree.h
 
 
@@ -89,6 +90,11 @@ def lib() -> C.CDLL:
         L.tree_verify_sample.restype = C.c_int
         L.dt_load_policy.argtypes = [C.POINTER(dt_policy), C.c_float, C.c_int32, vp, vp]
         L.dt_load_policy.restype = C.c_int
+        L.dt_flash_workspace_bytes.argtypes = [P, C.POINTER(C.c_size_t)]
+        L.dt_flash_workspace_bytes.restype = C.c_int
+        L.tree_build_flash.argtypes = [P, vp, vp, vp, vp, vp, vp, C.POINTER(dt_tree), vp,
+                                       C.c_size_t, vp]
+        L.tree_build_flash.restype = C.c_int
         A = C.POINTER(dt_attn_params)
         L.dt_attn_workspace_bytes.argtypes = [A, C.POINTER(C.c_size_t)]
         L.dt_attn_workspace_bytes.restype = C.c_int
@@ -225,6 +231,26 @@ def tree_verify_sample(p: dt_params, tree: dict, block_logits: torch.Tensor, U: 
                                   _ptr(workspace), workspace.numel(), _stream(stream))
     if rc != DT_OK:
         raise DtError("tree_verify_sample", rc)
+
+
+def dt_flash_workspace_bytes(p: dt_params) -> int:
+    n = C.c_size_t(0)
+    rc = lib().dt_flash_workspace_bytes(C.byref(p), C.byref(n))
+    if rc != DT_OK:
+        raise DtError("dt_flash_workspace_bytes", rc)
+    return int(n.value)
+
+
+def tree_build_flash(p: dt_params, block_logits: torch.Tensor, U: torch.Tensor, Wt: torch.Tensor,
+                     root_token: torch.Tensor, n_budget: torch.Tensor, tau: torch.Tensor,
+                     out: dict, workspace: torch.Tensor, stream=None) -> None:
+    """The two-stage M-ary tree (M = p.k); outputs into a tree from alloc_tree(p)."""
+    ts = _tree_struct(out)
+    rc = lib().tree_build_flash(C.byref(p), _ptr(block_logits), _ptr(U), _ptr(Wt),
+                                _ptr(root_token), _ptr(n_budget), _ptr(tau), C.byref(ts),
+                                _ptr(workspace), workspace.numel(), _stream(stream))
+    if rc != DT_OK:
+        raise DtError("tree_build_flash", rc)
 
 
 def make_attn_params(*, R: int, Hq: int, Hkv: int, D: int, Ncap: int, Cmax: int,

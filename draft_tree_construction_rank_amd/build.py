@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdtree.so")
 SOURCES = ["abi.hip", "build_kernels.hip", "build_resident.hip", "verify_kernels.hip",
-           "attn_kernels.hip"]
+           "attn_kernels.hip", "flash_kernels.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          # no packed fp32 instructions anywhere in the device code

@@ -373,6 +373,41 @@ dt_status tree_attention(const dt_attn_params* p, const void* Q, const void* K, 
     return DT_OK;
 }
 
+static dt_status validate_flash(const dt_params* p) {
+    const dt_status v = validate(p);
+    if (v != DT_OK) return v;
+    if (p->mode != DT_GREEDY || p->cond != DT_COND_PARENT) return DT_EINVAL;
+    return DT_OK;
+}
+
+dt_status dt_flash_workspace_bytes(const dt_params* p, size_t* bytes) {
+    const dt_status v = validate_flash(p);
+    if (v != DT_OK) return v;
+    if (!bytes) return DT_EINVAL;
+    *bytes = flash_plan(p).total;
+    return DT_OK;
+}
+
+dt_status tree_build_flash(const dt_params* p, const void* block_logits, const void* U,
+                           const void* Wt, const int32_t* root_token, const int32_t* n_budget,
+                           const float* tau, const dt_tree* out, void* workspace,
+                           size_t ws_bytes, void* stream) {
+    const dt_status v = validate_flash(p);
+    if (v != DT_OK) return v;
+    if (!block_logits || !U || !Wt || !root_token || !n_budget || !tau || !tree_ptrs_ok(out) ||
+        !workspace)
+        return DT_EINVAL;
+    if (((uintptr_t)block_logits & 15) || ((uintptr_t)U & 15) || ((uintptr_t)Wt & 15) ||
+        ((uintptr_t)workspace & 255))
+        return DT_EINVAL;
+    const FlashPlan pl = flash_plan(p);
+    if (ws_bytes < pl.total) return DT_ENOSPC;
+    if (launch_build_flash(p, pl, block_logits, U, Wt, root_token, n_budget, tau, out,
+                           (char*)workspace, (hipStream_t)stream) != hipSuccess)
+        return DT_EDEVICE;
+    return DT_OK;
+}
+
 dt_status dt_load_policy(const dt_policy* pol, float load, int32_t R, float* tau,
                          int32_t* n_budget) {
     if (!pol || !tau || !n_budget || R < 1) return DT_EINVAL;

@@ -207,4 +207,17 @@ hipError_t launch_tree_attention(const dt_attn_params* p, const AttnPlan& pl, co
                                  const int32_t* n_nodes, const uint64_t* anc, void* O,
                                  char* ws, hipStream_t st);
 
+// Two-stage M-ary tree (flash_kernels.hip): M = k tokens per depth, NS = 1 + M (B - 1)
+// states a request, T tiles of 64 states, SP vocabulary splits; the workspace holds the
+// token sets, then the per-(state, split) log-sum-exp records.
+struct FlashPlan {
+    int M, NS, T, SP;
+    size_t sets_bytes, total;
+};
+FlashPlan flash_plan(const dt_params* p);
+hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const void* L,
+                              const void* U, const void* Wt, const int32_t* root_token,
+                              const int32_t* n_budget, const float* tau, const dt_tree* out,
+                              char* ws, hipStream_t st);
+
 }  // namespace dt

@@ -216,6 +216,25 @@ dt_status dt_load_policy(const dt_policy* pol, float load, int32_t R, float* tau
                          int32_t* n_budget);
 
 /* Human-readable name of a status code (static string). */
+/* ---- Two-stage M-ary tree ------------------------------------------------------------------
+ * The TreeFlash construction (TreeFlash explainer, technical summary, methodology: two-stage
+ * inference construction) on this library's Markov head, M = p->k.  Stage 1: for every block
+ * row j, the M tokens with the largest unconditioned block logits (ties: lower id) are the
+ * only tokens of the tree at depth j + 1.  Stage 2: the parent-conditioned law of every state
+ * (row j, token t) -- t = root_token for j = 0, t in stage 1's set of row j - 1 otherwise --
+ * is evaluated over the whole vocabulary, z = L[j] + U[t] . W, q(c) = softmax(z)_c for the M
+ * tokens c of row j's set; the 1 + M (B - 1) states are independent, so this is one parallel
+ * pass.  Final selection: the best-first top-N with per-round stopping of tree_build (same
+ * calibration, survival, global order and canonical emission) over the lattice in which a node
+ * of depth j with token t has as children row j's set, ranked by their conditional logits.
+ * Greedy mode and DT_COND_PARENT only (DT_EINVAL otherwise).  Outputs as tree_build; cand rows
+ * hold the M ranked children; level_rows is not written. */
+dt_status dt_flash_workspace_bytes(const dt_params* p, size_t* bytes);
+dt_status tree_build_flash(const dt_params* p, const void* block_logits, const void* U,
+                           const void* Wt, const int32_t* root_token, const int32_t* n_budget,
+                           const float* tau, const dt_tree* out, void* workspace,
+                           size_t ws_bytes, void* stream);
+
 /* ---- Tree attention: the verify forward's attention over a round's trees -------------
  * One attention layer of the target model that scores every tree position in one pass
  * (PCTree summary, introduction: the target checks all nodes of the tree in one forward;

@@ -88,20 +88,21 @@ def stored_subseeds(key: str):
 
 
 def certified(inst: inputs.Instance, requests=None, max_tries: int = 60, verify_target=None,
-              margin=None, key: str = None):
+              margin=None, key: str = None, method: int = 0):
     """Return (instance, oracle tree over `requests`) with every listed request certified.
 
     Requests that miss the margin get a new block-logits sub-seed (only those are rebuilt);
     the instance returned carries the sub-seeds used.  `verify_target`, if given, is a
     callable (inst, tree) -> margins of the verify step over tree["requests"], folded into
     the certification.  With `key`, the sub-seeds stored for that case are applied first;
-    every margin is still measured, and requests that miss it are re-drawn as usual."""
+    every margin is still measured, and requests that miss it are re-drawn as usual.
+    `method` selects the oracle's builder (oracle.BUILD_FLASH: the two-stage M-ary tree)."""
     if key is not None:
         sub = stored_subseeds(key)
         if sub is not None and len(sub) == inst.R:
             inst = redraw(inst, np.asarray(sub, np.int64))
     reqs = list(range(inst.R)) if requests is None else list(requests)
-    tree = oracle.build_tree(inst, requests=reqs)
+    tree = oracle.build_tree(inst, requests=reqs, method=method)
     margins = tree["margins"].copy()
     if verify_target is not None:
         _fold_verify(margins, verify_target(inst, tree))
@@ -113,7 +114,7 @@ def certified(inst: inputs.Instance, requests=None, max_tries: int = 60, verify_
         for i in bad:
             sub[reqs[i]] += 1000 * (attempt + 1)
         inst = redraw(inst, sub)
-        part = oracle.build_tree(inst, requests=[reqs[i] for i in bad])
+        part = oracle.build_tree(inst, requests=[reqs[i] for i in bad], method=method)
         for f, v in tree.items():
             if f != "requests":
                 v[bad] = part[f]

@@ -307,6 +307,55 @@ def mechanism_isolation(torch, rt, inputs, rho=0.8):
                      "sem": round(float(acc.std(ddof=1) / np.sqrt(len(acc))), 3),
                      "tree_build_us_median": _stats(us)["median"]}
         del tgt
+    # the two-stage M-ary tree (M = k = 4) on the same inputs and target
+    rnd = rt.Round(inst)
+    nb = torch.full((inst.R,), rnd.p.Ncap, dtype=torch.int32, device="cuda")
+    fws = torch.empty(Bd.dt_flash_workspace_bytes(rnd.p), dtype=torch.uint8, device="cuda")
+    fcall = lambda: Bd.tree_build_flash(rnd.p, d.L, d.U, d.Wt, d.root_token, nb, d.tau, rnd.tree, fws)
+    fcall()
+    torch.cuda.synchronize()
+    tgt = markov_target(torch, inst, d, rnd.tree, rho)
+    rnd.verify_greedy(tgt)
+    torch.cuda.synchronize()
+    acc = rnd.vout["accept_len"].float().cpu().numpy()
+    us = time_calls(torch, [fcall], 10)[0]
+    out["treeflash_m4"] = {"mean_accept_len": round(float(acc.mean()), 3),
+                           "sem": round(float(acc.std(ddof=1) / np.sqrt(len(acc))), 3),
+                           "tree_build_us_median": _stats(us)["median"]}
+    return out
+
+
+def flash_profile(torch, rt, inputs, flusher, steps=30):
+    """tree_build_flash (M = 4, tau = 0) on the b7, b16 and batched workloads: warm and cold
+    µs per call; per call the MFMA flops of the state pass (R * (1 + M (B - 1)) states of
+    2 r V each) and its algorithmic bytes (every block row once, W once, the states' U rows)."""
+    from draft_tree_construction_rank_amd import binding as Bd
+    out = {}
+    for name in ("b7", "b16", "batched"):
+        inst = inputs.make_instance(name, tau=0.0)
+        d = rt.to_device(inst, "cuda", tau=0.0)
+        p = rt.params_for(inst)
+        tree = Bd.alloc_tree(p, "cuda")
+        ws = torch.empty(Bd.dt_flash_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        call = lambda: Bd.tree_build_flash(p, d.L, d.U, d.Wt, d.root_token, d.n_budget, d.tau, tree, ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        warm = _stats(time_calls(torch, [call], steps)[0])
+        cold = _stats(time_calls(torch, [call], max(10, steps // 3), flusher)[0])
+        ns = inst.R * (1 + inst.k * (inst.B - 1))
+        flops = 2.0 * ns * inst.r * inst.V
+        byts = float(inst.R * inst.B * inst.V * 2 + inst.r * inst.V * 2 + ns * inst.r * 2)
+        t = warm["median"] * 1e-6
+        out[name] = {"R": inst.R, "B": inst.B, "M": inst.k, "N": inst.Ncap, "states": ns,
+                     "build_us_warm": warm, "build_us_cold": cold,
+                     "trees_per_s": round(inst.R / t, 1),
+                     "mean_nodes": float(tree["n_nodes"].float().mean().item()),
+                     "mfma_tflops": round(flops / t / 1e12, 1),
+                     "mfma_frac": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "alg_gbs": round(byts / t / 1e9, 1),
+                     "hbm_frac": round(byts / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del d, tree, ws
     return out
 
 
@@ -644,6 +693,7 @@ def main():
         extras["mechanism_isolation_markov_target"] = mechanism_isolation(torch, rt, inputs)
         extras["multi_round_load_sweep"] = load_sweep(torch, rt, inputs)
         extras["tree_attention"] = attention_profile(torch, B, flusher)
+        extras["tree_build_flash"] = flash_profile(torch, rt, inputs, flusher)
         if not args.no_cpu_baseline:
             extras["tree_attention"]["oracle"] = attention_oracle_rate()
         extras["targets"] = {

@@ -209,10 +209,11 @@ hipError_t launch_tree_attention(const dt_attn_params* p, const AttnPlan& pl, co
 
 // Two-stage M-ary tree (flash_kernels.hip): M = k tokens per depth, NS = 1 + M (B - 1)
 // states a request, T tiles of 64 states, SP vocabulary splits; the workspace holds the
-// token sets, then the per-(state, split) log-sum-exp records.
+// token sets, the per-(state, split) log-sum-exp records, every state's children's
+// conditional logits, then stage 1's part lists (P parts a block row).
 struct FlashPlan {
-    int M, NS, T, SP;
-    size_t sets_bytes, total;
+    int M, NS, T, SP, P;
+    size_t sets_bytes, zc_off, setp_off, total;
 };
 FlashPlan flash_plan(const dt_params* p);
 hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const void* L,

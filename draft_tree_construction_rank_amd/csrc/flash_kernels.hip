@@ -24,7 +24,7 @@
 
 namespace dt {
 
-constexpr int kFlashSetThreads = 1024;
+constexpr int kFlashSetThreads = 256;
 constexpr int kFlashSelThreads = 256;
 constexpr int kFlashMaxStates = 1 + (kMaxB - 1) * kMaxK;  // 249
 constexpr int kFlashPool = kMaxNcap + kMaxNcap * kMaxK;   // kept + one level's children
@@ -38,8 +38,10 @@ struct FlashArgs {
     const float* tau;
     int32_t* sets;  // [R][B][M]
     float2* lsep;   // [R * NS][SP] (max, sum) in log2 units
+    float* zc;      // [R * NS][M] conditional logits of every state's children (set order)
+    uint64_t* setp; // [R * B][P][8] stage-1 part lists
     dt_tree out;
-    int R, B, M, V, r, Ncap, NS, SP, T;
+    int R, B, M, V, r, Ncap, NS, SP, T, P;
     int logits_bf16;
     float cal[16];
 };
@@ -61,26 +63,47 @@ __device__ __forceinline__ void flash_state(const FlashArgs& a, int req, int s, 
 }
 
 // ---- stage 1: top-M of every block row ----------------------------------------------------
+// Each row is scanned by P workgroups (P parts of its columns); each part's ranked list of
+// 8 packed (logit, token) entries goes to the workspace and a second kernel merges a row's P
+// lists.  An entry enters a thread's list only if it beats the list's last entry (one
+// compare for almost every element once the list is warm).
+__device__ __forceinline__ void flash_offer(TopK<kMaxK>& top, float v, int c) {
+    const uint64_t e = pack_entry(v, c);
+    if (e > top.k[kMaxK - 1]) top.push(e, 0.0f);
+}
+
 __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
     __shared__ uint64_t sk[kFlashSetThreads / 64][kMaxK];
-    const int row = blockIdx.x;  // req * B + j
+    const int row = blockIdx.x / a.P, part = blockIdx.x % a.P;  // row = req * B + j
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t base = (size_t)row * a.V;
     TopK<kMaxK> top;
     top.init();
     if (a.logits_bf16 && (a.V & 7) == 0) {
         const uint4* p = (const uint4*)((const uint16_t*)a.L + base);
-        for (int g = tid; g < a.V / 8; g += kFlashSetThreads) {
-            const uint4 w = p[g];
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        const int ng = a.V / 8;
+        const int g_beg = (int)((long)part * ng / a.P), g_end = (int)((long)(part + 1) * ng / a.P);
+        for (int g0 = g_beg + tid; g0 < g_end; g0 += 2 * kFlashSetThreads) {
+            const int g1 = g0 + kFlashSetThreads;
+            const uint4 w0 = p[g0], w1 = p[g1 < g_end ? g1 : g0];
+            const uint32_t x0[4] = {w0.x, w0.y, w0.z, w0.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                top.push(pack_entry(bf16_lo(ww[i]), 8 * g + 2 * i), 0.0f);
-                top.push(pack_entry(bf16_hi(ww[i]), 8 * g + 2 * i + 1), 0.0f);
+                flash_offer(top, bf16_lo(x0[i]), 8 * g0 + 2 * i);
+                flash_offer(top, bf16_hi(x0[i]), 8 * g0 + 2 * i + 1);
+            }
+            if (g1 < g_end) {
+                const uint32_t x1[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    flash_offer(top, bf16_lo(x1[i]), 8 * g1 + 2 * i);
+                    flash_offer(top, bf16_hi(x1[i]), 8 * g1 + 2 * i + 1);
+                }
             }
         }
     } else {
-        for (int c = tid; c < a.V; c += kFlashSetThreads) top.push(pack_entry(flash_logit(a, base + c), c), 0.0f);
+        const int c_beg = (int)((long)part * a.V / a.P), c_end = (int)((long)(part + 1) * a.V / a.P);
+        for (int c = c_beg + tid; c < c_end; c += kFlashSetThreads) flash_offer(top, flash_logit(a, base + c), c);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) top.merge_xor(off);
@@ -96,9 +119,29 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
             for (int i = 0; i < kMaxK; ++i) t.k[i] = sk[lane][i];
 #pragma unroll
         for (int off = 1; off < kFlashSetThreads / 64; off <<= 1) t.merge_xor(off);
-        if (lane == 0)
-            for (int i = 0; i < a.M; ++i) a.sets[(size_t)row * a.M + i] = entry_tok(t.k[i]);
+        if (lane < kMaxK) {
+            uint64_t v = 0;
+#pragma unroll
+            for (int i = 0; i < kMaxK; ++i) v = lane == i ? t.k[i] : v;
+            a.setp[((size_t)row * a.P + part) * kMaxK + lane] = v;
+        }
     }
+}
+
+// One wavefront per row merges the row's P part lists into its set S_j (M tokens).
+__global__ __launch_bounds__(64) void k_flash_sets_merge(FlashArgs a) {
+    const int row = blockIdx.x, lane = threadIdx.x;
+    TopK<kMaxK> t;
+    t.init();
+    if (lane < a.P)
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i) t.k[i] = a.setp[((size_t)row * a.P + lane) * kMaxK + i];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) t.merge_xor(off);
+    if (lane == 0)
+#pragma unroll
+        for (int i = 0; i < kMaxK; ++i)
+            if (i < a.M) a.sets[(size_t)row * a.M + i] = entry_tok(t.k[i]);
 }
 
 // ---- stage 2: log-sum-exp of every state over vocabulary splits ---------------------------
@@ -111,6 +154,7 @@ __global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
     __shared__ __align__(16) float sZ[kTileRows * kZStride];
     __shared__ int sTok[kTileRows];
     __shared__ size_t sLb[kTileRows];
+    __shared__ int sTgt[kTileRows][kMaxK];
     const int b = blockIdx.x;
     const int idx = b >> 3;
     const int tile = idx % a.T;
@@ -128,6 +172,7 @@ __global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
             int j;
             flash_state(a, req, g % a.NS, &j, &t);
             lb = ((size_t)req * a.B + j) * a.V;
+            for (int i = 0; i < a.M; ++i) sTgt[tid][i] = a.sets[((size_t)req * a.B + j) * a.M + i];
         }
         sTok[tid] = t;
         sLb[tid] = lb;
@@ -148,6 +193,14 @@ __global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
         const int col0 = ch * kChunkCols;
         mma_chunk<HEAD_BF16>(a.Wt, a.V, a.r, col0, nrows > 32, sA, sAf, sZ);
         if (live) {
+            // the state's children that fall in this thread's 32 columns: their conditional
+            // logits, the same fp32 values that enter the log-sum-exp
+            const int cb = col0 + 32 * q;
+            for (int i = 0; i < a.M; ++i) {
+                const int off = sTgt[row][i] - cb;
+                if (off >= 0 && off < 32)
+                    a.zc[(size_t)(g0 + row) * a.M + i] = sZ[row * kZStride + 32 * q + off] + flash_logit(a, lb + cb + off);
+            }
             float m = -INFINITY;
             float zv[32];
 #pragma unroll
@@ -201,7 +254,6 @@ struct FlashSel {
 // rule (survival from the calibration table, s < tau dropped, global order survival desc,
 // depth asc, sibling-rank path asc, budget N) applied level by level; because survival
 // never increases along a path this equals best-first over the lattice.
-template <bool HEAD_BF16>
 __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) {
     __shared__ FlashSel sm;
     const int req = blockIdx.x, tid = threadIdx.x;
@@ -221,43 +273,31 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
     if (tid == 0) sm.nkept = 0;
     __syncthreads();
     if (!bad_root) {
-        // log-sum-exp of every state: its splits' records combined
-        for (int s = tid; s < NS; s += kFlashSelThreads) {
-            const float2* rec = a.lsep + (size_t)(req * NS + s) * a.SP;
+        // log-sum-exp of every state: its splits' records combined, P threads a state
+        const int P = NS <= kFlashSelThreads / 4 ? 4 : 1;
+        for (int w = tid; w < ((NS * P + kFlashSelThreads - 1) / kFlashSelThreads) * kFlashSelThreads; w += kFlashSelThreads) {
+            const int s = w / P, part = w % P;
             Lse2 st;
             st.init();
-            for (int p = 0; p < a.SP; p += 8) {
-                float2 v[8];
+            if (s < NS) {
+                const float2* rec = a.lsep + (size_t)(req * NS + s) * a.SP;
+                for (int p = part * 16; p < a.SP; p += 16 * P) {
+                    float2 v[16];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = p + u < a.SP ? rec[p + u] : make_float2(-INFINITY, 0.0f);
+                    for (int u = 0; u < 16; ++u) v[u] = p + u < a.SP ? rec[p + u] : make_float2(-INFINITY, 0.0f);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) st.merge(v[u].x, v[u].y);
-            }
-            sm.lse2[s] = st.m + log2f(st.s);
-        }
-        // conditional logits of every state's children (the tokens of S_j): block logit plus
-        // the head's dot product, in log2 units
-        for (int w = tid; w < NS * M; w += kFlashSelThreads) {
-            const int s = w / M, i = w % M;
-            int j, t;
-            flash_state(a, req, s, &j, &t);
-            const int c = sm.set[j][i];
-            float acc = 0.0f;
-            if constexpr (HEAD_BF16) {
-                const uint32_t* u = (const uint32_t*)((const uint16_t*)a.U + (size_t)t * a.r);
-                const uint32_t* wv = (const uint32_t*)((const uint16_t*)a.Wt + (size_t)c * a.r);
-                for (int e = 0; e < a.r / 2; ++e) {
-                    const uint32_t x = u[e], y = wv[e];
-                    acc = fmaf(bf16_lo(x), bf16_lo(y), acc);
-                    acc = fmaf(bf16_hi(x), bf16_hi(y), acc);
+                    for (int u = 0; u < 16; ++u) st.merge(v[u].x, v[u].y);
                 }
-            } else {
-                const float* u = (const float*)a.U + (size_t)t * a.r;
-                const float* wv = (const float*)a.Wt + (size_t)c * a.r;
-                for (int e = 0; e < a.r; ++e) acc = fmaf(u[e], wv[e], acc);
             }
-            sm.cy2[s][i] = (flash_logit(a, ((size_t)req * B + j) * a.V + c) + acc) * kLog2e;
+            if (P == 4) {
+                st.merge_xor(1);
+                st.merge_xor(2);
+            }
+            if (s < NS && part == 0) sm.lse2[s] = st.m + log2f(st.s);
         }
+        // conditional logits of every state's children (written by the state pass)
+        for (int w = tid; w < NS * M; w += kFlashSelThreads)
+            sm.cy2[w / M][w % M] = a.zc[(size_t)(req * NS) * M + w] * kLog2e;
         __syncthreads();
         // sibling order of every state: conditional logit desc, token asc
         for (int s = tid; s < NS; s += kFlashSelThreads) {
@@ -295,7 +335,8 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
                     sm.front[0] = -1;
                 }
             } else {
-                if (tid < sm.nkept && low_depth((uint32_t)sm.kkey[tid]) == d - 1) {
+                const bool fr = tid < sm.nkept && low_depth((uint32_t)sm.kkey[tid]) == d - 1;
+                if (fr) {
                     const uint32_t lo = (uint32_t)sm.kkey[tid];
                     int fi = 0;
                     for (int e = 0; e < sm.nkept; ++e) {
@@ -305,12 +346,10 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
                     sm.kfi[tid] = (int16_t)fi;
                     sm.front[fi] = (int16_t)tid;
                 }
-                if (tid == 0) {
-                    int nf = 0;
-                    for (int e = 0; e < sm.nkept; ++e) nf += low_depth((uint32_t)sm.kkey[e]) == d - 1;
-                    sm.nfront = nf;
-                }
+                const int nf = __syncthreads_count(fr);
+                if (tid == 0) sm.nfront = nf;
             }
+            if (tid == 0) sm.nvalid = 0;
             __syncthreads();
             const int nf = sm.nfront, nk = sm.nkept;
             if (nf == 0) break;
@@ -342,9 +381,11 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
             __syncthreads();
             // keep the nb best: rank = number of larger keys (valid keys are distinct)
             const int np = nk + nf * M;
+            int nv = 0;
             for (int e = tid; e < np; e += kFlashSelThreads) {
                 const uint64_t ke = sm.pkey[e];
                 if (ke == 0) continue;
+                ++nv;
                 int rank = 0;
                 for (int f = 0; f < np; ++f) rank += sm.pkey[f] > ke;
                 if (rank < nb) {
@@ -355,11 +396,9 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
                     sm.klogq[rank] = sm.plogq[e];
                 }
             }
-            if (tid == 0) {
-                int nv = 0;
-                for (int e = 0; e < np; ++e) nv += sm.pkey[e] != 0;
-                sm.nkept = min(nb, nv);
-            }
+            if (nv) atomicAdd(&sm.nvalid, nv);
+            __syncthreads();
+            if (tid == 0) sm.nkept = min(nb, sm.nvalid);
             __syncthreads();
         }
     }
@@ -389,13 +428,11 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
         sm.cpar[pos] = (int16_t)par;
     }
     __syncthreads();
-    if (tid == 0) {
+    // ancestor mask: the node's own bit and its ancestors' (each node walks its own path)
+    if (tid < n) {
         uint64_t m = 0;
-        for (int i = 0; i < n; ++i) {
-            const int p = sm.cpar[i];
-            m = (p >= 0 ? sm.mask[p] : 0ull) | (1ull << i);
-            sm.mask[i] = m;
-        }
+        for (int p = tid; p >= 0; p = sm.cpar[p]) m |= 1ull << p;
+        sm.mask[tid] = m;
     }
     __syncthreads();
     const size_t base = (size_t)req * Ncap;
@@ -458,7 +495,13 @@ FlashPlan flash_plan(const dt_params* p) {
     const size_t sets = (size_t)p->R * p->B * p->k * sizeof(int32_t);
     pl.sets_bytes = (sets + 255) & ~(size_t)255;
     const size_t lsep = (size_t)p->R * pl.NS * pl.SP * sizeof(float2);
-    pl.total = pl.sets_bytes + ((lsep + 255) & ~(size_t)255);
+    pl.zc_off = pl.sets_bytes + ((lsep + 255) & ~(size_t)255);
+    const size_t zc = (size_t)p->R * pl.NS * p->k * sizeof(float);
+    pl.setp_off = pl.zc_off + ((zc + 255) & ~(size_t)255);
+    const int rows = p->R * p->B;
+    int parts = (512 + rows - 1) / rows;
+    pl.P = parts < 1 ? 1 : (parts > 32 ? 32 : parts);
+    pl.total = pl.setp_off + (((size_t)rows * pl.P * kMaxK * sizeof(uint64_t) + 255) & ~(size_t)255);
     return pl;
 }
 
@@ -475,6 +518,9 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
     a.tau = tau;
     a.sets = (int32_t*)ws;
     a.lsep = (float2*)(ws + pl.sets_bytes);
+    a.zc = (float*)(ws + pl.zc_off);
+    a.setp = (uint64_t*)(ws + pl.setp_off);
+    a.P = pl.P;
     a.out = *out;
     a.R = p->R;
     a.B = p->B;
@@ -487,8 +533,11 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
     a.T = pl.T;
     a.logits_bf16 = p->logits_dtype == DT_BF16;
     for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
-    k_flash_sets<<<p->R * p->B, kFlashSetThreads, 0, st>>>(a);
+    k_flash_sets<<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_flash_sets_merge<<<p->R * p->B, 64, 0, st>>>(a);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = a.T * ((a.SP + 7) / 8) * 8;
     if (p->head_dtype == DT_BF16)
@@ -497,10 +546,7 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
         k_flash_lse<false><<<grid, 256, 0, st>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p->head_dtype == DT_BF16)
-        k_flash_select<true><<<p->R, kFlashSelThreads, 0, st>>>(a);
-    else
-        k_flash_select<false><<<p->R, kFlashSelThreads, 0, st>>>(a);
+    k_flash_select<<<p->R, kFlashSelThreads, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -215,7 +215,6 @@ typedef struct dt_policy {
 dt_status dt_load_policy(const dt_policy* pol, float load, int32_t R, float* tau,
                          int32_t* n_budget);
 
-/* Human-readable name of a status code (static string). */
 /* ---- Two-stage M-ary tree ------------------------------------------------------------------
  * The TreeFlash construction (TreeFlash explainer, technical summary, methodology: two-stage
  * inference construction) on this library's Markov head, M = p->k.  Stage 1: for every block

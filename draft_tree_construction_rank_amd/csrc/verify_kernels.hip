@@ -330,18 +330,53 @@ __global__ __launch_bounds__(256) void k_vs_rows(const VsArgs a) {
             float* vr = a.vrow + (size_t)req * a.V;
             float mq = -INFINITY, mp = -INFINITY;
             float yq[32], yp[32];
+            if (a.bf16 && (a.V & 7) == 0 && cb + 32 <= a.V) {
+                // whole 32-column part inside the row: 16-byte loads of the block and target
+                // logits, 16-byte stores of the draft row
+                const uint4* lv = (const uint4*)((const uint16_t*)a.L + lbase + cb);
+                const uint4* tv = (const uint4*)((const uint16_t*)a.target + tbase + cb);
+                uint4 lw[4], tw[4];
 #pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                const int x = cb + j;
-                if (x < a.V) {
-                    yq[j] = (zr[j] + load_logit(a.L, lbase + x, a.bf16)) * a.y2scale;
-                    yp[j] = load_logit(a.target, tbase + x, a.bf16) * a.y2scale;
-                    vr[x] = yq[j];
+                for (int g = 0; g < 4; ++g) {
+                    lw[g] = lv[g];
+                    tw[g] = tv[g];
+                }
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t l4[4] = {lw[g].x, lw[g].y, lw[g].z, lw[g].w};
+                    const uint32_t t4[4] = {tw[g].x, tw[g].y, tw[g].z, tw[g].w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const int j = 8 * g + 2 * h;
+                        yq[j] = (zr[j] + bf16_lo(l4[h])) * a.y2scale;
+                        yq[j + 1] = (zr[j + 1] + bf16_hi(l4[h])) * a.y2scale;
+                        yp[j] = bf16_lo(t4[h]) * a.y2scale;
+                        yp[j + 1] = bf16_hi(t4[h]) * a.y2scale;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
                     mq = fmaxf(mq, yq[j]);
                     mp = fmaxf(mp, yp[j]);
-                } else {
-                    yq[j] = -INFINITY;
-                    yp[j] = -INFINITY;
+                }
+                float4* vo = (float4*)(vr + cb);
+#pragma unroll
+                for (int g = 0; g < 8; ++g)
+                    vo[g] = make_float4(yq[4 * g], yq[4 * g + 1], yq[4 * g + 2], yq[4 * g + 3]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) {
+                    const int x = cb + j;
+                    if (x < a.V) {
+                        yq[j] = (zr[j] + load_logit(a.L, lbase + x, a.bf16)) * a.y2scale;
+                        yp[j] = load_logit(a.target, tbase + x, a.bf16) * a.y2scale;
+                        vr[x] = yq[j];
+                        mq = fmaxf(mq, yq[j]);
+                        mp = fmaxf(mp, yp[j]);
+                    } else {
+                        yq[j] = -INFINITY;
+                        yp[j] = -INFINITY;
+                    }
                 }
             }
             float sq = 0.0f, sp = 0.0f;
@@ -407,7 +442,8 @@ struct ChainArgs {
 // request has; then every thread reads the SC partials.  nbar: barriers of the request
 // passed before this one.
 __device__ __forceinline__ bool vs_exchange(const ChainArgs& a, int req, int sp, int phase,
-                                            uint64_t val, int nbar, uint64_t* parts, int* bc) {
+                                            uint64_t val, int nbar, uint64_t* parts, int* bc,
+                                            uint64_t* shp) {
     uint64_t* red = a.vred + ((size_t)req * kVsPhases + phase) * kVsMaxSplits;
     const int tid = threadIdx.x;
     if (tid == 0) cst64(red + sp, val);
@@ -430,8 +466,11 @@ __device__ __forceinline__ bool vs_exchange(const ChainArgs& a, int req, int sp,
     }
     __syncthreads();
     const bool ok = bc[0] != 0;
+    // SC threads read one partial each from the coherent level; the rest read LDS
+    if (ok && tid < a.SC) shp[tid] = cld64(red + tid);
+    __syncthreads();
     if (ok)
-        for (int i = 0; i < a.SC; ++i) parts[i] = cld64(red + i);
+        for (int i = 0; i < a.SC; ++i) parts[i] = shp[i];
     __syncthreads();
     return ok;
 }
@@ -442,6 +481,7 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
     __shared__ Lse2 shl[2][8];
     __shared__ int s_tok[kMaxNcap], s_par[kMaxNcap];
     __shared__ int bc[2];
+    __shared__ uint64_t shp[kVsMaxSplits];
     const int req = blockIdx.x / a.SC, sp = blockIdx.x % a.SC, tid = threadIdx.x;
     VState st = a.state[req];
     if (!st.active) {
@@ -490,7 +530,7 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
     if (st.depth == a.B) {
         // a draw from p: Gumbel-max over target / T
         const uint64_t mine = slice_draw(false, 0.0f, 0.0f, 0.0f);
-        if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc)) emitted = pick(parts);
+        if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc, shp)) emitted = pick(parts);
         else failed = true;
         ++nbar;
     } else {
@@ -545,7 +585,7 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
                                   alpha * exp2f(yq[y] - lse_q),
                               0.0f);
             part = block_sum_f(part, shf);
-            if (!vs_exchange(a, req, sp, j, (uint64_t)__float_as_uint(part), nbar, parts, bc)) {
+            if (!vs_exchange(a, req, sp, j, (uint64_t)__float_as_uint(part), nbar, parts, bc, shp)) {
                 failed = true;
                 break;
             }
@@ -561,7 +601,7 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
         if (emitted < 0 && !failed) {
             // every sibling rejected: a draw from the residual max(p - alpha q, 0)
             const uint64_t mine = slice_draw(true, lse_q, lse_p, alpha);
-            if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc)) emitted = pick(parts);
+            if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc, shp)) emitted = pick(parts);
             else failed = true;
             ++nbar;
         }

@@ -592,6 +592,10 @@ def main():
     ap.add_argument("--attention-only", nargs="*", metavar="WORKLOAD", default=None,
                     help="time only tree_attention on the named workloads (all if none given) "
                          "and print their JSON; for profiling")
+    ap.add_argument("--sample-only", type=float, nargs="*", metavar="T", default=None,
+                    help="time only the lossless-sampling round (tree_build in sample mode + "
+                         "tree_verify_sample) at the given temperatures (1.0 if none given) "
+                         "and print their JSON; for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (requests shard "
@@ -619,6 +623,12 @@ def main():
         names = args.attention_only or list(ATTN_WORKLOADS)
         ATTN_WORKLOADS = {k: v for k, v in ATTN_WORKLOADS.items() if k in names}
         print(json.dumps(attention_profile(torch, B, Flusher(torch))), flush=True)
+        return
+    if args.sample_only is not None:
+        fl = Flusher(torch)
+        for T in args.sample_only or [1.0]:
+            r = sample_round_us(torch, rt, inputs, T, fl, steps=args.steps, warmup=args.warmup)
+            print(json.dumps({"sample_round": {"temperature": T, **r}}), flush=True)
         return
 
     inst = inputs.make_instance("batched", tau=args.tau)

@@ -47,7 +47,7 @@ Layout make_layout(const dt_params* p, bool allow_resident) {
     L.partials = take(cap_rows * rec_floats(L.KT) * sizeof(float));
     L.build_total = off;  // everything below is used by the verifiers only
     L.vsplits = 0;
-    L.vrow = L.vstate = L.vpart = L.vcnt = L.vred = 0;
+    L.vrow = L.vstate = L.vpart = L.vred = 0;
     L.vcsplits = 0;
     if (p->mode == DT_SAMPLE) {
         // sample verify: ceil(R/64) request tiles x vsplits vocabulary splits, grid <= 1024
@@ -57,15 +57,18 @@ Layout make_layout(const dt_params* p, bool allow_resident) {
         if (s > L.NC) s = L.NC;
         if (s < 1) s = 1;
         L.vsplits = s;
-        // rejection chain: about 512 workgroups over all requests, at most kVsMaxSplits each
+        // rejection chain: about 512 workgroups over all requests, at least enough that a
+        // workgroup's slice fits the groups its threads cache (kVsChainWords), at most
+        // kVsMaxSplits each and at most one per 8-word group of the vocabulary
         int c = (int)(512 / R);
+        const int need = (int)((V + kVsChainWords - 1) / kVsChainWords);
+        if (c < need) c = need;
         c = c < 1 ? 1 : (c > kVsMaxSplits ? kVsMaxSplits : c);
-        if ((size_t)c > V) c = (int)V;
+        if ((size_t)c > (V + 7) / 8) c = (int)((V + 7) / 8);
         L.vcsplits = c;
         L.vrow = take(R * V * sizeof(float));
         L.vstate = take(2 * R * sizeof(VState));
         L.vpart = take(R * (size_t)L.vsplits * 4 * sizeof(float));
-        L.vcnt = take(R * sizeof(unsigned));
         L.vred = take(R * (size_t)kVsPhases * kVsMaxSplits * sizeof(uint64_t));
     }
     {

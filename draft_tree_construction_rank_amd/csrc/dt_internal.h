@@ -76,9 +76,8 @@ struct Layout {
     size_t vrow;      // float [R][V]: sample verify, draft row of the node (log2 units)
     size_t vstate;    // VState [R]
     size_t vpart;     // float [R][vsplits][4]: sample verify partial (max, sum) of q and p
-    size_t vcnt;      // unsigned [R]: sample verify, per-request barrier counters
     size_t vred;      // u64 [R][kVsPhases][kVsMaxSplits]: per-slice partials of a step's
-                      // reductions (residual masses, draws)
+                      // reductions (residual masses, draws), tagged with the step
     size_t gpart;     // (float, int) [R][gsplits]: greedy verify, split argmax of the root rows
     size_t trace;     // u64 [kMaxGrid][kTraceLevels][16]: phase timestamps (DT_TRACE builds only)
     size_t build_total;  // extent of the regions tree_build uses (a prefix of the layout)
@@ -102,13 +101,14 @@ inline int kt_for(int k) { return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8; }
 // a multiple of 4 for 16-byte accesses.
 __host__ __device__ constexpr int rec_floats(int KT) { return ((2 + 3 * KT) + 3) & ~3; }
 
-// Walk state of one request in sample verify.  nbar: per-request barriers passed so far in
-// the round (the chain's workgroups of a request count the same barriers).
+// Walk state of one request in sample verify (nemit: steps taken, one token emitted each).
 struct alignas(8) VState {
-    int active, v, row, depth, token, nacc, nemit, nbar;
+    int active, v, row, depth, token, nacc, nemit, pad;
     uint64_t hash;
 };
 constexpr int kVsMaxSplits = 16;     // chain workgroups per request at most
+constexpr int kVsChainWords = 256 * 6 * 8;  // vocabulary words a chain workgroup keeps in
+                                            // registers (threads x cached groups x 8)
 constexpr int kVsPhases = kMaxK + 1;  // reductions of one step: k residual masses, one draw
 
 // Control words at the start of the workspace.  Per-level words are indexed by the level

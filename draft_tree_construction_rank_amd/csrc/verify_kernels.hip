@@ -225,12 +225,12 @@ hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
 //   k_vs_rows  - for every request still walking at a node of depth < B: the node's draft
 //                row y_q = (L[d] + U[t] . Wt) * log2(e)/T on MFMA (same tile as expansion),
 //                stored to vrow, plus per-split (max, sum) of y_q and of the target row;
-//   k_vs_split - the rejection chain, each request on S workgroups that split the
+//   k_vs_split - the rejection chain, each request on SC workgroups that split the
 //                vocabulary: every workgroup of a request takes the same decisions (they
 //                depend only on values every workgroup computes identically), and each
 //                vocabulary-wide reduction (a residual mass, a draw) is one partial per
-//                slice, published and summed in slice order after a per-request barrier.
-//                p and q are evaluated where they are needed, never stored.
+//                slice, exchanged through tagged slots and summed in slice order.  A
+//                workgroup keeps its slice's p and q in registers for the whole step.
 // Residuals in closed form: after j rejections the target law is max(p - a_j q, 0) / S_j
 // with a_0 = 0, S_0 = 1, a_{j+1} = a_j + S_j / c_j, c_j = 1 - (q mass of the rejected
 // siblings), S_{j+1} = sum max(p - a_{j+1} q, 0), and the draft law is q / c_j on the
@@ -241,7 +241,7 @@ hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
 // =======================================================================================
 __global__ __launch_bounds__(256) void k_vs_init(int R, int B, uint32_t round,
                                                  const int32_t* root_token, dt_tree tree,
-                                                 VState* state, unsigned* vcnt, dt_verify_out out) {
+                                                 VState* state, uint64_t* vred, dt_verify_out out) {
     const int req = blockIdx.x * blockDim.x + threadIdx.x;
     if (req >= R) return;
     VState s;
@@ -253,10 +253,11 @@ __global__ __launch_bounds__(256) void k_vs_init(int R, int B, uint32_t round,
     s.token = root_token[req];
     s.nacc = 0;
     s.nemit = 0;
-    s.nbar = 0;
+    s.pad = 0;
     s.hash = root_hash(round, req, s.token);
     state[req] = s;
-    vcnt[req] = 0u;
+    // the chain's exchange slots: no slot may hold a tag of this round's steps yet
+    for (int i = 0; i < kVsPhases * kVsMaxSplits; ++i) vred[(size_t)req * kVsPhases * kVsMaxSplits + i] = 0ull;
     for (int i = 0; i < B; ++i) out.path[(size_t)req * B + i] = -1;
     for (int i = 0; i <= B; ++i) out.out_tokens[(size_t)req * (B + 1) + i] = -1;
     out.accept_len[req] = 0;
@@ -274,6 +275,7 @@ struct VsArgs {
     int R, B, V, r, Ncap, NC, S;
     float y2scale;
     int bf16;
+    int vec;  // bf16 logits, V a multiple of 8, 16-byte aligned L and target: 16-byte loads
 };
 
 template <bool HEAD_BF16>
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(256) void k_vs_rows(const VsArgs a) {
             float* vr = a.vrow + (size_t)req * a.V;
             float mq = -INFINITY, mp = -INFINITY;
             float yq[32], yp[32];
-            if (a.bf16 && (a.V & 7) == 0 && cb + 32 <= a.V) {
+            if (a.vec && cb + 32 <= a.V) {
                 // whole 32-column part inside the row: 16-byte loads of the block and target
                 // logits, 16-byte stores of the draft row
                 const uint4* lv = (const uint4*)((const uint16_t*)a.L + lbase + cb);
@@ -427,7 +429,6 @@ struct ChainArgs {
     VState* next;         // next step's walk states
     const float* vrow;
     const float* vpart;
-    unsigned* vcnt;
     uint64_t* vred;
     dt_tree tree;
     dt_verify_out out;
@@ -435,52 +436,146 @@ struct ChainArgs {
     float y2scale, invT;
     uint32_t seed_lo, seed_hi, spin_limit;
     int bf16;
+    int vec;  // bf16 target, V a multiple of 8, 16-byte aligned target: 16-byte loads
 };
 
-// Per-request exchange of one partial per slice: publishes this workgroup's value in the
-// phase's slot, counts the barrier and waits (bounded) until every workgroup of the
-// request has; then every thread reads the SC partials.  nbar: barriers of the request
-// passed before this one.
+// Per-request exchange of one partial per slice.  Each reduction of a step has its own slot
+// per slice (phase j < k: the residual mass after sibling j; kMaxK: the draw), used at most
+// once a step, and a slot word carries the step's tag (walk step + 1, at most 33) in its low
+// byte: a workgroup writes its partial and tag in one 64-bit store, and SC threads wait
+// (bounded) until every slot of the request holds this step's tag.  Slots are zeroed at the
+// start of a round, and a step is one launch, so no slot can hold a stale word with the
+// current tag.  Every thread then reads the SC words, in slice order.
 __device__ __forceinline__ bool vs_exchange(const ChainArgs& a, int req, int sp, int phase,
-                                            uint64_t val, int nbar, uint64_t* parts, int* bc,
+                                            uint64_t val, uint32_t tag, uint64_t* parts,
                                             uint64_t* shp) {
     uint64_t* red = a.vred + ((size_t)req * kVsPhases + phase) * kVsMaxSplits;
     const int tid = threadIdx.x;
-    if (tid == 0) cst64(red + sp, val);
-    publish();
-    __syncthreads();
-    if (tid == 0) {
-        int ok = 1;
-        const unsigned target = (unsigned)(a.SC * (nbar + 1));
-        cadd32(a.vcnt + req, 1u);
+    if (tid == 0) cst64(red + sp, val | tag);
+    int ok = 1;
+    if (tid < a.SC) {
+        uint64_t w = cld64(red + tid);
         uint32_t it = 0;
-        while ((int)(cld32(a.vcnt + req) - target) < 0) {
+        while ((uint32_t)(w & 0xFFu) != tag) {
             __builtin_amdgcn_s_sleep(2);
             if (++it > a.spin_limit) {
                 ok = 0;
                 break;
             }
+            w = cld64(red + tid);
         }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        bc[0] = ok;
+        shp[tid] = w;
     }
-    __syncthreads();
-    const bool ok = bc[0] != 0;
-    // SC threads read one partial each from the coherent level; the rest read LDS
-    if (ok && tid < a.SC) shp[tid] = cld64(red + tid);
-    __syncthreads();
+    ok = __syncthreads_and(ok);
     if (ok)
         for (int i = 0; i < a.SC; ++i) parts[i] = shp[i];
     __syncthreads();
-    return ok;
+    return ok != 0;
 }
 
-__global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
+// A draw's slot word: key order in the high half, the complemented token (24 bits) above the
+// tag, so that the largest word is the largest key, then the lowest token; 0 above the tag:
+// no candidate in the slice.
+__device__ __forceinline__ uint64_t vs_draw_word(float key, int tok) {
+    return ((uint64_t)ord32(key) << 32) | ((uint64_t)(~(uint32_t)tok & 0xFFFFFFu) << 8);
+}
+
+// E = -ln u, an Exp(1) variate, for u = (m + 1/2) 2^-24 with m = the top 24 bits of w (the
+// uniform of u01).  A Gumbel variate is -ln E, so ranking x + Gumbel is ranking x - ln E and,
+// for positive weights d, ranking d + Gumbel in the log domain is ranking d / E.  For m < 2^23
+// u is exact in float32 and E = -ln u; above, v = 1 - u is exact: below 2^-6 the series
+// v + v^2/2 + ... + v^5/5 (truncation below 2e-10 relative), otherwise -ln of the rounded u
+// (relative error below 2e-6).
+__device__ __forceinline__ float exp1_variate(uint32_t w) {
+    const uint32_t m = w >> 8;
+    const float u = ((float)m + 0.5f) * (1.0f / 16777216.0f);
+    const float v = ((float)(16777216u - m) - 0.5f) * (1.0f / 16777216.0f);
+    const float poly = v * (1.0f + v * (0.5f + v * (1.0f / 3.0f + v * (0.25f + v * 0.2f))));
+    return (m >= (1u << 23) && v < 0.015625f) ? poly : -logf(u);
+}
+
+// The chain keeps its slice of p and q in registers: thread t of a workgroup owns the
+// 8-element groups g_lo + t + kVsThreads * i of the slice, for i < kVsCached (loaded once a
+// step, before the first sibling's test), and recomputes any groups beyond those from memory
+// on every pass (only vocabularies above kVsThreads * kVsCached * 8 * kVsMaxSplits words).
+constexpr int kVsThreads = 256;
+constexpr int kVsCached = 6;
+static_assert(kVsChainWords == kVsThreads * kVsCached * 8, "chain slice capacity");
+
+// Eight target logits (raw, not tempered) of group g; -inf past the vocabulary.
+__device__ __forceinline__ void vs_load_t8(const ChainArgs& a, size_t tbase, int g, float (&t)[8]) {
+    const int x0 = 8 * g;
+    if (a.vec) {
+        const uint4 w = *(const uint4*)((const uint16_t*)a.target + tbase + x0);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            t[2 * h] = bf16_lo(ws[h]);
+            t[2 * h + 1] = bf16_hi(ws[h]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            t[e] = x0 + e < a.V ? load_logit(a.target, tbase + x0 + e, a.bf16) : -INFINITY;
+    }
+}
+
+// Eight draft logits (log2 units) of group g; -inf past the vocabulary.
+__device__ __forceinline__ void vs_load_y8(const ChainArgs& a, const float* yq, int g, float (&y)[8]) {
+    const int x0 = 8 * g;
+    if (a.vec) {
+        const float4 v0 = *(const float4*)(yq + x0), v1 = *(const float4*)(yq + x0 + 4);
+        y[0] = v0.x; y[1] = v0.y; y[2] = v0.z; y[3] = v0.w;
+        y[4] = v1.x; y[5] = v1.y; y[6] = v1.z; y[7] = v1.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = x0 + e < a.V ? yq[x0 + e] : -INFINITY;
+    }
+}
+
+// p and q (normalised, linear units) from the raw logits; 0 past the vocabulary.
+__device__ __forceinline__ void vs_pq8(const ChainArgs& a, const float (&t)[8], const float (&y)[8],
+                                       float lse_q, float lse_p, float (&p)[8], float (&q)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        p[e] = exp2f(t[e] * a.y2scale - lse_p);
+        q[e] = exp2f(y[e] - lse_q);
+    }
+}
+
+// Exponential-race entries of one group of the residual max(p - alpha q, 0) (index 8g + e):
+// the key d / E ranks like ln d + Gumbel.
+__device__ __forceinline__ void vs_resid_draw8(const ChainArgs& a, uint64_t hash, int g,
+                                               const float (&p)[8], const float (&q)[8],
+                                               float alpha, ArgMax& best) {
+    float d[8];
+    bool any = false;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        d[e] = p[e] - alpha * q[e];
+        any |= d[e] > 0.0f;
+    }
+    if (!any) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4 w = rand4((uint32_t)(2 * g + h), STREAM_RESID, hash, a.seed_lo, a.seed_hi);
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float de = d[4 * h + e];
+            if (de > 0.0f)
+                amax_seq(best, de * __builtin_amdgcn_rcpf(exp1_variate(ws[e])), 8 * g + 4 * h + e);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kVsThreads) void k_vs_split(const ChainArgs a) {
     __shared__ float shf[8];
     __shared__ ArgMax sha[8];
     __shared__ Lse2 shl[2][8];
     __shared__ int s_tok[kMaxNcap], s_par[kMaxNcap];
-    __shared__ int bc[2];
+    __shared__ int s_x[kMaxK];
+    __shared__ float s_yx[kMaxK], s_tx[kMaxK];
     __shared__ uint64_t shp[kVsMaxSplits];
     const int req = blockIdx.x / a.SC, sp = blockIdx.x % a.SC, tid = threadIdx.x;
     VState st = a.state[req];
@@ -488,60 +583,95 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
         if (sp == 0 && tid == 0) a.next[req] = st;
         return;
     }
+    const uint32_t tag = (uint32_t)st.nemit + 1u;
     const int n = a.tree.n_nodes[req];
     if (tid < a.Ncap) {
         s_tok[tid] = a.tree.token[(size_t)req * a.Ncap + tid];
         s_par[tid] = a.tree.parent[(size_t)req * a.Ncap + tid];
     }
-    const int lo = (int)((long long)sp * a.V / a.SC), hi = (int)((long long)(sp + 1) * a.V / a.SC);
+    // this workgroup's slice: 8-element groups [g_lo, g_hi)
+    const int G8 = (a.V + 7) >> 3;
+    const int g_lo = (int)((long long)sp * G8 / a.SC), g_hi = (int)((long long)(sp + 1) * G8 / a.SC);
+    const int g_rest = g_lo + tid + kVsThreads * kVsCached;  // first group not cached
     const size_t tbase = ((size_t)req * (a.Ncap + 1) + st.row) * (size_t)a.V;
     const float* yq = a.vrow + (size_t)req * a.V;
-    int nbar = st.nbar;
     int emitted = -1;
     bool descend = false, failed = false;
     uint64_t parts[kVsMaxSplits];
-    // draw of this slice as a ranked entry (key desc, then lower index); 0 = no candidate
-    auto slice_draw = [&](bool residual, float lse_q, float lse_p, float alpha) -> uint64_t {
-        ArgMax best{-INFINITY, 0x7fffffff};
-        for (int g = (lo >> 2) + tid; 4 * g < hi; g += blockDim.x) {
-            const uint4 w = rand4((uint32_t)g, STREAM_RESID, st.hash, a.seed_lo, a.seed_hi);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int x = 4 * g + e;
-                if (x < lo || x >= hi) continue;
-                const float t = load_logit(a.target, tbase + x, a.bf16);
-                if (!residual) {
-                    best = amax(best, ArgMax{t * a.invT + gumbel(ws[e]), x});
-                } else {
-                    const float d = exp2f(t * a.y2scale - lse_p) - alpha * exp2f(yq[x] - lse_q);
-                    if (d > 0.0f) best = amax(best, ArgMax{logf(d) + gumbel(ws[e]), x});
-                }
-            }
-        }
-        best = block_amax(best, sha);
-        return best.v == -INFINITY ? 0ull : pack_entry(best.v, best.i);
-    };
     auto pick = [&](const uint64_t* ps) -> int {
         uint64_t b = 0;
         for (int i = 0; i < a.SC; ++i) b = ps[i] > b ? ps[i] : b;
-        return b ? entry_tok(b) : -1;
+        return (b >> 8) ? (int)(~(uint32_t)(b >> 8) & 0xFFFFFFu) : -1;
+    };
+    auto ranked = [&](ArgMax best) -> uint64_t {
+        best = block_amax(best, sha);
+        return best.v == -INFINITY ? 0ull : vs_draw_word(best.v, best.i);
     };
     if (st.depth == a.B) {
         // a draw from p: Gumbel-max over target / T
-        const uint64_t mine = slice_draw(false, 0.0f, 0.0f, 0.0f);
-        if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc, shp)) emitted = pick(parts);
+        ArgMax best{-INFINITY, 0x7fffffff};
+        for (int g = g_lo + tid; g < g_hi; g += kVsThreads) {
+            float t[8];
+            vs_load_t8(a, tbase, g, t);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 w = rand4((uint32_t)(2 * g + h), STREAM_RESID, st.hash, a.seed_lo,
+                                      a.seed_hi);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int x = 8 * g + 4 * h + e;
+                    if (x < a.V) amax_seq(best, t[4 * h + e] * a.invT - logf(exp1_variate(ws[e])), x);
+                }
+            }
+        }
+        const uint64_t mine = ranked(best);
+        if (vs_exchange(a, req, sp, kMaxK, mine, tag, parts, shp)) emitted = pick(parts);
         else failed = true;
-        ++nbar;
     } else {
+        // the drawn siblings' raw logits, fetched while the normalisers are formed
+        const int32_t* cand = a.tree.cand + ((size_t)req * (a.Ncap + 1) + st.row) * a.k;
+        if (tid < a.k) {
+            const int x = cand[tid];
+            // an empty slot (a ranked list shorter than k, only possible with non-finite
+            // draft logits) is no drawn sibling
+            const bool ok = x >= 0 && x < a.V;
+            s_x[tid] = ok ? x : -1;
+            s_yx[tid] = ok ? yq[x] : 0.0f;
+            s_tx[tid] = ok ? load_logit(a.target, tbase + x, a.bf16) : 0.0f;
+        }
+        // the slice's raw logits: every load in flight at once (groups past the slice load
+        // its first group and are zeroed when converted)
+        float ct[kVsCached][8], cy[kVsCached][8];
+#pragma unroll
+        for (int i = 0; i < kVsCached; ++i) {
+            const int g = g_lo + tid + kVsThreads * i;
+            vs_load_t8(a, tbase, g < g_hi ? g : g_lo, ct[i]);
+            vs_load_y8(a, yq, g < g_hi ? g : g_lo, cy[i]);
+        }
         // normalisers of q and p (log2 units), from the draft-row partials
         Lse2 lq, lp;
         lq.init();
         lp.init();
-        for (int s = tid; s < a.S; s += blockDim.x) {
-            const float* rec = a.vpart + ((size_t)req * a.S + s) * 4;
-            lq.merge(rec[0], rec[1]);
-            lp.merge(rec[2], rec[3]);
+        {
+            constexpr int kRecs = 4;  // records a thread loads before merging (S <= 1024)
+            float4 rec[kRecs];
+#pragma unroll
+            for (int i = 0; i < kRecs; ++i) {
+                const int s = tid + kVsThreads * i;
+                rec[i] = s < a.S ? *(const float4*)(a.vpart + ((size_t)req * a.S + s) * 4)
+                                 : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+            }
+#pragma unroll
+            for (int i = 0; i < kRecs; ++i) {
+                lq.merge(rec[i].x, rec[i].y);
+                lp.merge(rec[i].z, rec[i].w);
+            }
+            for (int s = tid + kVsThreads * kRecs; s < a.S; s += kVsThreads) {
+                const float* r = a.vpart + ((size_t)req * a.S + s) * 4;
+                lq.merge(r[0], r[1]);
+                lp.merge(r[2], r[3]);
+            }
         }
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -555,20 +685,26 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
         __syncthreads();
         lq.init();
         lp.init();
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) {
+        for (int i = 0; i < kVsThreads / 64; ++i) {
             lq.merge(shl[0][i].m, shl[0][i].s);
             lp.merge(shl[1][i].m, shl[1][i].s);
         }
         const float lse_q = lq.m + log2f(lq.s), lse_p = lp.m + log2f(lp.s);
-        const int32_t* cand = a.tree.cand + ((size_t)req * (a.Ncap + 1) + st.row) * a.k;
+        float cp[kVsCached][8], cq[kVsCached][8];
+#pragma unroll
+        for (int i = 0; i < kVsCached; ++i) {
+            vs_pq8(a, ct[i], cy[i], lse_q, lse_p, cp[i], cq[i]);
+            if (g_lo + tid + kVsThreads * i >= g_hi) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cp[i][e] = cq[i][e] = 0.0f;
+            }
+        }
         float alpha = 0.0f, S = 1.0f, c = 1.0f;
         for (int j = 0; j < a.k; ++j) {
-            const int x = cand[j];
-            // an empty slot (a ranked list shorter than k, only possible with non-finite
-            // draft logits) is no drawn sibling
-            if (x < 0 || x >= a.V) continue;
-            const float qx = exp2f(yq[x] - lse_q);
-            const float px = exp2f(load_logit(a.target, tbase + x, a.bf16) * a.y2scale - lse_p);
+            const int x = s_x[j];
+            if (x < 0) continue;
+            const float qx = exp2f(s_yx[j] - lse_q);
+            const float px = exp2f(s_tx[j] * a.y2scale - lse_p);
             const uint4 w = rand4((uint32_t)(j >> 2), STREAM_ACCEPT, st.hash, a.seed_lo, a.seed_hi);
             const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
             const float u = u01(ws[j & 3]);
@@ -580,18 +716,25 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
             alpha += S / c;
             c -= qx;
             float part = 0.0f;
-            for (int y = lo + tid; y < hi; y += blockDim.x)
-                part += fmaxf(exp2f(load_logit(a.target, tbase + y, a.bf16) * a.y2scale - lse_p) -
-                                  alpha * exp2f(yq[y] - lse_q),
-                              0.0f);
+#pragma unroll
+            for (int i = 0; i < kVsCached; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part += fmaxf(cp[i][e] - alpha * cq[i][e], 0.0f);
+            for (int g = g_rest; g < g_hi; g += kVsThreads) {
+                float t8[8], y8[8], p8[8], q8[8];
+                vs_load_t8(a, tbase, g, t8);
+                vs_load_y8(a, yq, g, y8);
+                vs_pq8(a, t8, y8, lse_q, lse_p, p8, q8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part += fmaxf(p8[e] - alpha * q8[e], 0.0f);
+            }
             part = block_sum_f(part, shf);
-            if (!vs_exchange(a, req, sp, j, (uint64_t)__float_as_uint(part), nbar, parts, bc, shp)) {
+            if (!vs_exchange(a, req, sp, j, (uint64_t)__float_as_uint(part) << 32, tag, parts, shp)) {
                 failed = true;
                 break;
             }
-            ++nbar;
             S = 0.0f;
-            for (int i = 0; i < a.SC; ++i) S += __uint_as_float((uint32_t)parts[i]);
+            for (int i = 0; i < a.SC; ++i) S += __uint_as_float((uint32_t)(parts[i] >> 32));
             if (!(S > 0.0f)) {
                 emitted = x;
                 descend = true;
@@ -600,10 +743,22 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
         }
         if (emitted < 0 && !failed) {
             // every sibling rejected: a draw from the residual max(p - alpha q, 0)
-            const uint64_t mine = slice_draw(true, lse_q, lse_p, alpha);
-            if (vs_exchange(a, req, sp, kMaxK, mine, nbar, parts, bc, shp)) emitted = pick(parts);
+            ArgMax best{-INFINITY, 0x7fffffff};
+#pragma unroll
+            for (int i = 0; i < kVsCached; ++i) {
+                const int g = g_lo + tid + kVsThreads * i;
+                if (g < g_hi) vs_resid_draw8(a, st.hash, g, cp[i], cq[i], alpha, best);
+            }
+            for (int g = g_rest; g < g_hi; g += kVsThreads) {
+                float t8[8], y8[8], p8[8], q8[8];
+                vs_load_t8(a, tbase, g, t8);
+                vs_load_y8(a, yq, g, y8);
+                vs_pq8(a, t8, y8, lse_q, lse_p, p8, q8);
+                vs_resid_draw8(a, st.hash, g, p8, q8, alpha, best);
+            }
+            const uint64_t mine = ranked(best);
+            if (vs_exchange(a, req, sp, kMaxK, mine, tag, parts, shp)) emitted = pick(parts);
             else failed = true;
-            ++nbar;
         }
     }
     __syncthreads();
@@ -623,7 +778,6 @@ __global__ __launch_bounds__(256) void k_vs_split(const ChainArgs a) {
     }
     a.out.out_tokens[(size_t)req * (a.B + 1) + st.nemit] = emitted;
     st.nemit += 1;
-    st.nbar = nbar;
     if (w >= 0) {
         a.out.path[(size_t)req * a.B + st.nacc] = w;
         st.nacc += 1;
@@ -645,9 +799,9 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
                                 const void* Wt, const int32_t* root_token, const void* target,
                                 const dt_verify_out* out, hipStream_t st) {
     VState* state = (VState*)(ws + lay.vstate);  // two buffers of R: this step's, the next's
-    unsigned* vcnt = (unsigned*)(ws + lay.vcnt);
+    uint64_t* vred = (uint64_t*)(ws + lay.vred);
     hipLaunchKernelGGL(k_vs_init, dim3((p->R + 255) / 256), dim3(256), 0, st, p->R, p->B,
-                       p->round, root_token, *tree, state, vcnt, *out);
+                       p->round, root_token, *tree, state, vred, *out);
     VsArgs va{};
     va.L = L;
     va.U = U;
@@ -664,12 +818,13 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
     va.S = lay.vsplits;
     va.y2scale = (float)(1.4426950408889634 / (double)p->temperature);
     va.bf16 = p->logits_dtype == DT_BF16;
+    const bool al16 = (((uintptr_t)L | (uintptr_t)target) & 15) == 0;
+    va.vec = va.bf16 && (p->V & 7) == 0 && al16;
     ChainArgs ca{};
     ca.target = target;
     ca.vrow = va.vrow;
     ca.vpart = va.vpart;
-    ca.vcnt = vcnt;
-    ca.vred = (uint64_t*)(ws + lay.vred);
+    ca.vred = vred;
     ca.tree = *tree;
     ca.out = *out;
     ca.R = p->R;
@@ -685,6 +840,7 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
     ca.seed_hi = (uint32_t)(p->seed >> 32);
     ca.spin_limit = kSpinLimit;
     ca.bf16 = va.bf16;
+    ca.vec = va.vec;
     const int tiles = (p->R + kTileRows - 1) / kTileRows;
     const dim3 grid(tiles * lay.vsplits);
     for (int step = 0; step <= p->B; ++step) {
@@ -695,7 +851,7 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
             hipLaunchKernelGGL(k_vs_rows<true>, grid, dim3(256), 0, st, va);
         else
             hipLaunchKernelGGL(k_vs_rows<false>, grid, dim3(256), 0, st, va);
-        hipLaunchKernelGGL(k_vs_split, dim3(p->R * lay.vcsplits), dim3(256), 0, st, ca);
+        hipLaunchKernelGGL(k_vs_split, dim3(p->R * lay.vcsplits), dim3(kVsThreads), 0, st, ca);
     }
     return hipGetLastError();
 }

@@ -592,6 +592,9 @@ def main():
     ap.add_argument("--attention-only", nargs="*", metavar="WORKLOAD", default=None,
                     help="time only tree_attention on the named workloads (all if none given) "
                          "and print their JSON; for profiling")
+    ap.add_argument("--flash-only", action="store_true",
+                    help="time only tree_build_flash on the b7, b16 and batched workloads and "
+                         "print their JSON; for profiling")
     ap.add_argument("--sample-only", type=float, nargs="*", metavar="T", default=None,
                     help="time only the lossless-sampling round (tree_build in sample mode + "
                          "tree_verify_sample) at the given temperatures (1.0 if none given) "
@@ -623,6 +626,10 @@ def main():
         names = args.attention_only or list(ATTN_WORKLOADS)
         ATTN_WORKLOADS = {k: v for k, v in ATTN_WORKLOADS.items() if k in names}
         print(json.dumps(attention_profile(torch, B, Flusher(torch))), flush=True)
+        return
+    if args.flash_only:
+        print(json.dumps({"tree_build_flash": flash_profile(torch, rt, inputs, Flusher(torch),
+                                                            steps=args.steps)}), flush=True)
         return
     if args.sample_only is not None:
         fl = Flusher(torch)

@@ -43,6 +43,7 @@ struct FlashArgs {
     dt_tree out;
     int R, B, M, V, r, Ncap, NS, SP, T, P;
     int logits_bf16;
+    int lvec;  // bf16 logits, V a multiple of 8, 16-byte aligned L: 16-byte loads of L rows
     float cal[16];
 };
 
@@ -79,25 +80,29 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
     const size_t base = (size_t)row * a.V;
     TopK<kMaxK> top;
     top.init();
-    if (a.logits_bf16 && (a.V & 7) == 0) {
+    if (a.lvec) {
         const uint4* p = (const uint4*)((const uint16_t*)a.L + base);
         const int ng = a.V / 8;
         const int g_beg = (int)((long)part * ng / a.P), g_end = (int)((long)(part + 1) * ng / a.P);
-        for (int g0 = g_beg + tid; g0 < g_end; g0 += 2 * kFlashSetThreads) {
-            const int g1 = g0 + kFlashSetThreads;
-            const uint4 w0 = p[g0], w1 = p[g1 < g_end ? g1 : g0];
-            const uint32_t x0[4] = {w0.x, w0.y, w0.z, w0.w};
+        // four 16-byte loads in flight per thread (groups past the part reload its first)
+        constexpr int kU = 4;
+        for (int g0 = g_beg + tid; g0 < g_end; g0 += kU * kFlashSetThreads) {
+            uint4 w[kU];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                flash_offer(top, bf16_lo(x0[i]), 8 * g0 + 2 * i);
-                flash_offer(top, bf16_hi(x0[i]), 8 * g0 + 2 * i + 1);
+            for (int u = 0; u < kU; ++u) {
+                const int g = g0 + u * kFlashSetThreads;
+                w[u] = p[g < g_end ? g : g0];
             }
-            if (g1 < g_end) {
-                const uint32_t x1[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    flash_offer(top, bf16_lo(x1[i]), 8 * g1 + 2 * i);
-                    flash_offer(top, bf16_hi(x1[i]), 8 * g1 + 2 * i + 1);
+            for (int u = 0; u < kU; ++u) {
+                const int g = g0 + u * kFlashSetThreads;
+                if (g < g_end) {
+                    const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        flash_offer(top, bf16_lo(x[i]), 8 * g + 2 * i);
+                        flash_offer(top, bf16_hi(x[i]), 8 * g + 2 * i + 1);
+                    }
                 }
             }
         }
@@ -147,8 +152,172 @@ __global__ __launch_bounds__(64) void k_flash_sets_merge(FlashArgs a) {
 // ---- stage 2: log-sum-exp of every state over vocabulary splits ---------------------------
 // Workgroup b: XCD x = b % 8 takes splits x, x + 8, ...; the T tiles of one split are adjacent
 // in that XCD's queue, so they run together and read the split's W columns from its L2.
+
+// bf16 heads: the transposed block of the expansion (W as the MFMA A operand, the tile's U
+// rows from LDS as B), so lane l holds state l % 32 (and 32 + l % 32) at 16 columns of each
+// 32-column block and the online log-sum-exp runs on the accumulators; the block logits are
+// the accumulators' initial values, so z = L + U.W leaves the MFMA directly.  Wavefront w
+// takes the split's blocks w, w + 4, ...; the next block's W fragments and logits are loaded
+// while the current block's epilogue runs.
+constexpr int kFlashLseWaves = 4;
+static_assert(kFlashLseWaves * 64 == 256, "k_flash_lse runs 256 threads");
+
+// Raw bf16 block logits of a lane's 16 columns (c0 + 8j + 4h + i), 16-byte-aligned rows only.
+__device__ __forceinline__ void flash_lgroups(const FlashArgs& a, size_t lb, int c0, int h,
+                                              uint2 (&g)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = c0 + 8 * j + 4 * h;
+        g[j] = *(const uint2*)((const uint16_t*)a.L + lb + (c < a.V ? c : a.V - 4));
+    }
+}
+
+// The accumulators' initial values: the block logits of the lane's columns (clamped into the
+// row past V; those columns are masked in the epilogue).
+__device__ __forceinline__ void flash_to_acc(const FlashArgs& a, const uint2 (&g)[4], size_t lb,
+                                             int c0, int h, f32x16& acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (a.lvec) {
+            acc[4 * j + 0] = bf16_lo(g[j].x);
+            acc[4 * j + 1] = bf16_hi(g[j].x);
+            acc[4 * j + 2] = bf16_lo(g[j].y);
+            acc[4 * j + 3] = bf16_hi(g[j].y);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = c0 + 8 * j + 4 * h + i;
+                acc[4 * j + i] = flash_logit(a, lb + (c < a.V ? c : a.V - 1));
+            }
+        }
+    }
+}
+
+// One state's 16 values of a block: the conditional logits of its children that fall in
+// these columns (the same fp32 values that enter the log-sum-exp), then the online
+// log-sum-exp (log2 units).
+__device__ __forceinline__ void flash_epi(const FlashArgs& a, f32x16& z, int c0, int h,
+                                          const int* tgt, size_t zrow, Lse2& st) {
+    if (c0 + kBlockCols > a.V) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (c0 + 8 * (e >> 2) + 4 * h + (e & 3) >= a.V) z[e] = -INFINITY;
+    }
+    for (int i = 0; i < a.M; ++i) {
+        const int off = tgt[i] - c0;
+        if (off >= 0 && off < kBlockCols && ((off >> 2) & 1) == h) {
+            const int e = 4 * (off >> 3) + (off & 3);
+            float v = z[0];
+#pragma unroll
+            for (int q = 1; q < 16; ++q) v = q == e ? z[q] : v;
+            a.zc[zrow + i] = v;
+        }
+    }
+    constexpr float kLog2e = 1.4426950408889634f;
+    float zmax = z[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) zmax = fmaxf(zmax, z[e]);
+    if (zmax == -INFINITY) return;
+    const float cm = zmax * kLog2e;
+    if (cm > st.m) {
+        st.s = (st.m == -INFINITY) ? 0.0f : st.s * exp2f(st.m - cm);
+        st.m = cm;
+    }
+    float ps = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ps += exp2f(z[e] * kLog2e - st.m);
+    st.s += ps;
+}
+
+__device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
+    __shared__ __align__(16) uint16_t sA[kTileRows * kAStride];
+    __shared__ int sTok[kTileRows];
+    __shared__ size_t sLb[kTileRows];
+    __shared__ int sTgt[kTileRows][kMaxK];
+    __shared__ Lse2 sW[kFlashLseWaves][kTileRows];
+    const int b = blockIdx.x;
+    const int idx = b >> 3;
+    const int tile = idx % a.T;
+    const int split = (idx / a.T) * 8 + (b & 7);
+    if (split >= a.SP) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, p0 = lane & 31;
+    const int rows_total = a.R * a.NS;
+    const int g0 = tile * kTileRows;
+    const int nrows = min(kTileRows, rows_total - g0);
+    if (tid < kTileRows) {
+        int t = -1;
+        size_t lb = 0;
+        for (int i = 0; i < kMaxK; ++i) sTgt[tid][i] = -1;
+        if (tid < nrows) {
+            const int g = g0 + tid, req = g / a.NS;
+            int j;
+            flash_state(a, req, g % a.NS, &j, &t);
+            lb = ((size_t)req * a.B + j) * a.V;
+            for (int i = 0; i < a.M; ++i) sTgt[tid][i] = a.sets[((size_t)req * a.B + j) * a.M + i];
+        }
+        sTok[tid] = t;
+        sLb[tid] = lb;
+    }
+    __syncthreads();
+    load_a_tile<true>(a.U, a.r, nrows, [&](int row) { return sTok[row]; }, sA, nullptr);
+    __syncthreads();
+    const int NB = (a.V + kBlockCols - 1) / kBlockCols;
+    const int b_beg = (int)((long)split * NB / a.SP), b_end = (int)((long)(split + 1) * NB / a.SP);
+    const bool two = nrows > 32;
+    const bool live0 = p0 < nrows, live1 = 32 + p0 < nrows;
+    const size_t lb0 = sLb[p0], lb1 = sLb[32 + p0];
+    const size_t zr0 = (size_t)(g0 + p0) * a.M, zr1 = (size_t)(g0 + 32 + p0) * a.M;
+    Lse2 s0, s1;
+    s0.init();
+    s1.init();
+    bf16x8 wf[16];
+    uint2 n0[4], n1[4];
+    int blk = b_beg + wave;
+    if (blk < b_end) {
+        load_wfrag(a.Wt, a.V, a.r, blk * kBlockCols, wf);
+        if (a.lvec) {
+            flash_lgroups(a, lb0, blk * kBlockCols, h, n0);
+            if (two) flash_lgroups(a, lb1, blk * kBlockCols, h, n1);
+        }
+    }
+    for (; blk < b_end; blk += kFlashLseWaves) {
+        const int c0 = blk * kBlockCols;
+        f32x16 acc0, acc1;
+        flash_to_acc(a, n0, lb0, c0, h, acc0);
+        if (two) flash_to_acc(a, n1, lb1, c0, h, acc1);
+        mma_wfrag(wf, two, sA, acc0, acc1);
+        if (blk + kFlashLseWaves < b_end) {
+            const int cn = c0 + kFlashLseWaves * kBlockCols;
+            load_wfrag(a.Wt, a.V, a.r, cn, wf);
+            if (a.lvec) {
+                flash_lgroups(a, lb0, cn, h, n0);
+                if (two) flash_lgroups(a, lb1, cn, h, n1);
+            }
+        }
+        if (live0) flash_epi(a, acc0, c0, h, sTgt[p0], zr0, s0);
+        if (two && live1) flash_epi(a, acc1, c0, h, sTgt[32 + p0], zr1, s1);
+    }
+    // lanes l and l ^ 32 hold the same state; then the wavefronts' blocks
+    s0.merge_xor(32);
+    s1.merge_xor(32);
+    if (h == 0) {
+        sW[wave][p0] = s0;
+        sW[wave][32 + p0] = s1;
+    }
+    __syncthreads();
+    if (tid < nrows) {
+        Lse2 t;
+        t.init();
+#pragma unroll
+        for (int w = 0; w < kFlashLseWaves; ++w) t.merge(sW[w][tid].m, sW[w][tid].s);
+        a.lsep[(size_t)(g0 + tid) * a.SP + split] = make_float2(t.m, t.s);
+    }
+}
+
+// float32 heads: 64 x 128 chunks through an LDS tile (thread: state tid / 4, 32 columns of
+// each chunk).
 template <bool HEAD_BF16>
-__global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
+__device__ __forceinline__ void flash_lse_chunks(const FlashArgs& a) {
     __shared__ __align__(16) uint16_t sA[kTileRows * kAStride];
     __shared__ __align__(16) float sAf[HEAD_BF16 ? 1 : kTileRows * kAfStride];
     __shared__ __align__(16) float sZ[kTileRows * kZStride];
@@ -203,13 +372,33 @@ __global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
             }
             float m = -INFINITY;
             float zv[32];
+            if (a.lvec && cb + 32 <= a.V) {
+                // the 32 block logits in four 16-byte loads
+                const uint4* lp = (const uint4*)((const uint16_t*)a.L + lb + cb);
+                uint4 lw[4];
 #pragma unroll
-            for (int i = 0; i < 32; ++i) {
-                const int c = col0 + 32 * q + i;
-                const float z = c < a.V ? (sZ[row * kZStride + 32 * q + i] + flash_logit(a, lb + c)) * kLog2e
-                                        : -INFINITY;
-                zv[i] = z;
-                m = fmaxf(m, z);
+                for (int g = 0; g < 4; ++g) lw[g] = lp[g];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t w4[4] = {lw[g].x, lw[g].y, lw[g].z, lw[g].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int i = 8 * g + 2 * e;
+                        zv[i] = (sZ[row * kZStride + 32 * q + i] + bf16_lo(w4[e])) * kLog2e;
+                        zv[i + 1] = (sZ[row * kZStride + 32 * q + i + 1] + bf16_hi(w4[e])) * kLog2e;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 32; ++i) m = fmaxf(m, zv[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 32; ++i) {
+                    const int c = cb + i;
+                    const float z = c < a.V ? (sZ[row * kZStride + 32 * q + i] + flash_logit(a, lb + c)) * kLog2e
+                                            : -INFINITY;
+                    zv[i] = z;
+                    m = fmaxf(m, z);
+                }
             }
             float s = 0.0f;
             if (m != -INFINITY)
@@ -222,6 +411,14 @@ __global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
     st.merge_xor(1);
     st.merge_xor(2);
     if (live && q == 0) a.lsep[(size_t)(g0 + row) * a.SP + split] = make_float2(st.m, st.s);
+}
+
+template <bool HEAD_BF16>
+__global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
+    if constexpr (HEAD_BF16)
+        flash_lse_blocks(a);
+    else
+        flash_lse_chunks<false>(a);
 }
 
 // ---- final selection and emission ------------------------------------------------------------
@@ -489,8 +686,10 @@ FlashPlan flash_plan(const dt_params* p) {
     pl.NS = 1 + (p->B - 1) * p->k;
     pl.T = (p->R * pl.NS + kTileRows - 1) / kTileRows;
     const int chunks = (p->V + kChunkCols - 1) / kChunkCols;
+    // about 512 workgroups, and a multiple of 8 splits so that every XCD takes the same
+    // number (workgroup b runs on XCD b % 8; with 9 splits one XCD did twice the work)
     int sp = (512 + pl.T - 1) / pl.T;
-    sp = sp < 1 ? 1 : (sp > 256 ? 256 : sp);
+    sp = sp < 8 ? 8 : (sp > 256 ? 256 : sp & ~7);
     pl.SP = sp > chunks ? chunks : sp;
     const size_t sets = (size_t)p->R * p->B * p->k * sizeof(int32_t);
     pl.sets_bytes = (sets + 255) & ~(size_t)255;
@@ -499,7 +698,9 @@ FlashPlan flash_plan(const dt_params* p) {
     const size_t zc = (size_t)p->R * pl.NS * p->k * sizeof(float);
     pl.setp_off = pl.zc_off + ((zc + 255) & ~(size_t)255);
     const int rows = p->R * p->B;
-    int parts = (512 + rows - 1) / rows;
+    // about 2048 workgroups for stage 1 (a 1024-row batch scanned whole rows per workgroup
+    // at a quarter of the chip's bandwidth)
+    int parts = (2048 + rows - 1) / rows;
     pl.P = parts < 1 ? 1 : (parts > 32 ? 32 : parts);
     pl.total = pl.setp_off + (((size_t)rows * pl.P * kMaxK * sizeof(uint64_t) + 255) & ~(size_t)255);
     return pl;
@@ -532,6 +733,7 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
     a.SP = pl.SP;
     a.T = pl.T;
     a.logits_bf16 = p->logits_dtype == DT_BF16;
+    a.lvec = a.logits_bf16 && (p->V & 7) == 0 && ((uintptr_t)L & 15) == 0;
     for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
     k_flash_sets<<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();

@@ -68,9 +68,25 @@ __device__ __forceinline__ void flash_state(const FlashArgs& a, int req, int s, 
 // 8 packed (logit, token) entries goes to the workspace and a second kernel merges a row's P
 // lists.  An entry enters a thread's list only if it beats the list's last entry (one
 // compare for almost every element once the list is warm).
-__device__ __forceinline__ void flash_offer(TopK<kMaxK>& top, float v, int c) {
+__device__ __forceinline__ void flash_offer(TopK<kMaxK>& top, float v, int c, uint64_t bound = 0) {
     const uint64_t e = pack_entry(v, c);
-    if (e > top.k[kMaxK - 1]) top.push(e, 0.0f);
+    const uint64_t kth = top.k[kMaxK - 1];
+    if (e > (kth > bound ? kth : bound)) top.push(e, 0.0f);
+}
+
+// The largest last entry of the wavefront's lists: a lane whose list ends there holds
+// kMaxK entries at least as large, so no element below it can reach the part's top kMaxK
+// (entries are unique: each packs its own token).  Offering against it keeps the lanes of a
+// wavefront from taking the insertion branch in turn once their lists are warm.
+__device__ __forceinline__ uint64_t flash_wave_bound(const TopK<kMaxK>& top) {
+    uint64_t k = top.k[kMaxK - 1];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, off), hi = __shfl_xor((uint32_t)(k >> 32), off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    return k;
 }
 
 __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
@@ -84,27 +100,46 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
         const uint4* p = (const uint4*)((const uint16_t*)a.L + base);
         const int ng = a.V / 8;
         const int g_beg = (int)((long)part * ng / a.P), g_end = (int)((long)(part + 1) * ng / a.P);
-        // four 16-byte loads in flight per thread (groups past the part reload its first)
+        // four 16-byte loads in flight per thread (groups past the part reload its first);
+        // the trip count is the same for every lane (the bound is a wavefront reduction)
         constexpr int kU = 4;
-        for (int g0 = g_beg + tid; g0 < g_end; g0 += kU * kFlashSetThreads) {
+        uint64_t bound = 0;
+        for (int gb = g_beg; gb < g_end; gb += kU * kFlashSetThreads) {
+            const int g0 = gb + tid;
             uint4 w[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int g = g0 + u * kFlashSetThreads;
-                w[u] = p[g < g_end ? g : g0];
+                w[u] = p[g < g_end ? g : g_beg];
             }
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int g = g0 + u * kFlashSetThreads;
-                if (g < g_end) {
-                    const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                // the group's eight entries, a mask of those above the bound, then one
+                // insertion per candidate (rare once the lists are warm)
+                const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                uint64_t e[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        flash_offer(top, bf16_lo(x[i]), 8 * g + 2 * i);
-                        flash_offer(top, bf16_hi(x[i]), 8 * g + 2 * i + 1);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    e[2 * i] = pack_entry(bf16_lo(x[i]), 8 * g + 2 * i);
+                    e[2 * i + 1] = pack_entry(bf16_hi(x[i]), 8 * g + 2 * i + 1);
+                }
+                const uint64_t kth = top.k[kMaxK - 1];
+                const uint64_t thr = kth > bound ? kth : bound;
+                uint32_t m = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) m |= (e[i] > thr) ? (1u << i) : 0u;
+                m = g < g_end ? m : 0u;
+                while (m != 0u) {
+                    const int i = __builtin_ctz(m);
+                    m &= m - 1u;
+                    uint64_t v = e[0];
+#pragma unroll
+                    for (int q = 1; q < 8; ++q) v = q == i ? e[q] : v;
+                    if (v > top.k[kMaxK - 1]) top.push(v, 0.0f);
                 }
             }
+            bound = flash_wave_bound(top);
         }
     } else {
         const int c_beg = (int)((long)part * a.V / a.P), c_end = (int)((long)(part + 1) * a.V / a.P);

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(64) void k_flash_sets_merge(FlashArgs a) {
 // takes the split's blocks w, w + 4, ...; the next block's W fragments and logits are loaded
 // while the current block's epilogue runs.
 constexpr int kFlashLseWaves = 4;
+constexpr int kFlashTile = 128;  // states per workgroup of the bf16 state pass (4 MFMA row blocks)
 static_assert(kFlashLseWaves * 64 == 256, "k_flash_lse runs 256 threads");
 
 // Raw bf16 block logits of a lane's 16 columns (c0 + 8j + 4h + i), 16-byte-aligned rows only.
@@ -265,11 +266,11 @@ __device__ __forceinline__ void flash_epi(const FlashArgs& a, f32x16& z, int c0,
 }
 
 __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
-    __shared__ __align__(16) uint16_t sA[kTileRows * kAStride];
-    __shared__ int sTok[kTileRows];
-    __shared__ size_t sLb[kTileRows];
-    __shared__ int sTgt[kTileRows][kMaxK];
-    __shared__ Lse2 sW[kFlashLseWaves][kTileRows];
+    __shared__ __align__(16) uint16_t sA[kFlashTile * kAStride];
+    __shared__ int sTok[kFlashTile];
+    __shared__ size_t sLb[kFlashTile];
+    __shared__ int sTgt[kFlashTile][kMaxK];
+    __shared__ Lse2 sW[kFlashLseWaves][kFlashTile];
     const int b = blockIdx.x;
     const int idx = b >> 3;
     const int tile = idx % a.T;
@@ -277,9 +278,9 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
     if (split >= a.SP) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, p0 = lane & 31;
     const int rows_total = a.R * a.NS;
-    const int g0 = tile * kTileRows;
-    const int nrows = min(kTileRows, rows_total - g0);
-    if (tid < kTileRows) {
+    const int g0 = tile * kFlashTile;
+    const int nrows = min(kFlashTile, rows_total - g0);
+    if (tid < kFlashTile) {
         int t = -1;
         size_t lb = 0;
         for (int i = 0; i < kMaxK; ++i) sTgt[tid][i] = -1;
@@ -294,50 +295,81 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
         sLb[tid] = lb;
     }
     __syncthreads();
-    load_a_tile<true>(a.U, a.r, nrows, [&](int row) { return sTok[row]; }, sA, nullptr);
+    // the U rows of the tile's states, in two 64-row halves
+    load_a_tile<true>(a.U, a.r, min(nrows, kTileRows), [&](int row) { return sTok[row]; }, sA, nullptr);
+    load_a_tile<true>(a.U, a.r, max(nrows - kTileRows, 0), [&](int row) { return sTok[kTileRows + row]; },
+                      sA + kTileRows * kAStride, nullptr);
     __syncthreads();
     const int NB = (a.V + kBlockCols - 1) / kBlockCols;
     const int b_beg = (int)((long)split * NB / a.SP), b_end = (int)((long)(split + 1) * NB / a.SP);
-    const bool two = nrows > 32;
-    const bool live0 = p0 < nrows, live1 = 32 + p0 < nrows;
-    const size_t lb0 = sLb[p0], lb1 = sLb[32 + p0];
-    const size_t zr0 = (size_t)(g0 + p0) * a.M, zr1 = (size_t)(g0 + 32 + p0) * a.M;
-    Lse2 s0, s1;
-    s0.init();
-    s1.init();
+    // row block q (32 states: q * 32 + lane % 32) is live when the tile reaches it
+    const int nq = (nrows + 31) >> 5;
+    size_t lbq[4], zrq[4];
+    bool liveq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int row = 32 * q + p0;
+        lbq[q] = sLb[row];
+        zrq[q] = (size_t)(g0 + row) * a.M;
+        liveq[q] = row < nrows;
+    }
+    Lse2 st[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) st[q].init();
+    // per block: row blocks 0-1, then 2-3 on the same W fragments (one accumulator pair
+    // live at a time); the logits of the next pair and the next block are in flight while
+    // the current pair's epilogue runs
     bf16x8 wf[16];
-    uint2 n0[4], n1[4];
+    uint2 la[2][4], lc[2][4];  // logits of row blocks 0-1 (this block), of 2-3
     int blk = b_beg + wave;
     if (blk < b_end) {
         load_wfrag(a.Wt, a.V, a.r, blk * kBlockCols, wf);
         if (a.lvec) {
-            flash_lgroups(a, lb0, blk * kBlockCols, h, n0);
-            if (two) flash_lgroups(a, lb1, blk * kBlockCols, h, n1);
+            flash_lgroups(a, lbq[0], blk * kBlockCols, h, la[0]);
+            if (nq > 1) flash_lgroups(a, lbq[1], blk * kBlockCols, h, la[1]);
         }
     }
     for (; blk < b_end; blk += kFlashLseWaves) {
         const int c0 = blk * kBlockCols;
         f32x16 acc0, acc1;
-        flash_to_acc(a, n0, lb0, c0, h, acc0);
-        if (two) flash_to_acc(a, n1, lb1, c0, h, acc1);
-        mma_wfrag(wf, two, sA, acc0, acc1);
-        if (blk + kFlashLseWaves < b_end) {
-            const int cn = c0 + kFlashLseWaves * kBlockCols;
+        flash_to_acc(a, la[0], lbq[0], c0, h, acc0);
+        if (nq > 1) flash_to_acc(a, la[1], lbq[1], c0, h, acc1);
+        mma_wfrag(wf, nq > 1, sA, acc0, acc1);
+        if (nq > 2 && a.lvec) {
+            flash_lgroups(a, lbq[2], c0, h, lc[0]);
+            if (nq > 3) flash_lgroups(a, lbq[3], c0, h, lc[1]);
+        }
+        const bool more = blk + kFlashLseWaves < b_end;
+        const int cn = c0 + kFlashLseWaves * kBlockCols;
+        if (nq <= 2 && more) {
             load_wfrag(a.Wt, a.V, a.r, cn, wf);
             if (a.lvec) {
-                flash_lgroups(a, lb0, cn, h, n0);
-                if (two) flash_lgroups(a, lb1, cn, h, n1);
+                flash_lgroups(a, lbq[0], cn, h, la[0]);
+                if (nq > 1) flash_lgroups(a, lbq[1], cn, h, la[1]);
             }
         }
-        if (live0) flash_epi(a, acc0, c0, h, sTgt[p0], zr0, s0);
-        if (two && live1) flash_epi(a, acc1, c0, h, sTgt[32 + p0], zr1, s1);
+        if (liveq[0]) flash_epi(a, acc0, c0, h, sTgt[p0], zrq[0], st[0]);
+        if (nq > 1 && liveq[1]) flash_epi(a, acc1, c0, h, sTgt[32 + p0], zrq[1], st[1]);
+        if (nq > 2) {
+            flash_to_acc(a, lc[0], lbq[2], c0, h, acc0);
+            if (nq > 3) flash_to_acc(a, lc[1], lbq[3], c0, h, acc1);
+            mma_wfrag(wf, nq > 3, sA + kTileRows * kAStride, acc0, acc1);
+            if (more) {
+                load_wfrag(a.Wt, a.V, a.r, cn, wf);
+                if (a.lvec) {
+                    flash_lgroups(a, lbq[0], cn, h, la[0]);
+                    flash_lgroups(a, lbq[1], cn, h, la[1]);
+                }
+            }
+            if (liveq[2]) flash_epi(a, acc0, c0, h, sTgt[64 + p0], zrq[2], st[2]);
+            if (nq > 3 && liveq[3]) flash_epi(a, acc1, c0, h, sTgt[96 + p0], zrq[3], st[3]);
+        }
     }
     // lanes l and l ^ 32 hold the same state; then the wavefronts' blocks
-    s0.merge_xor(32);
-    s1.merge_xor(32);
-    if (h == 0) {
-        sW[wave][p0] = s0;
-        sW[wave][32 + p0] = s1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        st[q].merge_xor(32);
+        if (h == 0) sW[wave][32 * q + p0] = st[q];
     }
     __syncthreads();
     if (tid < nrows) {
@@ -719,7 +751,9 @@ FlashPlan flash_plan(const dt_params* p) {
     FlashPlan pl{};
     pl.M = p->k;
     pl.NS = 1 + (p->B - 1) * p->k;
-    pl.T = (p->R * pl.NS + kTileRows - 1) / kTileRows;
+    // state tiles: 128 states for bf16 heads (k_flash_lse's transposed blocks), 64 for float32
+    const int tile = p->head_dtype == DT_BF16 ? kFlashTile : kTileRows;
+    pl.T = (p->R * pl.NS + tile - 1) / tile;
     const int chunks = (p->V + kChunkCols - 1) / kChunkCols;
     // about 512 workgroups, and a multiple of 8 splits so that every XCD takes the same
     // number (workgroup b runs on XCD b % 8; with 9 splits one XCD did twice the work)

@@ -28,7 +28,8 @@ Layout make_layout(const dt_params* p, bool allow_resident) {
     L.G = kMaxGrid;
     const size_t tmax = (R * N + kTileRows - 1) / kTileRows;
     // records: (parent row, vocabulary split) pairs; a level of T row groups of g rows uses
-    // at most g * max(G, T) of them (g = kTileRows in tile mode, kGroupRows in group mode)
+    // at most g * max(G, T) of them (g = kTileRows in tile mode, kGroupRows in group mode),
+    // because splits_for() keeps S <= max(1, G / T): more splits would write past this region
     size_t cap_rows = (size_t)kGroupRows * (tmax > (size_t)L.G ? tmax : (size_t)L.G);
     // the W-resident kernel writes one record per parent row and workgroup
     L.resident = allow_resident && resident_params_ok(p);

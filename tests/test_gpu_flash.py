@@ -3,7 +3,8 @@ or_build_flash, element by element on margin-certified inputs: token sets, topol
 tokens, masks, candidate rows, status, survival bits exactly; logq within 1e-5 relative.
 
 Cases: small float32 instances (several M, B, N, tau, calibration plateaus, several
-requests, a bad root and a clamped budget) and the full-vocabulary bf16 workloads (B = 7,
+requests, a bad root and a clamped budget), small bf16 instances (several state tiles,
+vocabularies that are not a multiple of 8, r < 256) and the full-vocabulary bf16 workloads (B = 7,
 N = 32; B = 16, N = 64; the 64-request batch at tau = 0 and 0.05), each with the plain and
 the strong head, every request compared.
 """
@@ -70,6 +71,22 @@ def test_flash_small(B, kw, table):
     inst = instance("tiny", strong=True, **kw)
     if table == "plateau":
         inst.cal = np.array([0.25] * 4 + [0.5] * 4 + [0.75] * 4 + [1.0] * 4, np.float32)
+    _case(B, inst, margin=STRESS_MARGIN)
+
+
+# bfloat16 heads at small V: the state pass's transposed blocks with several 128-state tiles
+# (a partial last tile of 1, 2 or 3 row blocks), vocabularies that are not a multiple of 8
+# (logits read one value at a time) or end in a partial 32-column block, and r < 256.
+SMALL_BF16 = [
+    dict(seed=21, V=130, r=16, B=8, k=4, Ncap=24, R=5, dtype="bf16"),
+    dict(seed=22, V=200, r=32, B=6, k=3, Ncap=16, R=11, dtype="bf16"),
+    dict(seed=23, V=1000, r=64, B=4, k=2, Ncap=12, R=40, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL_BF16, ids=[str(i) for i in range(len(SMALL_BF16))])
+def test_flash_small_bf16(B, kw):
+    inst = instance("tiny", strong=True, tau=0.0, **kw)
     _case(B, inst, margin=STRESS_MARGIN)
 
 

@@ -70,6 +70,21 @@ def test_sample_small(rt, cfg):
     _sample_case(rt, inst, margin=STRESS_MARGIN)
 
 
+# Vocabularies above what the rejection chain keeps in registers (16 slices of 12288 words):
+# every slice also streams its last groups from memory at each pass; one vocabulary a
+# multiple of 8 (16-byte loads), one not.
+LARGE_V = [
+    dict(seed=15, V=200003, r=16, B=3, k=2, Ncap=6, R=2, dtype="bf16", temperature=1.0),
+    dict(seed=16, V=204800, r=16, B=3, k=3, Ncap=8, R=3, dtype="bf16", temperature=0.8),
+]
+
+
+@pytest.mark.parametrize("cfg", LARGE_V, ids=lambda c: "V%d" % c["V"])
+def test_sample_large_vocabulary(rt, cfg):
+    inst = instance("tiny", strong=True, cal="monotone", rho=0.7, mode="sample", **cfg)
+    _sample_case(rt, inst, margin=STRESS_MARGIN)
+
+
 @pytest.mark.parametrize("T", [0.6, 1.0, 1.5])
 def test_sample_config(rt, T):
     """Lossless sampling workload: 32 requests, B=16, k=4, N=64, V=151936, rho=0.7; every

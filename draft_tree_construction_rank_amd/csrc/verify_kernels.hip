@@ -409,6 +409,195 @@ __global__ __launch_bounds__(256) void k_vs_rows(const VsArgs a) {
     }
 }
 
+// bf16 head and logits, V a multiple of 8, 16-byte aligned rows: the draft rows on the
+// expansion's transposed block (W as the MFMA A operand straight from memory, the walking
+// requests' U rows from LDS as B, the block logits as the accumulators' initial values), so
+// that lane l holds request m0 + 32q + l % 32 at 16 columns of each 32-column block; the
+// draft row is stored and both online log-sum-exps run on those registers.  A workgroup
+// takes up to 64 requests (two row blocks) over one vocabulary split, its four wavefronts
+// the split's blocks w, w + 4, ...; the next block's W fragments, block logits and target
+// logits are in flight while the current block's epilogue runs.  Workgroup b runs on XCD
+// b % 8 and takes split (b / 8 / T) * 8 + b % 8 of tile (b / 8) % T.
+constexpr int kVsTile = 64;
+constexpr int kVsRowWaves = 4;
+
+// Four groups of 4 bf16 of a row at the lane's columns c0 + 8j + 4h (clamped into the row
+// past V; those columns are masked by the epilogue).
+__device__ __forceinline__ void vs_row_words(const VsArgs& a, const void* base, size_t rb, int c0,
+                                             int h, uint2 (&g)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = c0 + 8 * j + 4 * h;
+        g[j] = *(const uint2*)((const uint16_t*)base + rb + (c < a.V ? c : a.V - 4));
+    }
+}
+
+// z = L + U.W of one request at the lane's 16 columns and tg its target words there: stores
+// the draft row and folds both rows into the online log-sum-exps (log2 units).
+__device__ __forceinline__ void vs_row_epi(const VsArgs& a, const f32x16& z, const uint2 (&tg)[4],
+                                           int c0, int h, float* vr, Lse2& lq, Lse2& lp) {
+    const bool full = c0 + kBlockCols <= a.V;
+    float yq[16], yp[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float t4[4] = {bf16_lo(tg[j].x), bf16_hi(tg[j].x), bf16_lo(tg[j].y), bf16_hi(tg[j].y)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool in = full || c0 + 8 * j + 4 * h + i < a.V;
+            yq[4 * j + i] = in ? z[4 * j + i] * a.y2scale : -INFINITY;
+            yp[4 * j + i] = in ? t4[i] * a.y2scale : -INFINITY;
+        }
+        const int c = c0 + 8 * j + 4 * h;
+        if (full) {
+            *(float4*)(vr + c) = make_float4(yq[4 * j], yq[4 * j + 1], yq[4 * j + 2], yq[4 * j + 3]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (c + i < a.V) vr[c + i] = yq[4 * j + i];
+        }
+    }
+    float mq = yq[0], mp = yp[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) {
+        mq = fmaxf(mq, yq[e]);
+        mp = fmaxf(mp, yp[e]);
+    }
+    float sq = 0.0f, sp = 0.0f;
+    if (mq != -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            sq += exp2f(yq[e] - mq);
+            sp += exp2f(yp[e] - mp);
+        }
+        lq.merge(mq, sq);
+        lp.merge(mp, sp);
+    }
+}
+
+__global__ __launch_bounds__(kVsRowWaves * 64) void k_vs_rows_blocks(const VsArgs a) {
+    __shared__ __align__(16) uint16_t sA[kVsTile * kAStride];
+    __shared__ int sTok[kVsTile];
+    static_assert(kVsTile == kTileRows, "one A tile of two 32-row blocks");
+    __shared__ size_t sLb[kVsTile], sTb[kVsTile];
+    __shared__ int sLive[kVsTile];
+    __shared__ Lse2 sW[2][kVsRowWaves][kVsTile];
+    __shared__ int sAny;
+    const int T = (a.R + kVsTile - 1) / kVsTile;
+    const int b = blockIdx.x, idx = b >> 3;
+    const int tile = idx % T, split = (idx / T) * 8 + (b & 7);
+    if (split >= a.S) return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, p0 = lane & 31;
+    const int m0 = tile * kVsTile;
+    const int nrows = min(kVsTile, a.R - m0);
+    if (tid == 0) sAny = 0;
+    __syncthreads();
+    if (tid < kVsTile) {
+        int live = 0, tok = -1;
+        size_t lb = 0, tb = 0;
+        if (tid < nrows) {
+            const VState s = a.state[m0 + tid];
+            live = s.active && s.depth < a.B;
+            if (live) {
+                const int req = m0 + tid;
+                tok = (uint32_t)s.token < (uint32_t)a.V ? s.token : 0;  // never index U out of range
+                lb = ((size_t)req * a.B + s.depth) * (size_t)a.V;
+                tb = ((size_t)req * (a.Ncap + 1) + s.row) * (size_t)a.V;
+            }
+        }
+        sLive[tid] = live;
+        sTok[tid] = tok;
+        sLb[tid] = lb;
+        sTb[tid] = tb;
+        if (live) atomicOr(&sAny, 1);
+    }
+    __syncthreads();
+    if (!sAny) return;
+    load_a_tile<true>(a.U, a.r, nrows, [&](int row) { return sTok[row]; }, sA, nullptr);
+    __syncthreads();
+    const int NB = (a.V + kBlockCols - 1) / kBlockCols;
+    const int b_beg = (int)((long)split * NB / a.S), b_end = (int)((long)(split + 1) * NB / a.S);
+    const int nq = (nrows + 31) >> 5;
+    Lse2 lq[2], lp[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        lq[q].init();
+        lp[q].init();
+    }
+    // the tile's block and target logits are loaded with the block's W fragments, one block
+    // ahead
+    bf16x8 wf[16];
+    uint2 nl[2][4], nt[2][4];
+    const size_t la0 = sLb[p0], la1 = sLb[32 + p0], ta0 = sTb[p0], ta1 = sTb[32 + p0];
+    auto prefetch = [&](int c0) {
+        load_wfrag(a.Wt, a.V, a.r, c0, wf);
+        vs_row_words(a, a.L, la0, c0, h, nl[0]);
+        vs_row_words(a, a.target, ta0, c0, h, nt[0]);
+        if (nq > 1) {
+            vs_row_words(a, a.L, la1, c0, h, nl[1]);
+            vs_row_words(a, a.target, ta1, c0, h, nt[1]);
+        }
+    };
+    auto to_acc = [&](const uint2 (&g)[4], f32x16& acc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[4 * j + 0] = bf16_lo(g[j].x);
+            acc[4 * j + 1] = bf16_hi(g[j].x);
+            acc[4 * j + 2] = bf16_lo(g[j].y);
+            acc[4 * j + 3] = bf16_hi(g[j].y);
+        }
+    };
+    int blk = b_beg + wave;
+    if (blk < b_end) prefetch(blk * kBlockCols);
+    for (; blk < b_end; blk += kVsRowWaves) {
+        const int c0 = blk * kBlockCols;
+        const bool more = blk + kVsRowWaves < b_end;
+        {
+            const bool two = nq > 1;
+            f32x16 acc0, acc1;
+            uint2 t0[4], t1[4];  // this block's target words (nt is refilled for the next)
+            to_acc(nl[0], acc0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t0[j] = nt[0][j];
+            if (two) {
+                to_acc(nl[1], acc1);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t1[j] = nt[1][j];
+            }
+            mma_wfrag(wf, two, sA, acc0, acc1);
+            if (more) prefetch(c0 + kVsRowWaves * kBlockCols);
+            if (sLive[p0]) vs_row_epi(a, acc0, t0, c0, h, a.vrow + (size_t)(m0 + p0) * a.V, lq[0], lp[0]);
+            if (two && sLive[32 + p0])
+                vs_row_epi(a, acc1, t1, c0, h, a.vrow + (size_t)(m0 + 32 + p0) * a.V, lq[1], lp[1]);
+        }
+    }
+    // lanes l and l ^ 32 hold the same request; then the wavefronts' blocks
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        lq[q].merge_xor(32);
+        lp[q].merge_xor(32);
+        if (h == 0) {
+            sW[0][wave][32 * q + p0] = lq[q];
+            sW[1][wave][32 * q + p0] = lp[q];
+        }
+    }
+    __syncthreads();
+    if (tid < nrows && sLive[tid]) {
+        Lse2 tq, tp;
+        tq.init();
+        tp.init();
+#pragma unroll
+        for (int w = 0; w < kVsRowWaves; ++w) {
+            tq.merge(sW[0][w][tid].m, sW[0][w][tid].s);
+            tp.merge(sW[1][w][tid].m, sW[1][w][tid].s);
+        }
+        float* rec = a.vpart + ((size_t)(m0 + tid) * a.S + split) * 4;
+        rec[0] = tq.m;
+        rec[1] = tq.s;
+        rec[2] = tp.m;
+        rec[3] = tp.s;
+    }
+}
+
 // Block-wide float sum in a fixed order (deterministic); every thread gets the total.
 __device__ float block_sum_f(float v, float* sh) {
     const int tid = threadIdx.x, nw = blockDim.x >> 6;
@@ -841,13 +1030,30 @@ hipError_t launch_verify_sample(const dt_params* p, const Layout& lay, char* ws,
     ca.spin_limit = kSpinLimit;
     ca.bf16 = va.bf16;
     ca.vec = va.vec;
-    const int tiles = (p->R + kTileRows - 1) / kTileRows;
-    const dim3 grid(tiles * lay.vsplits);
+    // bf16 head and 16-byte-ready logits: the transposed-block rows pass over 64-request
+    // tiles and a multiple of 8 splits (about 512 workgroups; never more splits than the
+    // partial records hold); otherwise the LDS-tile pass
+    const bool blocks = p->head_dtype == DT_BF16 && va.vec;
+    dim3 grid;
+    if (blocks) {
+        const int tiles = (p->R + kVsTile - 1) / kVsTile;
+        const int NB = (p->V + kBlockCols - 1) / kBlockCols;
+        int sp = (512 / tiles) & ~7;
+        sp = sp < 8 ? 8 : sp;
+        sp = sp > lay.vsplits ? lay.vsplits : sp;
+        sp = sp > NB ? NB : sp;
+        va.S = ca.S = sp;
+        grid = dim3(tiles * ((sp + 7) / 8) * 8);
+    } else {
+        grid = dim3(((p->R + kTileRows - 1) / kTileRows) * lay.vsplits);
+    }
     for (int step = 0; step <= p->B; ++step) {
         va.state = state + (size_t)(step & 1) * p->R;
         ca.state = va.state;
         ca.next = state + (size_t)((step + 1) & 1) * p->R;
-        if (p->head_dtype == DT_BF16)
+        if (blocks)
+            hipLaunchKernelGGL(k_vs_rows_blocks, grid, dim3(kVsRowWaves * 64), 0, st, va);
+        else if (p->head_dtype == DT_BF16)
             hipLaunchKernelGGL(k_vs_rows<true>, grid, dim3(256), 0, st, va);
         else
             hipLaunchKernelGGL(k_vs_rows<false>, grid, dim3(256), 0, st, va);

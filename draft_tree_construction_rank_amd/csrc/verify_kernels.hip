@@ -222,9 +222,10 @@ hipError_t launch_verify_greedy(const dt_params* p, const Layout& lay, char* ws,
 // =======================================================================================
 // Lossless sample verify (TreeSpark lossless section).  The requests walk in lock-step,
 // one node per step; a step is two launches:
-//   k_vs_rows  - for every request still walking at a node of depth < B: the node's draft
-//                row y_q = (L[d] + U[t] . Wt) * log2(e)/T on MFMA (same tile as expansion),
-//                stored to vrow, plus per-split (max, sum) of y_q and of the target row;
+//   k_vs_rows_blocks (k_vs_rows for float32 heads or logits) - for every request still
+//                walking at a node of depth < B: the node's draft row
+//                y_q = (L[d] + U[t] . Wt) * log2(e)/T on MFMA, stored to vrow, plus per-split
+//                (max, sum) of y_q and of the target row;
 //   k_vs_split - the rejection chain, each request on SC workgroups that split the
 //                vocabulary: every workgroup of a request takes the same decisions (they
 //                depend only on values every workgroup computes identically), and each

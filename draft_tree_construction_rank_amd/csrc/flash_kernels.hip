@@ -490,37 +490,162 @@ __global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
 
 // ---- final selection and emission ------------------------------------------------------------
 struct FlashSel {
+    // the select pool's keys: kept nodes, then the level's surviving candidates (room for a
+    // masked read of eight keys past the end)
+    alignas(16) uint64_t pkey[kFlashPool + 8];
+    alignas(16) uint64_t kkey[2][kMaxNcap];  // kept nodes by key desc (two buffers: one level's
+                                             // input and output)
+    // the candidates of a level kept at its end, as bits over their index w = (parent's
+    // frontier index) M + sibling rank, which is their canonical order (by level parity)
+    alignas(16) uint64_t cbits[2][kMaxNcap * kMaxK / 64];
+    int16_t wpos[kMaxNcap * kMaxK];  // candidate index -> kept index at the end of its level
+    int32_t ktok[2][kMaxNcap];
+    int16_t kstate[2][kMaxNcap];  // the node's own state (-1 at depth B)
+    int16_t kfi[2][kMaxNcap];     // its index in the frontier of the level after its own
+    float klogq[2][kMaxNcap];
+    // the level's surviving candidates, in pool order after the kept nodes
+    int32_t ctok[kMaxNcap * kMaxK];
+    int16_t cstate[kMaxNcap * kMaxK];
+    float clogq[kMaxNcap * kMaxK];
     int32_t set[kMaxB][kMaxK];
+    float cal[16];
     float lse2[kFlashMaxStates];
     uint8_t rslot[kFlashMaxStates][kMaxK];  // children of a state in sibling order: slots of S_j
     float cy2[kFlashMaxStates][kMaxK];      // their conditional logits (log2 units)
-    // the select pool: kept nodes first, then one level's candidates
-    uint64_t pkey[kFlashPool];
-    int32_t ptok[kFlashPool];
-    int16_t pstate[kFlashPool];  // the node's own state (-1 at depth B)
-    int16_t pfi[kFlashPool];     // its index in the frontier of the level after its own
-    float plogq[kFlashPool];
-    // kept nodes, sorted by key descending
-    uint64_t kkey[kMaxNcap];
-    int32_t ktok[kMaxNcap];
-    int16_t kstate[kMaxNcap];
-    int16_t kfi[kMaxNcap];
-    float klogq[kMaxNcap];
-    int16_t front[kMaxNcap];  // frontier index -> kept index
-    int16_t canon[kMaxNcap];  // kept index -> canonical position
-    int16_t korder[kMaxNcap]; // canonical position -> kept index
-    int16_t cpar[kMaxNcap];   // canonical position -> parent's canonical position
-    uint64_t mask[kMaxNcap];  // canonical position -> ancestor mask
-    int nkept, nfront, nvalid;
+    float zraw[kFlashMaxStates * kMaxK];    // the same in set order, as the state pass wrote them
+    int16_t pmap[kMaxB + 1][kMaxNcap];  // (depth, frontier index) -> canonical position
+    int16_t korder[kMaxNcap];           // canonical position -> kept index
+    int16_t cpar[kMaxNcap];             // canonical position -> parent's canonical position
+    uint64_t mask[kMaxNcap];            // canonical position -> ancestor mask
+    int ncand[2];                       // surviving candidates of a level (by level parity)
 };
+
+constexpr int kFlashBitWords = kMaxNcap * kMaxK / 64;
+constexpr int kFlashZPer = (kFlashMaxStates * kMaxK + kFlashSelThreads - 1) / kFlashSelThreads;
+
+// Set bits of the candidate bitmap below index w.
+__device__ __forceinline__ int bits_below(const uint64_t (&bm)[kFlashBitWords], int w) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kFlashBitWords; ++q) {
+        const uint64_t m = q < (w >> 6) ? bm[q] : q == (w >> 6) ? bm[q] & ((1ull << (w & 63)) - 1ull) : 0ull;
+        c += __popcll(m);
+    }
+    return c;
+}
+
+// Position of the n-th (from 0) set bit of m; m has more than n set bits.
+__device__ __forceinline__ int nth_bit(uint64_t m, int n) {
+    int pos = 0;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) {
+        const int c = __popcll(m & ((1ull << s) - 1ull));
+        if (n >= c) {
+            n -= c;
+            m >>= s;
+            pos += s;
+        }
+    }
+    return pos;
+}
+
+// Ranks of NO keys of this thread in the pool (number of larger pool keys): eight keys per
+// step as four 16-byte LDS reads in flight, then the last fewer than eight masked by index.
+template <int NO>
+__device__ __forceinline__ void flash_rank(const uint64_t* pkey, int np, const uint64_t (&k)[NO],
+                                           int (&r)[NO]) {
+    const ulonglong2* p2 = (const ulonglong2*)pkey;
+    const int n8 = np & ~7;
+    for (int f = 0; f < n8 / 2; f += 4) {
+        ulonglong2 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = p2[f + u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int o = 0; o < NO; ++o) r[o] += (int)(x[u].x > k[o]) + (int)(x[u].y > k[o]);
+    }
+    ulonglong2 x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = p2[n8 / 2 + u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int o = 0; o < NO; ++o)
+            r[o] += (int)(n8 + 2 * u < np && x[u].x > k[o]) + (int)(n8 + 2 * u + 1 < np && x[u].y > k[o]);
+}
+
+// Position of the n-th (from 0) set bit of the candidate bitmap; it has more than n.
+__device__ __forceinline__ int nth_bit_map(const uint64_t (&bm)[kFlashBitWords], int n) {
+    int word = -1;
+    uint64_t sel = 0;
+#pragma unroll
+    for (int q = 0; q < kFlashBitWords; ++q) {
+        const int c = __popcll(bm[q]);
+        if (word < 0) {
+            if (n < c) {
+                word = q;
+                sel = bm[q];
+            } else {
+                n -= c;
+            }
+        }
+    }
+    return 64 * word + nth_bit(sel, n);
+}
+
+// Scatter of this thread's pool entries e = tid + 256 o that rank inside the budget into the
+// output buffer of kept nodes.  A kept node of depth d - 1 takes its frontier index (its
+// position in the level's frontier, which is in candidate-index order); a kept candidate
+// starts with none and marks its index in the level's bitmap.
+template <int NO>
+__device__ __forceinline__ void flash_keep(FlashSel& sm, int cur, int nk, int np, int nb, int d,
+                                           int M, const uint64_t (&bm)[kFlashBitWords], int tid) {
+    uint64_t k[NO];
+    int r[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+        const int e = tid + o * kFlashSelThreads;
+        k[o] = e < np ? sm.pkey[e] : ~0ull;
+        r[o] = 0;
+    }
+    flash_rank<NO>(sm.pkey, np, k, r);
+    const int nxt = cur ^ 1;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+        const int e = tid + o * kFlashSelThreads;
+        if (e >= np || r[o] >= nb) continue;
+        const int rk = r[o];
+        sm.kkey[nxt][rk] = k[o];
+        const uint32_t lo = (uint32_t)k[o];
+        const int w = low_fi(lo) * M + low_rank(lo);  // the node's index among its level's candidates
+        if (e < nk) {
+            const bool fr = low_depth(lo) == d - 1;
+            sm.ktok[nxt][rk] = sm.ktok[cur][e];
+            sm.kstate[nxt][rk] = sm.kstate[cur][e];
+            sm.kfi[nxt][rk] = fr ? (int16_t)bits_below(bm, w) : sm.kfi[cur][e];
+            sm.klogq[nxt][rk] = sm.klogq[cur][e];
+        } else {
+            const int c = e - nk;
+            sm.ktok[nxt][rk] = sm.ctok[c];
+            sm.kstate[nxt][rk] = sm.cstate[c];
+            sm.kfi[nxt][rk] = 0;
+            sm.klogq[nxt][rk] = sm.clogq[c];
+            atomicOr((unsigned long long*)&sm.cbits[d & 1][w >> 6], 1ull << (w & 63));
+            sm.wpos[w] = (int16_t)rk;
+        }
+    }
+}
 
 // One workgroup per request.  Reading of the final selection: the parent-conditioned tree's
 // rule (survival from the calibration table, s < tau dropped, global order survival desc,
 // depth asc, sibling-rank path asc, budget N) applied level by level; because survival
-// never increases along a path this equals best-first over the lattice.
+// never increases along a path this equals best-first over the lattice.  A candidate below
+// the last of N kept keys cannot enter (N larger keys exist), so only the others join the
+// level's pool.
 __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) {
     __shared__ FlashSel sm;
-    const int req = blockIdx.x, tid = threadIdx.x;
+    const int req = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int M = a.M, B = a.B, NS = a.NS, Ncap = a.Ncap;
     const int root = a.root_token[req];
     const bool bad_root = root < 0 || root >= a.V;
@@ -532,170 +657,189 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
     }
     const float tau = a.tau[req];
     constexpr float kLn2 = 0.6931471805599453f, kLog2e = 1.4426950408889634f;
-    for (int i = tid; i < B * M; i += kFlashSelThreads)
-        sm.set[i / M][i % M] = a.sets[((size_t)req * B + i / M) * M + i % M];
-    if (tid == 0) sm.nkept = 0;
-    __syncthreads();
+    // (every load of the set-up issued before the first is used: the token sets, the raw
+    // child logits, the split records)
+    const int nzc = NS * M;
+    int sv = 0;
+    if (tid < B * M) sv = a.sets[(size_t)req * B * M + tid];
+    float zr[kFlashZPer];
+#pragma unroll
+    for (int u = 0; u < kFlashZPer; ++u) {
+        const int w = tid + u * kFlashSelThreads;
+        zr[u] = w < nzc ? a.zc[(size_t)req * nzc + w] : 0.0f;
+    }
+    if (tid < 16) sm.cal[tid] = a.cal[tid];
+    if (tid < 2) sm.ncand[tid] = 0;
+    if (tid < 2 * kFlashBitWords) sm.cbits[tid / kFlashBitWords][tid % kFlashBitWords] = 0ull;
+    int cur = 0, nk = 0;
     if (!bad_root) {
-        // log-sum-exp of every state: its splits' records combined, P threads a state
-        const int P = NS <= kFlashSelThreads / 4 ? 4 : 1;
-        for (int w = tid; w < ((NS * P + kFlashSelThreads - 1) / kFlashSelThreads) * kFlashSelThreads; w += kFlashSelThreads) {
-            const int s = w / P, part = w % P;
+        // every state's splits' log-sum-exp records combined: P threads a state, eight record
+        // pairs a step with the next step's in flight
+        int lp = 0;
+        while (lp < 4 && (NS << (lp + 1)) <= kFlashSelThreads) ++lp;
+        const int P = 1 << lp;
+        for (int w0 = 0; w0 < NS * P; w0 += kFlashSelThreads) {
+            const int w = w0 + tid, s = w >> lp, part = w & (P - 1);
             Lse2 st;
             st.init();
             if (s < NS) {
                 const float2* rec = a.lsep + (size_t)(req * NS + s) * a.SP;
-                for (int p = part * 16; p < a.SP; p += 16 * P) {
-                    float2 v[16];
+                if ((a.SP & 1) == 0) {
+                    const float4* r4 = (const float4*)rec;
+                    const int n2 = a.SP >> 1;
+                    float4 v[8];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) v[u] = p + u < a.SP ? rec[p + u] : make_float2(-INFINITY, 0.0f);
+                    for (int u = 0; u < 8; ++u) {
+                        const int p = part + u * P;
+                        v[u] = p < n2 ? r4[p] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+                    }
+                    for (int p0 = part; p0 < n2; p0 += 8 * P) {
+                        float4 nv[8];
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) st.merge(v[u].x, v[u].y);
+                        for (int u = 0; u < 8; ++u) {
+                            const int p = p0 + (8 + u) * P;
+                            nv[u] = p < n2 ? r4[p] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+                        }
+                        float mx = -INFINITY;
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) mx = fmaxf(mx, fmaxf(v[u].x, v[u].z));
+                        if (mx != -INFINITY) {
+                            float sum = 0.0f;
+#pragma unroll
+                            for (int u = 0; u < 8; ++u)
+                                sum += v[u].y * exp2f(v[u].x - mx) + v[u].w * exp2f(v[u].z - mx);
+                            st.merge(mx, sum);
+                        }
+#pragma unroll
+                        for (int u = 0; u < 8; ++u) v[u] = nv[u];
+                    }
+                } else {
+                    for (int p = part; p < a.SP; p += P) st.merge(rec[p].x, rec[p].y);
                 }
             }
-            if (P == 4) {
-                st.merge_xor(1);
-                st.merge_xor(2);
-            }
+            for (int off = 1; off < P; off <<= 1) st.merge_xor(off);
             if (s < NS && part == 0) sm.lse2[s] = st.m + log2f(st.s);
         }
-        // conditional logits of every state's children (written by the state pass)
-        for (int w = tid; w < NS * M; w += kFlashSelThreads)
-            sm.cy2[w / M][w % M] = a.zc[(size_t)(req * NS) * M + w] * kLog2e;
+        if (tid < B * M) sm.set[tid / M][tid % M] = sv;
+#pragma unroll
+        for (int u = 0; u < kFlashZPer; ++u) {
+            const int w = tid + u * kFlashSelThreads;
+            if (w < nzc) sm.zraw[w] = zr[u] == zr[u] ? zr[u] * kLog2e : -INFINITY;  // (a total order)
+        }
         __syncthreads();
-        // sibling order of every state: conditional logit desc, token asc
-        for (int s = tid; s < NS; s += kFlashSelThreads) {
+        // sibling order of every state's children: conditional logit desc, token asc (each
+        // child counts the siblings ahead of it)
+        for (int w = tid; w < nzc; w += kFlashSelThreads) {
+            const int s = w / M, i = w - s * M;
             const int j = s == 0 ? 0 : 1 + (s - 1) / M;
-            float y[kMaxK];
-            int sl[kMaxK];
-            for (int i = 0; i < M; ++i) {
-                y[i] = sm.cy2[s][i];
-                sl[i] = i;
+            const float y = sm.zraw[w];
+            const int t = sm.set[j][i];
+            int rank = 0;
+            for (int q = 0; q < M; ++q) {
+                const float yq = sm.zraw[s * M + q];
+                rank += (int)(yq > y || (yq == y && sm.set[j][q] < t));
             }
-            for (int i = 1; i < M; ++i) {
-                const float xy = y[i];
-                const int xs = sl[i];
-                int b = i - 1;
-                while (b >= 0 && (y[b] < xy || (y[b] == xy && sm.set[j][sl[b]] > sm.set[j][xs]))) {
-                    y[b + 1] = y[b];
-                    sl[b + 1] = sl[b];
-                    --b;
-                }
-                y[b + 1] = xy;
-                sl[b + 1] = xs;
-            }
-            for (int i = 0; i < M; ++i) {
-                sm.cy2[s][i] = y[i];
-                sm.rslot[s][i] = (uint8_t)sl[i];
-            }
+            sm.cy2[s][rank] = y;
+            sm.rslot[s][rank] = (uint8_t)i;
         }
         __syncthreads();
-        // level loop
-        for (int d = 1; d <= B; ++d) {
-            // frontier: the kept nodes of depth d - 1 (the root at d = 1), canonical order
-            if (d == 1) {
-                if (tid == 0) {
-                    sm.nfront = 1;
-                    sm.front[0] = -1;
-                }
-            } else {
-                const bool fr = tid < sm.nkept && low_depth((uint32_t)sm.kkey[tid]) == d - 1;
-                if (fr) {
-                    const uint32_t lo = (uint32_t)sm.kkey[tid];
-                    int fi = 0;
-                    for (int e = 0; e < sm.nkept; ++e) {
-                        const uint32_t le = (uint32_t)sm.kkey[e];
-                        fi += (low_depth(le) == d - 1) & (le > lo);
-                    }
-                    sm.kfi[tid] = (int16_t)fi;
-                    sm.front[fi] = (int16_t)tid;
-                }
-                const int nf = __syncthreads_count(fr);
-                if (tid == 0) sm.nfront = nf;
+        // level loop: the frontier (kept nodes of depth d - 1, the root at d = 1) in
+        // canonical order, its children scored, the survivors compacted behind the kept
+        // nodes, every pool entry ranked and the best nb kept
+        for (int d = 1; nb > 0 && d <= B; ++d) {
+            uint64_t bm[kFlashBitWords];
+            int nf = 1;
+#pragma unroll
+            for (int q = 0; q < kFlashBitWords; ++q) bm[q] = d > 1 ? sm.cbits[(d - 1) & 1][q] : 0ull;
+            if (d > 1) {
+                nf = 0;
+#pragma unroll
+                for (int q = 0; q < kFlashBitWords; ++q) nf += __popcll(bm[q]);
             }
-            if (tid == 0) sm.nvalid = 0;
-            __syncthreads();
-            const int nf = sm.nfront, nk = sm.nkept;
             if (nf == 0) break;
-            // pool: the kept nodes, then every frontier node's M children
-            for (int e = tid; e < nk; e += kFlashSelThreads) {
-                sm.pkey[e] = sm.kkey[e];
-                sm.ptok[e] = sm.ktok[e];
-                sm.pstate[e] = sm.kstate[e];
-                sm.pfi[e] = sm.kfi[e];
-                sm.plogq[e] = sm.klogq[e];
-            }
-            for (int w = tid; w < nf * M; w += kFlashSelThreads) {
-                const int fi = w / M, i = w % M;
-                const int ke = sm.front[fi];
-                const int ps = ke < 0 ? 0 : sm.kstate[ke];
-                const float psurv = ke < 0 ? 1.0f : key_surv(sm.kkey[ke]);
-                const float l2 = sm.cy2[ps][i] - sm.lse2[ps];
-                const float q = exp2f(l2);
-                const int bin = min(15, max(0, (int)floorf(16.0f * q)));
-                const float sv = psurv * a.cal[bin];
-                const int slot = sm.rslot[ps][i];
-                const int e = nk + w;
-                sm.pkey[e] = sv < tau ? 0ull : make_key(sv, d, fi, i);
-                sm.ptok[e] = sm.set[d - 1][slot];
-                sm.pstate[e] = (int16_t)(d < B ? 1 + (d - 1) * M + slot : -1);
-                sm.pfi[e] = 0;
-                sm.plogq[e] = l2 * kLn2;
-            }
-            __syncthreads();
-            // keep the nb best: rank = number of larger keys (valid keys are distinct)
-            const int np = nk + nf * M;
-            int nv = 0;
-            for (int e = tid; e < np; e += kFlashSelThreads) {
-                const uint64_t ke = sm.pkey[e];
-                if (ke == 0) continue;
-                ++nv;
-                int rank = 0;
-                for (int f = 0; f < np; ++f) rank += sm.pkey[f] > ke;
-                if (rank < nb) {
-                    sm.kkey[rank] = ke;
-                    sm.ktok[rank] = sm.ptok[e];
-                    sm.kstate[rank] = sm.pstate[e];
-                    sm.kfi[rank] = sm.pfi[e];
-                    sm.klogq[rank] = sm.plogq[e];
+            // the bitmap this level's keep fills (last read by the level before)
+            if (tid < kFlashBitWords) sm.cbits[d & 1][tid] = 0ull;
+            const uint64_t thr = nk == nb ? sm.kkey[cur][nb - 1] : 0ull;
+            const int nc = nf * M;
+            int* ncand = &sm.ncand[d & 1];
+            for (int e = tid; e < nk; e += kFlashSelThreads) sm.pkey[e] = sm.kkey[cur][e];
+            for (int w0 = 0; w0 < nc; w0 += kFlashSelThreads) {
+                const int w = w0 + tid;
+                uint64_t key = 0;
+                int tok = 0, cst = -1;
+                float lq = 0.0f;
+                if (w < nc) {
+                    const int fi = w / M, i = w - fi * M;
+                    const int ke = d == 1 ? -1 : sm.wpos[nth_bit_map(bm, fi)];
+                    const int ps = ke < 0 ? 0 : sm.kstate[cur][ke];
+                    const float psurv = ke < 0 ? 1.0f : key_surv(sm.kkey[cur][ke]);
+                    const float l2 = sm.cy2[ps][i] - sm.lse2[ps];
+                    const float q = exp2f(l2);
+                    const int bin = min(15, max(0, (int)floorf(16.0f * q)));
+                    const float sv = psurv * sm.cal[bin];
+                    const int slot = sm.rslot[ps][i];
+                    key = sv < tau ? 0ull : make_key(sv, d, fi, i);
+                    tok = sm.set[d - 1][slot];
+                    cst = d < B ? 1 + (d - 1) * M + slot : -1;
+                    lq = l2 * kLn2;
+                }
+                const bool keep = key > thr;
+                const uint64_t bal = __ballot(keep);
+                int base = 0;
+                if (lane == 0 && bal) base = atomicAdd(ncand, __popcll(bal));
+                base = __shfl(base, 0);
+                if (keep) {
+                    const int c = base + __popcll(bal & ((1ull << lane) - 1ull));
+                    sm.pkey[nk + c] = key;
+                    sm.ctok[c] = tok;
+                    sm.cstate[c] = (int16_t)cst;
+                    sm.clogq[c] = lq;
                 }
             }
-            if (nv) atomicAdd(&sm.nvalid, nv);
             __syncthreads();
-            if (tid == 0) sm.nkept = min(nb, sm.nvalid);
+            const int np = nk + *ncand;
+            if (tid == 0) sm.ncand[(d + 1) & 1] = 0;
+            if (np <= kFlashSelThreads)
+                flash_keep<1>(sm, cur, nk, np, nb, d, M, bm, tid);
+            else if (np <= 2 * kFlashSelThreads)
+                flash_keep<2>(sm, cur, nk, np, nb, d, M, bm, tid);
+            else
+                flash_keep<3>(sm, cur, nk, np, nb, d, M, bm, tid);
             __syncthreads();
+            nk = min(nb, np);
+            cur ^= 1;
         }
     }
-    // emission in canonical order: depth asc, then (parent's frontier index, sibling rank)
-    const int n = sm.nkept;
+    // emission in canonical order: depth asc, then (parent's frontier index, sibling rank),
+    // which is the order of the keys' low words, descending
+    const int n = nk;
+    int dd = 0, pos = 0;
     if (tid < n) {
-        const uint32_t lo = (uint32_t)sm.kkey[tid];
-        const int dd = low_depth(lo);
-        int pos = 0;
-        for (int e = 0; e < n; ++e) {
-            const uint32_t le = (uint32_t)sm.kkey[e];
-            const int de = low_depth(le);
-            pos += (de < dd) | ((de == dd) & (le > lo));
+        const uint32_t lo = (uint32_t)sm.kkey[cur][tid];
+        dd = low_depth(lo);
+        const ulonglong2* k2 = (const ulonglong2*)sm.kkey[cur];
+#pragma unroll 1
+        for (int f = 0; f < kMaxNcap / 2; f += 8) {
+            ulonglong2 x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = k2[f + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                pos += (int)(2 * (f + u) < n && (uint32_t)x[u].x > lo) +
+                       (int)(2 * (f + u) + 1 < n && (uint32_t)x[u].y > lo);
         }
-        sm.canon[tid] = (int16_t)pos;
         sm.korder[pos] = (int16_t)tid;
+        sm.pmap[dd][sm.kfi[cur][tid]] = (int16_t)pos;
     }
     __syncthreads();
-    if (tid < n) {
-        const int pos = sm.canon[tid];
-        const uint32_t lo = (uint32_t)sm.kkey[tid];
-        const int dd = low_depth(lo), pfi = low_fi(lo);
-        int par = -1;
-        if (dd > 1)
-            for (int e = 0; e < n; ++e)
-                if (low_depth((uint32_t)sm.kkey[e]) == dd - 1 && sm.kfi[e] == pfi) par = sm.canon[e];
-        sm.cpar[pos] = (int16_t)par;
-    }
+    if (tid < n)
+        sm.cpar[pos] = dd > 1 ? sm.pmap[dd - 1][low_fi((uint32_t)sm.kkey[cur][tid])] : (int16_t)-1;
     __syncthreads();
-    // ancestor mask: the node's own bit and its ancestors' (each node walks its own path)
+    // ancestor mask: the node's own bit and its ancestors' (each node walks its own path;
+    // a parent's position is below its child's)
     if (tid < n) {
         uint64_t m = 0;
-        for (int p = tid; p >= 0; p = sm.cpar[p]) m |= 1ull << p;
+        for (int p = tid, s = 0; p >= 0 && p < n && s <= kMaxB; p = sm.cpar[p], ++s) m |= 1ull << p;
         sm.mask[tid] = m;
     }
     __syncthreads();
@@ -703,12 +847,12 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
     for (int i = tid; i < Ncap; i += kFlashSelThreads) {
         if (i < n) {
             const int e = sm.korder[i];
-            a.out.token[base + i] = sm.ktok[e];
+            a.out.token[base + i] = sm.ktok[cur][e];
             a.out.parent[base + i] = sm.cpar[i];
-            a.out.depth[base + i] = (uint8_t)low_depth((uint32_t)sm.kkey[e]);
+            a.out.depth[base + i] = (uint8_t)low_depth((uint32_t)sm.kkey[cur][e]);
             a.out.anc_mask[base + i] = sm.mask[i];
-            a.out.surv[base + i] = key_surv(sm.kkey[e]);
-            a.out.logq[base + i] = sm.klogq[e];
+            a.out.surv[base + i] = key_surv(sm.kkey[cur][e]);
+            a.out.logq[base + i] = sm.klogq[cur][e];
         } else {
             a.out.token[base + i] = -1;
             a.out.parent[base + i] = -2;
@@ -728,20 +872,19 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
                 v = sm.set[0][sm.rslot[0][i]];
             } else if (row - 1 < n) {
                 const int e = sm.korder[row - 1];
-                const int st = sm.kstate[e];
-                const int dd = low_depth((uint32_t)sm.kkey[e]);
-                if (st >= 0) v = sm.set[dd][sm.rslot[st][i]];
+                const int st = sm.kstate[cur][e];
+                const int de = low_depth((uint32_t)sm.kkey[cur][e]);
+                if (st >= 0) v = sm.set[de][sm.rslot[st][i]];
             }
         }
         a.out.cand[cb + w] = v;
     }
-    if (tid == 0) {
-        a.out.n_nodes[req] = n;
-        a.out.status[req] = status;
-        if (a.out.n_expand) {
-            int ne = bad_root ? 0 : 1;
-            for (int e = 0; e < n; ++e) ne += sm.kstate[e] >= 0;
-            a.out.n_expand[req] = ne;
+    if (tid < 64) {
+        const uint64_t ex = __ballot(tid < n && sm.kstate[cur][tid] >= 0);
+        if (tid == 0) {
+            a.out.n_nodes[req] = n;
+            a.out.status[req] = status;
+            if (a.out.n_expand) a.out.n_expand[req] = (bad_root ? 0 : 1) + __popcll(ex);
         }
     }
 }

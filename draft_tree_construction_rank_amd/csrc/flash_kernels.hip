@@ -25,7 +25,7 @@
 namespace dt {
 
 constexpr int kFlashSetThreads = 256;
-constexpr int kFlashSelThreads = 256;
+constexpr int kFlashSelThreads = 512;
 constexpr int kFlashMaxStates = 1 + (kMaxB - 1) * kMaxK;  // 249
 constexpr int kFlashPool = kMaxNcap + kMaxNcap * kMaxK;   // kept + one level's children
 
@@ -66,27 +66,36 @@ __device__ __forceinline__ void flash_state(const FlashArgs& a, int req, int s, 
 // ---- stage 1: top-M of every block row ----------------------------------------------------
 // Each row is scanned by P workgroups (P parts of its columns); each part's ranked list of
 // 8 packed (logit, token) entries goes to the workspace and a second kernel merges a row's P
-// lists.  An entry enters a thread's list only if it beats the list's last entry (one
-// compare for almost every element once the list is warm).
-__device__ __forceinline__ void flash_offer(TopK<kMaxK>& top, float v, int c, uint64_t bound = 0) {
+// lists.  An entry enters a thread's list only if it beats the list's last entry.  For bf16
+// logits read 8 at a time, each wavefront first takes a bound from its first loads (the
+// M-th largest of its lanes' maxima), and a group of 8 whose largest value is below the
+// bound or below a full list's last value is passed over with one float compare.
+__device__ __forceinline__ void flash_offer(TopK<kMaxK>& top, float v, int c) {
     const uint64_t e = pack_entry(v, c);
-    const uint64_t kth = top.k[kMaxK - 1];
-    if (e > (kth > bound ? kth : bound)) top.push(e, 0.0f);
+    if (e > top.k[kMaxK - 1]) top.push(e, 0.0f);
 }
 
-// The largest last entry of the wavefront's lists: a lane whose list ends there holds
-// kMaxK entries at least as large, so no element below it can reach the part's top kMaxK
-// (entries are unique: each packs its own token).  Offering against it keeps the lanes of a
-// wavefront from taking the insertion branch in turn once their lists are warm.
-__device__ __forceinline__ uint64_t flash_wave_bound(const TopK<kMaxK>& top) {
-    uint64_t k = top.k[kMaxK - 1];
+// A value b such that at least m lanes of the wavefront hold v >= b (-inf if fewer than m
+// lanes hold a value): every one of those m lanes has an element of the row at least b, so
+// the row's m-th largest value is too, and no element below b can be among its top m.
+__device__ __forceinline__ float wave_mth_largest(float v, int m) {
+    float b = -INFINITY;
+    // each round takes the largest remaining value and the lanes holding it (at most 64)
+    for (int r = 0; r < 64 && m > 0; ++r) {
+        float t = v;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)k, off), hi = __shfl_xor((uint32_t)(k >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        k = o > k ? o : k;
+        for (int off = 1; off < 64; off <<= 1) t = fmaxf(t, __shfl_xor(t, off));
+        const int c = __popcll(__ballot(v >= t));
+        if (c == 0) {  // no ordered value left
+            b = -INFINITY;
+            break;
+        }
+        b = t;
+        m -= c;
+        if (t == -INFINITY) break;
+        v = v >= t ? -INFINITY : v;
     }
-    return k;
+    return m > 0 ? -INFINITY : b;
 }
 
 __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
         // four 16-byte loads in flight per thread (groups past the part reload its first);
         // the trip count is the same for every lane (the bound is a wavefront reduction)
         constexpr int kU = 4;
-        uint64_t bound = 0;
+        float bound = -INFINITY;
         for (int gb = g_beg; gb < g_end; gb += kU * kFlashSetThreads) {
             const int g0 = gb + tid;
             uint4 w[kU];
@@ -112,34 +121,48 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
                 const int g = g0 + u * kFlashSetThreads;
                 w[u] = p[g < g_end ? g : g_beg];
             }
+            float f[kU][8], gmax[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f[u][2 * i] = bf16_lo(x[i]);
+                    f[u][2 * i + 1] = bf16_hi(x[i]);
+                }
+                const bool in = g0 + u * kFlashSetThreads < g_end;
+                gmax[u] = in ? fmaxf(fmaxf(fmaxf(f[u][0], f[u][1]), fmaxf(f[u][2], f[u][3])),
+                                     fmaxf(fmaxf(f[u][4], f[u][5]), fmaxf(f[u][6], f[u][7])))
+                             : -INFINITY;
+            }
+            // first step: the bound from the M-th largest lane maximum, so that the lists
+            // start near the row's top values instead of taking every early element
+            if (gb == g_beg)
+                bound = wave_mth_largest(fmaxf(fmaxf(gmax[0], gmax[1]), fmaxf(gmax[2], gmax[3])), a.M);
+            // the threshold's value: a group whose largest value is below it holds no entry
+            // above the threshold (a tie in value may still win on its token: exact test)
+            const uint64_t kth = top.k[kMaxK - 1];
+            const float thrv = kth == 0 ? bound : fmaxf(bound, entry_key(kth));
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int g = g0 + u * kFlashSetThreads;
-                // the group's eight entries, a mask of those above the bound, then one
-                // insertion per candidate (rare once the lists are warm)
-                const uint32_t x[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-                uint64_t e[8];
+                if (g < g_end && gmax[u] >= thrv) {
+                    // the group's entries at or above the threshold's value, one insertion
+                    // each (an entry enters only if it beats the list's last)
+                    uint32_t m = 0;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    e[2 * i] = pack_entry(bf16_lo(x[i]), 8 * g + 2 * i);
-                    e[2 * i + 1] = pack_entry(bf16_hi(x[i]), 8 * g + 2 * i + 1);
-                }
-                const uint64_t kth = top.k[kMaxK - 1];
-                const uint64_t thr = kth > bound ? kth : bound;
-                uint32_t m = 0;
+                    for (int i = 0; i < 8; ++i) m |= (f[u][i] >= thrv) ? (1u << i) : 0u;
+                    while (m != 0u) {
+                        const int i = __builtin_ctz(m);
+                        m &= m - 1u;
+                        float v = f[u][0];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) m |= (e[i] > thr) ? (1u << i) : 0u;
-                m = g < g_end ? m : 0u;
-                while (m != 0u) {
-                    const int i = __builtin_ctz(m);
-                    m &= m - 1u;
-                    uint64_t v = e[0];
-#pragma unroll
-                    for (int q = 1; q < 8; ++q) v = q == i ? e[q] : v;
-                    if (v > top.k[kMaxK - 1]) top.push(v, 0.0f);
+                        for (int q = 1; q < 8; ++q) v = q == i ? f[u][q] : v;
+                        const uint64_t e = pack_entry(v, 8 * g + i);
+                        if (e > top.k[kMaxK - 1]) top.push(e, 0.0f);
+                    }
                 }
             }
-            bound = flash_wave_bound(top);
         }
     } else {
         const int c_beg = (int)((long)part * a.V / a.P), c_end = (int)((long)(part + 1) * a.V / a.P);

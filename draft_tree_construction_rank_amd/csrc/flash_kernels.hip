@@ -224,11 +224,33 @@ static_assert(kFlashLseWaves * 64 == 256, "k_flash_lse runs 256 threads");
 // Raw bf16 block logits of a lane's 16 columns (c0 + 8j + 4h + i), 16-byte-aligned rows only.
 __device__ __forceinline__ void flash_lgroups(const FlashArgs& a, size_t lb, int c0, int h,
                                               uint2 (&g)[4]) {
+    if (c0 + kBlockCols <= a.V) {
+        // a whole block: one address, the four groups at immediate offsets
+        const uint2* p = (const uint2*)((const uint16_t*)a.L + lb + c0 + 4 * h);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int c = c0 + 8 * j + 4 * h;
-        g[j] = *(const uint2*)((const uint16_t*)a.L + lb + (c < a.V ? c : a.V - 4));
+        for (int j = 0; j < 4; ++j) g[j] = p[2 * j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + 8 * j + 4 * h;
+            g[j] = *(const uint2*)((const uint16_t*)a.L + lb + (c < a.V ? c : a.V - 4));
+        }
     }
+}
+
+// The W fragments of a block; for r = 256 one row address per lane and the sixteen k-steps
+// at immediate offsets (the general loader clamps and addresses every step).
+__device__ __forceinline__ void flash_wfrag(const FlashArgs& a, int c0, bf16x8 (&wf)[16]) {
+    if (a.r != 256) {
+        load_wfrag(a.Wt, a.V, a.r, c0, wf);
+        return;
+    }
+    const int lane = threadIdx.x & 63;
+    const int col = c0 + (lane & 31);
+    const uint4* p = (const uint4*)((const uint16_t*)a.Wt + (size_t)(col < a.V ? col : a.V - 1) * 256) +
+                     (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 16; ++s) wf[s] = __builtin_bit_cast(bf16x8, p[2 * s]);
 }
 
 // The accumulators' initial values: the block logits of the lane's columns (clamped into the
@@ -254,23 +276,29 @@ __device__ __forceinline__ void flash_to_acc(const FlashArgs& a, const uint2 (&g
 
 // One state's 16 values of a block: the conditional logits of its children that fall in
 // these columns (the same fp32 values that enter the log-sum-exp), then the online
-// log-sum-exp (log2 units).
+// log-sum-exp (log2 units).  ntgt is the state's smallest child column not yet passed by
+// this wavefront's blocks (they come in increasing order), so most blocks test it alone.
 __device__ __forceinline__ void flash_epi(const FlashArgs& a, f32x16& z, int c0, int h,
-                                          const int* tgt, size_t zrow, Lse2& st) {
+                                          const int* tgt, size_t zrow, int& ntgt, Lse2& st) {
     if (c0 + kBlockCols > a.V) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             if (c0 + 8 * (e >> 2) + 4 * h + (e & 3) >= a.V) z[e] = -INFINITY;
     }
-    for (int i = 0; i < a.M; ++i) {
-        const int off = tgt[i] - c0;
-        if (off >= 0 && off < kBlockCols && ((off >> 2) & 1) == h) {
-            const int e = 4 * (off >> 3) + (off & 3);
-            float v = z[0];
+    if (ntgt < c0 + kBlockCols) {
+        int nx = 0x7FFFFFFF;
+        for (int i = 0; i < a.M; ++i) {
+            const int t = tgt[i], off = t - c0;
+            if (off >= 0 && off < kBlockCols && ((off >> 2) & 1) == h) {
+                const int e = 4 * (off >> 3) + (off & 3);
+                float v = z[0];
 #pragma unroll
-            for (int q = 1; q < 16; ++q) v = q == e ? z[q] : v;
-            a.zc[zrow + i] = v;
+                for (int q = 1; q < 16; ++q) v = q == e ? z[q] : v;
+                a.zc[zrow + i] = v;
+            }
+            if (off >= kBlockCols) nx = min(nx, t);
         }
+        ntgt = nx;
     }
     constexpr float kLog2e = 1.4426950408889634f;
     float zmax = z[0];
@@ -282,9 +310,11 @@ __device__ __forceinline__ void flash_epi(const FlashArgs& a, f32x16& z, int c0,
         st.s = (st.m == -INFINITY) ? 0.0f : st.s * exp2f(st.m - cm);
         st.m = cm;
     }
+    // the hardware exp2 without exp2f's rescaling of tiny results: terms below 2^-126 of the
+    // running maximum flush to zero, far below float32 resolution of the sum
     float ps = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ps += exp2f(z[e] * kLog2e - st.m);
+    for (int e = 0; e < 16; ++e) ps += __builtin_amdgcn_exp2f(z[e] * kLog2e - st.m);
     st.s += ps;
 }
 
@@ -337,8 +367,14 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
         liveq[q] = row < nrows;
     }
     Lse2 st[4];
+    int ntgt[4];  // per row block: the state's smallest child column not yet passed
 #pragma unroll
-    for (int q = 0; q < 4; ++q) st[q].init();
+    for (int q = 0; q < 4; ++q) {
+        st[q].init();
+        int n = 0x7FFFFFFF;
+        for (int i = 0; i < a.M; ++i) n = min(n, sTgt[32 * q + p0][i] < 0 ? n : sTgt[32 * q + p0][i]);
+        ntgt[q] = n;
+    }
     // per block: row blocks 0-1, then 2-3 on the same W fragments (one accumulator pair
     // live at a time); the logits of the next pair and the next block are in flight while
     // the current pair's epilogue runs
@@ -346,7 +382,7 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
     uint2 la[2][4], lc[2][4];  // logits of row blocks 0-1 (this block), of 2-3
     int blk = b_beg + wave;
     if (blk < b_end) {
-        load_wfrag(a.Wt, a.V, a.r, blk * kBlockCols, wf);
+        flash_wfrag(a, blk * kBlockCols, wf);
         if (a.lvec) {
             flash_lgroups(a, lbq[0], blk * kBlockCols, h, la[0]);
             if (nq > 1) flash_lgroups(a, lbq[1], blk * kBlockCols, h, la[1]);
@@ -365,27 +401,27 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
         const bool more = blk + kFlashLseWaves < b_end;
         const int cn = c0 + kFlashLseWaves * kBlockCols;
         if (nq <= 2 && more) {
-            load_wfrag(a.Wt, a.V, a.r, cn, wf);
+            flash_wfrag(a, cn, wf);
             if (a.lvec) {
                 flash_lgroups(a, lbq[0], cn, h, la[0]);
                 if (nq > 1) flash_lgroups(a, lbq[1], cn, h, la[1]);
             }
         }
-        if (liveq[0]) flash_epi(a, acc0, c0, h, sTgt[p0], zrq[0], st[0]);
-        if (nq > 1 && liveq[1]) flash_epi(a, acc1, c0, h, sTgt[32 + p0], zrq[1], st[1]);
+        if (liveq[0]) flash_epi(a, acc0, c0, h, sTgt[p0], zrq[0], ntgt[0], st[0]);
+        if (nq > 1 && liveq[1]) flash_epi(a, acc1, c0, h, sTgt[32 + p0], zrq[1], ntgt[1], st[1]);
         if (nq > 2) {
             flash_to_acc(a, lc[0], lbq[2], c0, h, acc0);
             if (nq > 3) flash_to_acc(a, lc[1], lbq[3], c0, h, acc1);
             mma_wfrag(wf, nq > 3, sA + kTileRows * kAStride, acc0, acc1);
             if (more) {
-                load_wfrag(a.Wt, a.V, a.r, cn, wf);
+                flash_wfrag(a, cn, wf);
                 if (a.lvec) {
                     flash_lgroups(a, lbq[0], cn, h, la[0]);
                     flash_lgroups(a, lbq[1], cn, h, la[1]);
                 }
             }
-            if (liveq[2]) flash_epi(a, acc0, c0, h, sTgt[64 + p0], zrq[2], st[2]);
-            if (nq > 3 && liveq[3]) flash_epi(a, acc1, c0, h, sTgt[96 + p0], zrq[3], st[3]);
+            if (liveq[2]) flash_epi(a, acc0, c0, h, sTgt[64 + p0], zrq[2], ntgt[2], st[2]);
+            if (nq > 3 && liveq[3]) flash_epi(a, acc1, c0, h, sTgt[96 + p0], zrq[3], ntgt[3], st[3]);
         }
     }
     // lanes l and l ^ 32 hold the same state; then the wavefronts' blocks
@@ -493,7 +529,7 @@ __device__ __forceinline__ void flash_lse_chunks(const FlashArgs& a) {
             float s = 0.0f;
             if (m != -INFINITY)
 #pragma unroll
-                for (int i = 0; i < 32; ++i) s += exp2f(zv[i] - m);
+                for (int i = 0; i < 32; ++i) s += __builtin_amdgcn_exp2f(zv[i] - m);  // (as above)
             st.merge(m, s);
         }
         __syncthreads();  // sZ is rewritten by the next chunk
@@ -504,7 +540,7 @@ __device__ __forceinline__ void flash_lse_chunks(const FlashArgs& a) {
 }
 
 template <bool HEAD_BF16>
-__global__ __launch_bounds__(256) void k_flash_lse(FlashArgs a) {
+__global__ __launch_bounds__(256, 2) void k_flash_lse(FlashArgs a) {  // two workgroups per CU
     if constexpr (HEAD_BF16)
         flash_lse_blocks(a);
     else

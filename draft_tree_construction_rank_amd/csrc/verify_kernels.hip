@@ -382,12 +382,14 @@ __global__ __launch_bounds__(256) void k_vs_rows(const VsArgs a) {
                     }
                 }
             }
+            // (the hardware exp2: terms below 2^-126 of the block maximum flush to zero, far
+            // below float32 resolution of a sum that holds the maximum's 1)
             float sq = 0.0f, sp = 0.0f;
 #pragma unroll
             for (int j = 0; j < 32; ++j) {
                 if (cb + j < a.V) {
-                    sq += exp2f(yq[j] - mq);
-                    sp += exp2f(yp[j] - mp);
+                    sq += __builtin_amdgcn_exp2f(yq[j] - mq);
+                    sp += __builtin_amdgcn_exp2f(yp[j] - mp);
                 }
             }
             if (mq != -INFINITY) {
@@ -466,9 +468,9 @@ __device__ __forceinline__ void vs_row_epi(const VsArgs& a, const f32x16& z, con
     float sq = 0.0f, sp = 0.0f;
     if (mq != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            sq += exp2f(yq[e] - mq);
-            sp += exp2f(yp[e] - mp);
+        for (int e = 0; e < 16; ++e) {  // (hardware exp2, as in k_vs_rows)
+            sq += __builtin_amdgcn_exp2f(yq[e] - mq);
+            sp += __builtin_amdgcn_exp2f(yp[e] - mp);
         }
         lq.merge(mq, sq);
         lp.merge(mp, sp);

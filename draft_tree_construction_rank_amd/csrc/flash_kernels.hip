@@ -255,11 +255,12 @@ __device__ __forceinline__ void flash_wfrag(const FlashArgs& a, int c0, bf16x8 (
 
 // The accumulators' initial values: the block logits of the lane's columns (clamped into the
 // row past V; those columns are masked in the epilogue).
+template <bool LVEC>
 __device__ __forceinline__ void flash_to_acc(const FlashArgs& a, const uint2 (&g)[4], size_t lb,
                                              int c0, int h, f32x16& acc) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if (a.lvec) {
+        if constexpr (LVEC) {
             acc[4 * j + 0] = bf16_lo(g[j].x);
             acc[4 * j + 1] = bf16_hi(g[j].x);
             acc[4 * j + 2] = bf16_lo(g[j].y);
@@ -318,6 +319,10 @@ __device__ __forceinline__ void flash_epi(const FlashArgs& a, f32x16& z, int c0,
     st.s += ps;
 }
 
+// LVEC: bf16 logits read 16 bytes at a time (a.lvec), fixed at compile time so that no
+// per-group branch makes the compiler wait for every load in flight (the next block's
+// fragments included) before it converts a group.
+template <bool LVEC>
 __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
     __shared__ __align__(16) uint16_t sA[kFlashTile * kAStride];
     __shared__ int sTok[kFlashTile];
@@ -383,7 +388,7 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
     int blk = b_beg + wave;
     if (blk < b_end) {
         flash_wfrag(a, blk * kBlockCols, wf);
-        if (a.lvec) {
+        if constexpr (LVEC) {
             flash_lgroups(a, lbq[0], blk * kBlockCols, h, la[0]);
             if (nq > 1) flash_lgroups(a, lbq[1], blk * kBlockCols, h, la[1]);
         }
@@ -391,10 +396,10 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
     for (; blk < b_end; blk += kFlashLseWaves) {
         const int c0 = blk * kBlockCols;
         f32x16 acc0, acc1;
-        flash_to_acc(a, la[0], lbq[0], c0, h, acc0);
-        if (nq > 1) flash_to_acc(a, la[1], lbq[1], c0, h, acc1);
+        flash_to_acc<LVEC>(a, la[0], lbq[0], c0, h, acc0);
+        if (nq > 1) flash_to_acc<LVEC>(a, la[1], lbq[1], c0, h, acc1);
         mma_wfrag(wf, nq > 1, sA, acc0, acc1);
-        if (nq > 2 && a.lvec) {
+        if (nq > 2 && LVEC) {
             flash_lgroups(a, lbq[2], c0, h, lc[0]);
             if (nq > 3) flash_lgroups(a, lbq[3], c0, h, lc[1]);
         }
@@ -402,7 +407,7 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
         const int cn = c0 + kFlashLseWaves * kBlockCols;
         if (nq <= 2 && more) {
             flash_wfrag(a, cn, wf);
-            if (a.lvec) {
+            if constexpr (LVEC) {
                 flash_lgroups(a, lbq[0], cn, h, la[0]);
                 if (nq > 1) flash_lgroups(a, lbq[1], cn, h, la[1]);
             }
@@ -410,12 +415,12 @@ __device__ __forceinline__ void flash_lse_blocks(const FlashArgs& a) {
         if (liveq[0]) flash_epi(a, acc0, c0, h, sTgt[p0], zrq[0], ntgt[0], st[0]);
         if (nq > 1 && liveq[1]) flash_epi(a, acc1, c0, h, sTgt[32 + p0], zrq[1], ntgt[1], st[1]);
         if (nq > 2) {
-            flash_to_acc(a, lc[0], lbq[2], c0, h, acc0);
-            if (nq > 3) flash_to_acc(a, lc[1], lbq[3], c0, h, acc1);
+            flash_to_acc<LVEC>(a, lc[0], lbq[2], c0, h, acc0);
+            if (nq > 3) flash_to_acc<LVEC>(a, lc[1], lbq[3], c0, h, acc1);
             mma_wfrag(wf, nq > 3, sA + kTileRows * kAStride, acc0, acc1);
             if (more) {
                 flash_wfrag(a, cn, wf);
-                if (a.lvec) {
+                if constexpr (LVEC) {
                     flash_lgroups(a, lbq[0], cn, h, la[0]);
                     flash_lgroups(a, lbq[1], cn, h, la[1]);
                 }
@@ -539,10 +544,12 @@ __device__ __forceinline__ void flash_lse_chunks(const FlashArgs& a) {
     if (live && q == 0) a.lsep[(size_t)(g0 + row) * a.SP + split] = make_float2(st.m, st.s);
 }
 
-template <bool HEAD_BF16>
+// LVEC (16-byte logit loads) is a separate kernel: one kernel with both paths needs more
+// registers than two waves per SIMD allow.
+template <bool HEAD_BF16, bool LVEC>
 __global__ __launch_bounds__(256, 2) void k_flash_lse(FlashArgs a) {  // two workgroups per CU
     if constexpr (HEAD_BF16)
-        flash_lse_blocks(a);
+        flash_lse_blocks<LVEC>(a);
     else
         flash_lse_chunks<false>(a);
 }
@@ -1013,10 +1020,12 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = a.T * ((a.SP + 7) / 8) * 8;
-    if (p->head_dtype == DT_BF16)
-        k_flash_lse<true><<<grid, 256, 0, st>>>(a);
+    if (p->head_dtype == DT_BF16 && a.lvec)
+        k_flash_lse<true, true><<<grid, 256, 0, st>>>(a);
+    else if (p->head_dtype == DT_BF16)
+        k_flash_lse<true, false><<<grid, 256, 0, st>>>(a);
     else
-        k_flash_lse<false><<<grid, 256, 0, st>>>(a);
+        k_flash_lse<false, false><<<grid, 256, 0, st>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_flash_select<<<p->R, kFlashSelThreads, 0, st>>>(a);

@@ -11,12 +11,14 @@
 // survival, order and emission) over the lattice in which a node of depth j with token t has
 // the children S_j, with q from state (j, t) and siblings ranked by their conditional logit.
 //
-// Kernels: k_flash_sets (top-M of every block row: one 1024-thread workgroup a row),
-// k_flash_lse (log-sum-exp of every state over vocabulary splits: a (64-state tile,
-// split) workgroup streams the split's W columns through MFMA, adds the block logits and
-// keeps an online log2-sum-exp per state), k_flash_select (one workgroup a request: the
-// conditional logits of the lattice children as dot products, the split log-sum-exps
-// combined, then the level-synchronous select and the emission, all in LDS).
+// Kernels: k_flash_sets (top-M of every block row: P workgroups a row, one list per part)
+// and k_flash_sets_merge (a row's P lists), k_flash_lse (log-sum-exp of every state over
+// vocabulary splits: a (state tile, split) workgroup streams the split's W columns through
+// MFMA with the block logits as the accumulators' initial values, keeps an online
+// log2-sum-exp per state and takes the children's conditional logits from the same
+// accumulators), k_flash_select (one workgroup a request: the split log-sum-exps combined,
+// sibling order, then the level-synchronous select over pruned pools and the emission, all
+// in LDS).
 #include <hip/hip_runtime.h>
 
 #include "dt_device.h"

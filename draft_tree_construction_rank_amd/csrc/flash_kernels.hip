@@ -67,14 +67,15 @@ __device__ __forceinline__ void flash_state(const FlashArgs& a, int req, int s, 
 
 // ---- stage 1: top-M of every block row ----------------------------------------------------
 // Each row is scanned by P workgroups (P parts of its columns); each part's ranked list of
-// 8 packed (logit, token) entries goes to the workspace and a second kernel merges a row's P
-// lists.  An entry enters a thread's list only if it beats the list's last entry.  For bf16
+// packed (logit, token) entries (the smallest of 1, 2, 4, 8 that holds M) goes to the
+// workspace and a second kernel merges a row's P lists.  An entry enters a thread's list only if it beats the list's last entry.  For bf16
 // logits read 8 at a time, each wavefront first takes a bound from its first loads (the
 // M-th largest of its lanes' maxima), and a group of 8 whose largest value is below the
 // bound or below a full list's last value is passed over with one float compare.
-__device__ __forceinline__ void flash_offer(TopK<kMaxK>& top, float v, int c) {
+template <int KT>
+__device__ __forceinline__ void flash_offer(TopK<KT>& top, float v, int c) {
     const uint64_t e = pack_entry(v, c);
-    if (e > top.k[kMaxK - 1]) top.push(e, 0.0f);
+    if (e > top.k[KT - 1]) top.push(e, 0.0f);
 }
 
 // A value b such that at least m lanes of the wavefront hold v >= b (-inf if fewer than m
@@ -100,12 +101,15 @@ __device__ __forceinline__ float wave_mth_largest(float v, int m) {
     return m > 0 ? -INFINITY : b;
 }
 
+// KT = the list length for M (kt_for(M) <= kMaxK); a part's list goes out as kMaxK entries,
+// zero-padded (zero is below every real entry).
+template <int KT>
 __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
-    __shared__ uint64_t sk[kFlashSetThreads / 64][kMaxK];
+    __shared__ uint64_t sk[kFlashSetThreads / 64][KT];
     const int row = blockIdx.x / a.P, part = blockIdx.x % a.P;  // row = req * B + j
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t base = (size_t)row * a.V;
-    TopK<kMaxK> top;
+    TopK<KT> top;
     top.init();
     if (a.lvec) {
         const uint4* p = (const uint4*)((const uint16_t*)a.L + base);
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
                 bound = wave_mth_largest(fmaxf(fmaxf(gmax[0], gmax[1]), fmaxf(gmax[2], gmax[3])), a.M);
             // the threshold's value: a group whose largest value is below it holds no entry
             // above the threshold (a tie in value may still win on its token: exact test)
-            const uint64_t kth = top.k[kMaxK - 1];
+            const uint64_t kth = top.k[KT - 1];
             const float thrv = kth == 0 ? bound : fmaxf(bound, entry_key(kth));
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
 #pragma unroll
                         for (int q = 1; q < 8; ++q) v = q == i ? f[u][q] : v;
                         const uint64_t e = pack_entry(v, 8 * g + i);
-                        if (e > top.k[kMaxK - 1]) top.push(e, 0.0f);
+                        if (e > top.k[KT - 1]) top.push(e, 0.0f);
                     }
                 }
             }
@@ -174,20 +178,20 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
     for (int off = 1; off < 64; off <<= 1) top.merge_xor(off);
     if (lane == 0)
 #pragma unroll
-        for (int i = 0; i < kMaxK; ++i) sk[wave][i] = top.k[i];
+        for (int i = 0; i < KT; ++i) sk[wave][i] = top.k[i];
     __syncthreads();
     if (wave == 0) {
-        TopK<kMaxK> t;
+        TopK<KT> t;
         t.init();
         if (lane < kFlashSetThreads / 64)
 #pragma unroll
-            for (int i = 0; i < kMaxK; ++i) t.k[i] = sk[lane][i];
+            for (int i = 0; i < KT; ++i) t.k[i] = sk[lane][i];
 #pragma unroll
         for (int off = 1; off < kFlashSetThreads / 64; off <<= 1) t.merge_xor(off);
         if (lane < kMaxK) {
             uint64_t v = 0;
 #pragma unroll
-            for (int i = 0; i < kMaxK; ++i) v = lane == i ? t.k[i] : v;
+            for (int i = 0; i < KT; ++i) v = lane == i ? t.k[i] : v;
             a.setp[((size_t)row * a.P + part) * kMaxK + lane] = v;
         }
     }
@@ -1015,7 +1019,15 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
     a.logits_bf16 = p->logits_dtype == DT_BF16;
     a.lvec = a.logits_bf16 && (p->V & 7) == 0 && ((uintptr_t)L & 15) == 0;
     for (int i = 0; i < 16; ++i) a.cal[i] = p->cal[i];
-    k_flash_sets<<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
+    const int kt = kt_for(p->k);
+    if (kt == 1)
+        k_flash_sets<1><<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
+    else if (kt == 2)
+        k_flash_sets<2><<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
+    else if (kt == 4)
+        k_flash_sets<4><<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
+    else
+        k_flash_sets<8><<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_flash_sets_merge<<<p->R * p->B, 64, 0, st>>>(a);

@@ -197,19 +197,21 @@ __global__ __launch_bounds__(kFlashSetThreads) void k_flash_sets(FlashArgs a) {
     }
 }
 
-// One wavefront per row merges the row's P part lists into its set S_j (M tokens).
+// One wavefront per row merges the row's P part lists into its set S_j (M tokens); a part
+// list's entries past KT are its zero padding.
+template <int KT>
 __global__ __launch_bounds__(64) void k_flash_sets_merge(FlashArgs a) {
     const int row = blockIdx.x, lane = threadIdx.x;
-    TopK<kMaxK> t;
+    TopK<KT> t;
     t.init();
     if (lane < a.P)
 #pragma unroll
-        for (int i = 0; i < kMaxK; ++i) t.k[i] = a.setp[((size_t)row * a.P + lane) * kMaxK + i];
+        for (int i = 0; i < KT; ++i) t.k[i] = a.setp[((size_t)row * a.P + lane) * kMaxK + i];
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) t.merge_xor(off);
     if (lane == 0)
 #pragma unroll
-        for (int i = 0; i < kMaxK; ++i)
+        for (int i = 0; i < KT; ++i)
             if (i < a.M) a.sets[(size_t)row * a.M + i] = entry_tok(t.k[i]);
 }
 
@@ -1030,7 +1032,14 @@ hipError_t launch_build_flash(const dt_params* p, const FlashPlan& pl, const voi
         k_flash_sets<8><<<p->R * p->B * pl.P, kFlashSetThreads, 0, st>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_flash_sets_merge<<<p->R * p->B, 64, 0, st>>>(a);
+    if (kt == 1)
+        k_flash_sets_merge<1><<<p->R * p->B, 64, 0, st>>>(a);
+    else if (kt == 2)
+        k_flash_sets_merge<2><<<p->R * p->B, 64, 0, st>>>(a);
+    else if (kt == 4)
+        k_flash_sets_merge<4><<<p->R * p->B, 64, 0, st>>>(a);
+    else
+        k_flash_sets_merge<8><<<p->R * p->B, 64, 0, st>>>(a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = a.T * ((a.SP + 7) / 8) * 8;

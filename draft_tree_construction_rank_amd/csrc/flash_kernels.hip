@@ -229,21 +229,22 @@ constexpr int kFlashLseWaves = 4;
 constexpr int kFlashTile = 128;  // states per workgroup of the bf16 state pass (4 MFMA row blocks)
 static_assert(kFlashLseWaves * 64 == 256, "k_flash_lse runs 256 threads");
 
-// Raw bf16 block logits of a lane's 16 columns (c0 + 8j + 4h + i), 16-byte-aligned rows only.
+// Raw bf16 block logits for a lane (16-byte-aligned rows only): lane half h loads the 16
+// columns c0 + 16h .. as two 16-byte pieces, g = (piece 0, piece 1); a piece past V (pieces
+// are whole: V is a multiple of 8) reloads the row's last one, masked in the epilogue.  The
+// lane needs columns c0 + 8j + 4h + i instead: flash_to_acc swaps halves with lane l ^ 32 at
+// use, so that the loads stay in flight until then.  (Two 16-byte loads per lane instead of
+// four 8-byte ones: each load instruction touches every state's row once.)
 __device__ __forceinline__ void flash_lgroups(const FlashArgs& a, size_t lb, int c0, int h,
                                               uint2 (&g)[4]) {
-    if (c0 + kBlockCols <= a.V) {
-        // a whole block: one address, the four groups at immediate offsets
-        const uint2* p = (const uint2*)((const uint16_t*)a.L + lb + c0 + 4 * h);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) g[j] = p[2 * j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = c0 + 8 * j + 4 * h;
-            g[j] = *(const uint2*)((const uint16_t*)a.L + lb + (c < a.V ? c : a.V - 4));
-        }
-    }
+    const uint16_t* row = (const uint16_t*)a.L + lb;
+    const int s0 = c0 + 16 * h, s1 = s0 + 8;
+    const uint4 x0 = *(const uint4*)(row + (s0 < a.V ? s0 : a.V - 8));
+    const uint4 x1 = *(const uint4*)(row + (s1 < a.V ? s1 : a.V - 8));
+    g[0] = make_uint2(x0.x, x0.y);
+    g[1] = make_uint2(x0.z, x0.w);
+    g[2] = make_uint2(x1.x, x1.y);
+    g[3] = make_uint2(x1.z, x1.w);
 }
 
 // The W fragments of a block; for r = 256 one row address per lane and the sixteen k-steps
@@ -266,14 +267,42 @@ __device__ __forceinline__ void flash_wfrag(const FlashArgs& a, int c0, bf16x8 (
 template <bool LVEC>
 __device__ __forceinline__ void flash_to_acc(const FlashArgs& a, const uint2 (&g)[4], size_t lb,
                                              int c0, int h, f32x16& acc) {
+    if constexpr (LVEC) {
+        // g holds groups 2h and 2h + 1 whole (flash_lgroups: g[2pc + e] is half e, columns
+        // 4e .. 4e + 3, of piece pc): keep this lane's half h of each piece, send the other
+        // half, and take the partner's half h of groups 2(1 - h) and 2(1 - h) + 1
+        const uint32_t keep[4] = {h ? g[1].x : g[0].x, h ? g[1].y : g[0].y, h ? g[3].x : g[2].x,
+                                  h ? g[3].y : g[2].y};
+        const uint32_t send[4] = {h ? g[0].x : g[1].x, h ? g[0].y : g[1].y, h ? g[2].x : g[3].x,
+                                  h ? g[2].y : g[3].y};
+        uint32_t recv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // results: [0] lane l % 32's value, [1] lane l % 32 + 32's
+            const auto sw = __builtin_amdgcn_permlane32_swap(send[i], send[i], false, false);
+            recv[i] = h ? sw[0] : sw[1];
+        }
+        // group j's two dwords: from the piece of group j held by half j / 2
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool mine = (j >> 1) == h;
+            const int pc = j & 1;  // which piece of the holder
+            w[2 * j] = mine ? keep[2 * pc] : recv[2 * pc];
+            w[2 * j + 1] = mine ? keep[2 * pc + 1] : recv[2 * pc + 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            acc[4 * j + 0] = bf16_lo(w[2 * j]);
+            acc[4 * j + 1] = bf16_hi(w[2 * j]);
+            acc[4 * j + 2] = bf16_lo(w[2 * j + 1]);
+            acc[4 * j + 3] = bf16_hi(w[2 * j + 1]);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        if constexpr (LVEC) {
-            acc[4 * j + 0] = bf16_lo(g[j].x);
-            acc[4 * j + 1] = bf16_hi(g[j].x);
-            acc[4 * j + 2] = bf16_lo(g[j].y);
-            acc[4 * j + 3] = bf16_hi(g[j].y);
-        } else {
+        {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int c = c0 + 8 * j + 4 * h + i;

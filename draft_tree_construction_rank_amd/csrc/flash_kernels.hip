@@ -697,8 +697,8 @@ __device__ __forceinline__ int nth_bit_map(const uint64_t (&bm)[kFlashBitWords],
     return 64 * word + nth_bit(sel, n);
 }
 
-// Scatter of this thread's pool entries e = tid + 256 o that rank inside the budget into the
-// output buffer of kept nodes.  A kept node of depth d - 1 takes its frontier index (its
+// Scatter of this thread's pool entries e = tid + kFlashSelThreads o that rank inside the
+// budget into the output buffer of kept nodes.  A kept node of depth d - 1 takes its frontier index (its
 // position in the level's frontier, which is in candidate-index order); a kept candidate
 // starts with none and marks its index in the level's bitmap.
 template <int NO>
@@ -902,12 +902,11 @@ __global__ __launch_bounds__(kFlashSelThreads) void k_flash_select(FlashArgs a) 
             __syncthreads();
             const int np = nk + *ncand;
             if (tid == 0) sm.ncand[(d + 1) & 1] = 0;
+            static_assert(kFlashPool <= 2 * kFlashSelThreads, "at most two pool entries a thread");
             if (np <= kFlashSelThreads)
                 flash_keep<1>(sm, cur, nk, np, nb, d, M, bm, tid);
-            else if (np <= 2 * kFlashSelThreads)
-                flash_keep<2>(sm, cur, nk, np, nb, d, M, bm, tid);
             else
-                flash_keep<3>(sm, cur, nk, np, nb, d, M, bm, tid);
+                flash_keep<2>(sm, cur, nk, np, nb, d, M, bm, tid);
             __syncthreads();
             nk = min(nb, np);
             cur ^= 1;

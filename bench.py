@@ -86,8 +86,8 @@ def gpu_targets(inst, tree, rho, gen_seed, torch):
 
 
 def algorithmic_bytes(inst, level_rows_per_req, n_expand) -> float:
-    """Bytes the method must move in one round (per the survey's per-unit figures):
-    L rows used (one V-row per request per level at which it expands) + W once + U rows."""
+    """Bytes the method must move in one round (algorithmic, per unit of work): the L rows
+    used (one V-row per request per level at which it expands) + W once + the U rows."""
     V, r = inst.V, inst.r
     l_bytes = sum(level_rows_per_req) * V * 2
     return l_bytes + r * V * 2 + sum(n_expand) * r * 2
@@ -601,8 +601,8 @@ def main():
                          "and print their JSON; for profiling")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (requests shard "
-              "across GPUs without communication; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (requests shard "
+              "across GPUs without communication). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

@@ -133,18 +133,23 @@ __device__ __forceinline__ void load_slice(const BuildArgs& a, const Slice& sl,
 #pragma unroll
         for (int s = 0; s < 16; ++s) wr[i][s] = src[2 * s];
     }
+    // the LDS blocks: 32 rows x 32 chunks of 16 bytes each, copied global -> LDS directly
+    // (1 KB a wavefront per copy) so that every copy of the slice is in flight at once; lane l
+    // of copy k fills slot d = 64k + l, which holds row jj = d / 32, chunk (d % 32) ^ jj
     const int nlds = sl.nb - kResWaves * kResAgprSlots;
     for (int i = 0; i < nlds; ++i) {
-        // 32 rows x 32 chunks of 16 bytes, four per thread
 #pragma unroll
-        for (int q = 0; q < (kBlockCols * 32) / kResThreads; ++q) {
-            const int x = tid + q * kResThreads;
-            const int jj = x >> 5, c = x & 31;
+        for (int k = wave; k < (kBlockCols * 32) / 64; k += kResWaves) {
+            const int d = 64 * k + lane;
+            const int jj = d >> 5, c = (d & 31) ^ jj;
             int col = (sl.b_beg + kResWaves * kResAgprSlots + i) * kBlockCols + jj;
             col = col < a.V ? col : a.V - 1;
-            sm.wl[i][32 * jj + (c ^ jj)] = *(const uint4*)(Wt + (size_t)col * 256 + 8 * c);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(Wt + (size_t)col * 256 + 8 * c),
+                (__attribute__((address_space(3))) void*)(sm.wl[i] + 64 * k), 16, 0, 0);
         }
     }
+    wait_vm();  // this wavefront's copies have landed (the caller's barrier orders them)
 }
 
 // Expansion of one tile (rows m0 .. m0 + 31 of the level) over the workgroup's slice; the

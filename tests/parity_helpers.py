@@ -148,6 +148,34 @@ def tree_targets(inst: inputs.Instance, tree: dict, rows) -> np.ndarray:
     return out
 
 
+def deep_path_targets(inst: inputs.Instance, tree: dict, tgt: np.ndarray, boost: float = 40.0):
+    """Plant the deepest root-to-node path of each tree in its targets `tgt` [R][Ncap+1][V]
+    (changed in place): along the path, each row's next path token is raised `boost` above
+    the row's maximum, so the target's choice at every step is the drafted child and a
+    verifier accepts the whole path (the leaf's own row is left as it was).  Returns the
+    path lengths (the depth of each tree's deepest node; lowest node index among equals)."""
+    depth = np.zeros(inst.R, np.int64)
+    for i in range(inst.R):
+        n = int(tree["n_nodes"][i])
+        if n == 0:
+            continue
+        d = tree["depth"][i, :n]
+        leaf = int(np.argmax(d))
+        path = []
+        j = leaf
+        while j >= 0:
+            path.append(j)
+            j = int(tree["parent"][i, j])
+        path.reverse()
+        row = 0
+        for j in path:
+            tok = int(tree["token"][i, j])
+            tgt[i, row, tok] = tgt[i, row].max() + boost
+            row = j + 1
+        depth[i] = int(d[leaf])
+    return depth
+
+
 def tie_targets(inst: inputs.Instance, tree: dict, seed: int) -> np.ndarray:
     """Greedy-verify targets [R][Ncap+1][V] with exact ties at every row's maximum.
 

@@ -3,8 +3,8 @@ or_build_flash, element by element on margin-certified inputs: token sets, topol
 tokens, masks, candidate rows, status, survival bits exactly; logq within 1e-5 relative.
 
 Cases: small float32 instances (several M, B, N, tau, calibration plateaus, several
-requests, a bad root and a clamped budget), small bf16 instances (several state tiles,
-vocabularies that are not a multiple of 8, r < 256) and the full-vocabulary bf16 workloads (B = 7,
+requests, a bad root and a clamped budget, the largest B with M = 8 and M = 1), small bf16
+instances (several state tiles, vocabularies that are not a multiple of 8, r < 256, B = 32) and the full-vocabulary bf16 workloads (B = 7,
 N = 32; B = 16, N = 64; the 64-request batch at tau = 0 and 0.05), each with the plain and
 the strong head, every request compared.
 """
@@ -61,6 +61,9 @@ SMALL = [
     dict(seed=6, V=200, r=16, B=4, k=8, Ncap=64, tau=0.0),
     dict(seed=7, V=64, r=8, B=4, k=3, Ncap=30, tau=0.05),
     dict(seed=8, V=64, r=8, B=4, k=2, Ncap=12, tau=0.0, R=5),
+    # the largest block count (B = 32): 249 states (M = 8), and a 32-deep chain (M = 1)
+    dict(seed=11, V=300, r=32, B=32, k=8, Ncap=64, tau=0.0, R=3),
+    dict(seed=13, V=100, r=8, B=32, k=1, Ncap=40, tau=0.0, R=2),
 ]
 
 
@@ -81,6 +84,7 @@ SMALL_BF16 = [
     dict(seed=21, V=130, r=16, B=8, k=4, Ncap=24, R=5, dtype="bf16"),
     dict(seed=22, V=200, r=32, B=6, k=3, Ncap=16, R=11, dtype="bf16"),
     dict(seed=23, V=1000, r=64, B=4, k=2, Ncap=12, R=40, dtype="bf16"),
+    dict(seed=24, V=300, r=32, B=32, k=8, Ncap=64, R=3, dtype="bf16"),
 ]
 
 

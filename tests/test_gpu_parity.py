@@ -11,7 +11,8 @@ import oracle
 from draft_tree_construction_rank_amd import inputs
 from oracle_helpers import check_structure, tree_paths
 from parity_helpers import (STRESS_MARGIN, case_instance, certified, compare_trees,
-                            compare_verify, instance, tie_targets, tree_targets)
+                            compare_verify, deep_path_targets, instance, tie_targets,
+                            tree_targets)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,6 +97,11 @@ SMALL = [
     # a wide batch: several 256-row groups per level (the last one ragged) and many merges
     # and selects per workgroup
     dict(seed=10, V=2048, r=32, B=3, k=4, Ncap=32, R=200, dtype="bf16"),
+    # the largest block count (B = 32): a 32-level chain, a wide tree of N = 64, and a level
+    # of more than 64 rows (group mode) at that B
+    dict(seed=11, V=700, r=16, B=32, k=1, Ncap=32, R=2, dtype="f32"),
+    dict(seed=12, V=1000, r=32, B=32, k=2, Ncap=64, R=3, dtype="bf16"),
+    dict(seed=13, V=1000, r=32, B=32, k=2, Ncap=64, R=40, dtype="bf16"),
 ]
 
 
@@ -241,6 +247,32 @@ def test_edge_bad_root_budget_and_empty(rt):
 def test_edge_single_level_and_k_equals_v(rt):
     inst = instance("tiny", strong=True, V=6, r=8, B=1, k=6, Ncap=6, R=2, dtype="f32")
     _greedy_case(rt, inst, margin=STRESS_MARGIN)
+
+
+@pytest.mark.parametrize("cfg", [dict(seed=11, V=700, r=16, B=32, k=1, Ncap=32, R=2, dtype="f32"),
+                                 dict(seed=12, V=1000, r=32, B=32, k=2, Ncap=64, R=3,
+                                      dtype="bf16")], ids=["chain", "tree"])
+def test_edge_deepest_path_accepted(rt, cfg):
+    """Targets planted to choose the drafted child along each tree's deepest path (B = 32):
+    the greedy walk accepts the whole path (all 32 blocks on the chain) and emits the leaf's
+    own target choice, as the oracle does."""
+    import torch
+    inst = instance("tiny", strong=True, cal="monotone", rho=0.5, **cfg)
+    print("case deepest path", cfg, flush=True)
+    inst, ref = certified(inst, margin=STRESS_MARGIN)
+    rnd, d, got = _gpu_round(rt, inst)
+    rows = list(range(inst.R))
+    compare_trees(ref, got, rows)
+    tgt = tree_targets(inst, ref, rows)
+    depth = deep_path_targets(inst, ref, tgt)
+    vres = oracle.verify_greedy(inst, ref, tgt)
+    assert np.array_equal(vres["accept_len"], depth), (vres["accept_len"], depth)
+    out = rnd.verify_greedy(rt.target_to_device(inst, tgt))
+    torch.cuda.synchronize()
+    gv = {k: v.cpu().numpy() for k, v in out.items()}
+    compare_verify(vres, gv, rows)
+    if inst.k == 1:
+        assert (gv["accept_len"] == inst.B).all() and (gv["n_out"] == inst.B + 1).all()
 
 
 def test_deterministic_repeat(rt):

@@ -9,7 +9,8 @@ import pytest
 import oracle
 from oracle_helpers import check_structure
 from parity_helpers import (STRESS_MARGIN, case_instance, certified, compare_trees,
-                            compare_verify, instance, sample_verify_margins, tree_targets)
+                            compare_verify, deep_path_targets, instance,
+                            sample_verify_margins, tree_targets)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,6 +62,9 @@ SMALL = [
     dict(seed=12, V=1000, r=16, B=4, k=3, Ncap=12, R=4, dtype="bf16", temperature=0.6),
     dict(seed=13, V=2053, r=32, B=5, k=4, Ncap=20, R=2, dtype="bf16", temperature=1.5),
     dict(seed=14, V=64, r=8, B=4, k=2, Ncap=8, R=70, dtype="f32", temperature=1.0),
+    # the largest block count (B = 32): a 32-step chain and a wide tree of N = 64
+    dict(seed=17, V=500, r=8, B=32, k=1, Ncap=32, R=2, dtype="f32", temperature=1.0),
+    dict(seed=18, V=1000, r=16, B=32, k=2, Ncap=64, R=3, dtype="bf16", temperature=0.8),
 ]
 
 
@@ -83,6 +87,37 @@ LARGE_V = [
 def test_sample_large_vocabulary(rt, cfg):
     inst = instance("tiny", strong=True, cal="monotone", rho=0.7, mode="sample", **cfg)
     _sample_case(rt, inst, margin=STRESS_MARGIN)
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(seed=17, V=500, r=8, B=32, k=1, Ncap=32, R=2, dtype="f32", temperature=1.0),
+    dict(seed=18, V=1000, r=16, B=32, k=2, Ncap=64, R=3, dtype="bf16", temperature=0.8)],
+    ids=["chain", "tree"])
+def test_sample_deepest_path_accepted(rt, cfg):
+    """Targets planted to put almost all their mass on the drafted child along each tree's
+    deepest path (B = 32): the rejection walk accepts the whole path (all 32 blocks on the
+    chain) and draws the last token from the leaf's target, as the oracle does; every
+    |u - p/q| and Gumbel-max gap of the walk is at least 1e-5 away."""
+    import torch
+    inst = instance("tiny", strong=True, cal="monotone", rho=0.7, mode="sample", **cfg)
+    print("case deepest path", cfg, flush=True)
+    inst, ref = certified(inst, margin=STRESS_MARGIN)
+    rnd = rt.Round(inst)
+    d = rt.to_device(inst)
+    rnd.build(d)
+    torch.cuda.synchronize()
+    rows = list(range(inst.R))
+    compare_trees(ref, rt.tree_to_numpy(rnd.tree), rows)
+    tgt = tree_targets(inst, ref, rows)
+    depth = deep_path_targets(inst, ref, tgt)
+    vref = oracle.verify_sample(inst, ref, tgt)
+    m = vref["margins"]
+    assert min(float(m["accept"].min()), float(m["draw_gap"].min())) >= STRESS_MARGIN
+    assert np.array_equal(vref["accept_len"], depth), (vref["accept_len"], depth)
+    out = rnd.verify_sample(d, rt.target_to_device(inst, tgt))
+    torch.cuda.synchronize()
+    gv = {k: v.cpu().numpy() for k, v in out.items()}
+    compare_verify(vref, gv, rows)
 
 
 @pytest.mark.parametrize("T", [0.6, 1.0, 1.5])
